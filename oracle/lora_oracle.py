@@ -1,0 +1,416 @@
+"""CPU oracle for batched multi-adapter LoRA application.
+
+TEST INFRASTRUCTURE ONLY.  This package is imported, called or executed only by
+``tests/``, by ``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of
+``bench.py``.  The product path (``rank_adapter_gemm_build_amd``) never touches it,
+and it shares no code, table or helper with the HIP library.
+
+It is deliberately plain and slow: numpy float64, one Python loop over tokens
+where the pages define the operation per token, a library matmul only where the
+pages' own description is a matmul.  Every function names the passage it follows.
+
+Pages cited (title, then the section used):
+  [llama.cpp]  "llama.cpp 源码完全拆解(十六):LoRA 适配器——低秩补丁如何挂进 ggml 计算图"
+  [TRT-LLM]    "TensorRT-LLM 源码完全拆解(二十一):LoRA 服务——adapter 池、批内多适配器与
+                前向替换的完整链路"
+  [vLLM-deep]  "vLLM LoRA 实现深度解析"
+  [vLLM-book]  "第16章 LoRA 适配器热切换：一个引擎承载多个微调"
+
+Operator (all pages agree up to notation): for a token x in R^k routed to an
+adapter with A in R^{r x k} (shrink, ``lora_a``) and B in R^{d x r} (expand,
+``lora_b``), the output is  h = W0 x + s * B (A x).  Row-major batch form with
+x stored [T, k] and W0 stored [d, k]:  Y = X W0^T + s (X A^T) B^T.
+
+Readings taken where the pages are silent (each is also listed in the design
+notes of the repository):
+  * u = A x is kept in float64 here; the GPU keeps it in fp32 and never rounds it
+    to bf16.
+  * "alpha missing" is alpha == 0.
+  * rsLoRA combines multiplicatively with the runtime adapter_scale.
+  * the no-LoRA group (slot id -1, or any id outside [0, S)) sorts LAST, under
+    the sentinel key S.
+  * a slot with rank 0 or scale 0 contributes nothing and leaves its rows
+    bit-untouched, as does a slice registered as missing.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(hand-derived fixtures in ``tests/golden``, closed forms, invariants, brute force
+on tiny inputs, and planted-mistake checks).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "lora_scale",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f64",
+    "round_to_dtype",
+    "effective_b",
+    "Adapter",
+    "Routing",
+    "route_by_sort",
+    "route_by_counting",
+    "shrink_per_token",
+    "expand_per_token",
+    "lora_apply",
+    "lora_apply_grouped",
+    "merged_apply",
+    "extra_macs_per_token",
+    "adapter_params",
+]
+
+
+# --------------------------------------------------------------------------- scale
+def lora_scale(alpha: float, rank: int, rslora: bool, adapter_scale: float = 1.0) -> np.float32:
+    """Scale s applied to the low-rank branch.
+
+    [llama.cpp] section "缩放系数到底乘在哪": the scale is adapter_scale*alpha/rank when
+    alpha is present, and plain adapter_scale when the file carries no alpha (the
+    loader then reads 0).  The rank is the adapter's own rank.
+    [TRT-LLM] "从检查点到 GPU:LoraManager 的加载流水线", step 4, and [vLLM-deep] §1
+    "rsLoRA 变体": with use_rslora the denominator is sqrt(r) instead of r.
+
+    Evaluated in float64 left to right (adapter_scale * alpha, then divided by r or
+    by sqrt(r)) and rounded once to float32.
+    """
+    if int(rank) != rank or rank < 1:
+        raise ValueError("rank must be a positive integer")
+    a = float(np.float32(alpha))
+    c = float(np.float32(adapter_scale))
+    if a == 0.0:
+        sigma = c
+    elif rslora:
+        sigma = c * a / math.sqrt(float(rank))
+    else:
+        sigma = c * a / float(rank)
+    return np.float32(sigma)
+
+
+# ---------------------------------------------------------------- number formats
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    bfloat16 keeps the upper 16 bits of a float32.  Written from the definition:
+    add 0x7FFF plus the lowest kept bit, then truncate.  NaNs stay NaN (quiet bit
+    forced).  Returns uint16 bit patterns.
+    """
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    is_nan = np.isnan(f)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    r = np.where(is_nan, ((u >> 16) | 0x40) & 0xFFFF, r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns (the bits are the top half of a float32)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_dtype(a, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage format, returned as float64.
+
+    'f32': one IEEE round-to-nearest-even to float32.  'bf16': to float32 first,
+    then to bfloat16 with ties to even (the GPU produces fp32 results and rounds
+    those once to bf16).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(f32_to_bf16_bits(a.astype(np.float32)))
+    raise ValueError(dtype)
+
+
+# ------------------------------------------------------------------ adapter pool
+@dataclass
+class Adapter:
+    """One adapter resident in one slot of one target module.
+
+    A[n] is [rank, k] and B[n] is [d_n, rank] per output slice n, as stored by PEFT
+    ([vLLM-deep] §3.3 LoRALayerWeights: lora_a (r, k), lora_b (d, r)); None marks a
+    missing slice, which contributes nothing ([TRT-LLM] "LoraConfig:哪些矩阵可以被
+    替换": missing q/k/v modules are padded with zeros).  Values are the exact stored
+    numbers as float64.  One rank for every slice of the slot ([TRT-LLM] "一次 decode
+    批次的路由": all modules of a slot share one rank).
+    """
+
+    rank: int
+    A: List[Optional[np.ndarray]]
+    B: List[Optional[np.ndarray]]
+    alpha: float
+    rslora: bool = False
+    adapter_scale: float = 1.0
+    premultiply: bool = False
+
+    def scale(self) -> np.float32:
+        return lora_scale(self.alpha, self.rank, self.rslora, self.adapter_scale)
+
+
+def effective_b(adapter: Adapter, n: int, wdtype: str):
+    """The B the expand multiplies, and the scale still applied after the branch.
+
+    Without pre-multiplication: (B, s) - the scale multiplies the finished branch
+    output ([llama.cpp] "真正的核心:建图时如何把低秩分支拼进去": ggml_scale on B(Ax)).
+    With it: ([vLLM-deep] §1 "推理优化:预合并 scaling", LoRALayerWeights.optimize():
+    lora_b *= scaling, then scaling = 1) the product s*B is formed once in float32 and
+    stored back in the pool format, and the remaining scale is 1.
+    """
+    B = adapter.B[n]
+    s = adapter.scale()
+    if B is None:
+        return None, float(s)
+    if not adapter.premultiply:
+        return np.asarray(B, dtype=np.float64), float(s)
+    prod32 = np.float32(s) * np.asarray(B, dtype=np.float32)  # one fp32 rounding
+    return round_to_dtype(prod32.astype(np.float64), wdtype), 1.0
+
+
+# ---------------------------------------------------------------------- routing
+@dataclass
+class Routing:
+    keys: np.ndarray          # [T]   slot id, or S for "no LoRA"
+    counts: np.ndarray        # [S+1] tokens per key
+    seg_offsets: np.ndarray   # [S+2] exclusive prefix of counts; [0]=0, [S]=#LoRA tokens, [S+1]=T
+    sorted_ids: np.ndarray    # [T]   token indices, grouped by key, ascending within a key
+    active_slots: np.ndarray  # [num_active] keys < S with count > 0, ascending
+    num_active: int
+    n_invalid: int            # ids outside {-1} U [0, S)
+    extra: Dict[str, object] = field(default_factory=dict)
+
+
+def _keys(ids: Sequence[int], S: int):
+    """Key of each token.
+
+    [vLLM-book] §16.4.2: token_lora_mapping holds the slot index, -1 meaning no
+    LoRA.  [TRT-LLM] "adapter 池:AdapterSlotManager 与两级缓存": requests without an
+    adapter are mapped to the sentinel max_num_adapters, whose rank is 0.  Ids that
+    are neither -1 nor a valid slot are treated as no-LoRA and counted.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    valid = (ids >= 0) & (ids < S)
+    keys = np.where(valid, ids, S).astype(np.int64)
+    n_invalid = int(np.count_nonzero(~valid & (ids != -1)))
+    return keys, n_invalid
+
+
+def _finish(keys, sorted_ids, counts, S, n_invalid) -> Routing:
+    T = len(keys)
+    offs = np.zeros(S + 2, dtype=np.int64)
+    for k in range(S + 1):  # [vLLM-book] §16.4.3: lora_token_start_loc, length max_loras+2, first 0
+        offs[k + 1] = offs[k] + counts[k]
+    assert offs[S + 1] == T
+    active = np.array([k for k in range(S) if counts[k] > 0], dtype=np.int64)
+    return Routing(keys=keys, counts=np.asarray(counts, dtype=np.int64), seg_offsets=offs,
+                   sorted_ids=np.asarray(sorted_ids, dtype=np.int64), active_slots=active,
+                   num_active=len(active), n_invalid=n_invalid)
+
+
+def route_by_sort(ids: Sequence[int], S: int) -> Routing:
+    """Routing metadata, formulation (i): a stable sort of token indices by key.
+
+    [vLLM-book] §16.4.2-§16.4.3: sort the tokens by slot, count the tokens of each
+    slot, take the start offset of each segment; the five index tensors of
+    LoRAKernelMeta.  Ties keep token order (a stable sort).
+    """
+    keys, n_invalid = _keys(ids, S)
+    T = len(keys)
+    order = sorted(range(T), key=lambda t: (int(keys[t]), t))
+    counts = [int(np.count_nonzero(keys == k)) for k in range(S + 1)]
+    return _finish(keys, order, counts, S, n_invalid)
+
+
+def route_by_counting(ids: Sequence[int], S: int) -> Routing:
+    """Routing metadata, formulation (ii): an explicit counting sort.
+
+    [TRT-LLM] "一次 decode 批次的路由:从请求到 slot_ids", step 4: per-slot counts by
+    bincount with a minimum length, then a cumulative sum gives each slot's first
+    row; the offsets array is one longer than the counts.  Tokens are then placed
+    in increasing token order at their key's running cursor.
+    """
+    keys, n_invalid = _keys(ids, S)
+    T = len(keys)
+    counts = [0] * (S + 1)
+    for t in range(T):
+        counts[int(keys[t])] += 1
+    cursor = [0] * (S + 1)
+    run = 0
+    for k in range(S + 1):
+        cursor[k] = run
+        run += counts[k]
+    sorted_ids = [0] * T
+    for t in range(T):
+        k = int(keys[t])
+        sorted_ids[cursor[k]] = t
+        cursor[k] += 1
+    return _finish(keys, sorted_ids, counts, S, n_invalid)
+
+
+# ------------------------------------------------------------- shrink / expand
+def _slice_offsets(slices: Sequence[int]) -> List[int]:
+    """Column offset of each output slice in the packed output ([TRT-LLM] "前向替换":
+    output_hidden_sizes and output_sizes_offset of the packed output buffer)."""
+    offs, o = [], 0
+    for d in slices:
+        offs.append(o)
+        o += int(d)
+    return offs
+
+
+def _contributes(ad: Optional[Adapter]) -> bool:
+    return ad is not None and ad.rank > 0 and float(ad.scale()) != 0.0
+
+
+def shrink_per_token(x: np.ndarray, adapters: Dict[int, Adapter], slices: Sequence[int],
+                     ids: Sequence[int], S: int, max_rank: int):
+    """u[n, t, j] = sum_c A_slot[n][j, c] * x[t, c]  (the shrink, lora_a).
+
+    [vLLM-book] §16.4.2: lora_shrink projects each token onto its adapter's rank
+    space, buffer [num_tokens, r]; [vLLM-deep] §6: lora_shrink computes A*x.
+    Defined for tokens routed to a registered slot and j < rank; a missing slice
+    gives zeros.  Returns (u [N, T, max_rank] float64, mask of defined entries).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    N = len(slices)
+    keys, _ = _keys(ids, S)
+    u = np.zeros((N, T, max_rank), dtype=np.float64)
+    mask = np.zeros((N, T, max_rank), dtype=bool)
+    for t in range(T):
+        ad = adapters.get(int(keys[t])) if keys[t] < S else None
+        if ad is None or ad.rank == 0:
+            continue
+        for n in range(N):
+            if ad.A[n] is not None:
+                u[n, t, :ad.rank] = np.asarray(ad.A[n], dtype=np.float64) @ x[t]
+            mask[n, t, :ad.rank] = True
+    return u, mask
+
+
+def expand_per_token(u: np.ndarray, adapters: Dict[int, Adapter], slices: Sequence[int],
+                     ids: Sequence[int], S: int, wdtype: str):
+    """delta[t, o_n + i] = s_eff * sum_j B_eff[n][i, j] * u[n, t, j]  (the expand, lora_b).
+
+    [vLLM-book] §16.4.2: lora_expand maps the rank-space buffer back to the output,
+    [num_tokens, d], one output slice at a time (§16.4.4 add_expand "按 output slice
+    写回").  The scale multiplies the completed sum ([llama.cpp] "真正的核心").
+    Returns (delta [T, sum d] float64, touched [T, N] bool: which (token, slice) the
+    branch writes).
+    """
+    T = u.shape[1]
+    N = len(slices)
+    offs = _slice_offsets(slices)
+    keys, _ = _keys(ids, S)
+    delta = np.zeros((T, int(sum(slices))), dtype=np.float64)
+    touched = np.zeros((T, N), dtype=bool)
+    for t in range(T):
+        ad = adapters.get(int(keys[t])) if keys[t] < S else None
+        if not _contributes(ad):
+            continue
+        for n in range(N):
+            Bn, s_eff = effective_b(ad, n, wdtype)
+            if Bn is None:
+                continue
+            delta[t, offs[n]:offs[n] + slices[n]] = s_eff * (Bn @ u[n, t, :ad.rank])
+            touched[t, n] = True
+    return delta, touched
+
+
+def lora_apply(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int], ids: Sequence[int],
+               S: int, wdtype: str, max_rank: Optional[int] = None) -> np.ndarray:
+    """y = y_base + s * B (A x) per token, in float64 (the definition).
+
+    [llama.cpp] "为什么低秩增量可以「后加」": h = W0 x + (alpha/r) B A x, the base and the
+    branch act on the same input and are summed; [TRT-LLM] "前向替换:LoraLayer 的三条
+    路径": the correction is added in place onto the base output (output.add_).
+    Rows of no-LoRA tokens, of empty or zero-scale slots and columns of missing
+    slices are returned as y_base unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = np.array(y_base, dtype=np.float64, copy=True)
+    if max_rank is None:
+        max_rank = max([a.rank for a in adapters.values()] + [1])
+    u, _ = shrink_per_token(x, adapters, slices, ids, S, max_rank)
+    delta, touched = expand_per_token(u, adapters, slices, ids, S, wdtype)
+    offs = _slice_offsets(slices)
+    for t in range(x.shape[0]):
+        for n in range(len(slices)):
+            if touched[t, n]:
+                sl = slice(offs[n], offs[n] + slices[n])
+                y[t, sl] = y[t, sl] + delta[t, sl]
+    return y
+
+
+def lora_apply_grouped(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int],
+                       ids: Sequence[int], S: int, wdtype: str) -> np.ndarray:
+    """Second formulation: the naive loop over the adapters present in the batch.
+
+    [vLLM-book] §16.4.1 "朴素方案的代价": for each adapter in the batch, gather its
+    tokens, output[idx] += scaling * (x[idx] @ A) @ B (row-vector notation; here A
+    is stored [r, k] and B [d, r], so the products are x A^T and then (.) B^T).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = np.array(y_base, dtype=np.float64, copy=True)
+    keys, _ = _keys(ids, S)
+    offs = _slice_offsets(slices)
+    for slot in sorted(set(int(k) for k in keys if k < S)):
+        ad = adapters.get(slot)
+        if not _contributes(ad):
+            continue
+        idx = np.nonzero(keys == slot)[0]
+        for n in range(len(slices)):
+            Bn, s_eff = effective_b(ad, n, wdtype)
+            if ad.A[n] is None or Bn is None:
+                continue
+            sl = slice(offs[n], offs[n] + slices[n])
+            y[np.ix_(idx, np.arange(sl.start, sl.stop))] += s_eff * ((x[idx] @ np.asarray(ad.A[n]).T) @ Bn.T)
+    return y
+
+
+def merged_apply(x, W0, adapters: Dict[int, Adapter], slices: Sequence[int], ids: Sequence[int],
+                 S: int, wdtype: str) -> np.ndarray:
+    """Linearity check: y_t = (W0 + s B A) x_t with the delta merged into the weight.
+
+    [llama.cpp] "为什么低秩增量可以「后加」" (W = W0 + BA acts linearly, so merging and
+    adding afterwards agree) and "从 PEFT 到 GGUF" (export-lora merges W0 + scale*BA
+    offline).  W0 is [sum d, k]; a slice whose A or B is missing merges nothing.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    keys, _ = _keys(ids, S)
+    offs = _slice_offsets(slices)
+    y = np.zeros((x.shape[0], W0.shape[0]), dtype=np.float64)
+    for t in range(x.shape[0]):
+        W = W0.copy()
+        ad = adapters.get(int(keys[t])) if keys[t] < S else None
+        if _contributes(ad):
+            for n in range(len(slices)):
+                Bn, s_eff = effective_b(ad, n, wdtype)
+                if ad.A[n] is None or Bn is None:
+                    continue
+                W[offs[n]:offs[n] + slices[n], :] += s_eff * (Bn @ np.asarray(ad.A[n], dtype=np.float64))
+        y[t] = W @ x[t]
+    return y
+
+
+# ------------------------------------------------------------------ arithmetic
+def extra_macs_per_token(k: int, slices: Sequence[int], r: int) -> int:
+    """Multiply-adds the unmerged branch adds per token: r*k for A x, then d*r for B(.).
+
+    [llama.cpp] "为什么低秩增量可以「后加」": 2dr extra multiply-adds per token when
+    d = k, against dk for the base matmul.
+    """
+    return int(r) * int(k) + int(sum(slices)) * int(r)
+
+
+def adapter_params(k: int, slices: Sequence[int], r: int) -> int:
+    """Elements of one adapter on one linear layer: r*(d + k) ([llama.cpp] "性能与工程取舍";
+    [vLLM-deep] §9 "显存估算": in_features*rank + out_features*rank)."""
+    return int(r) * (int(k) + int(sum(slices)))
