@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched multi-adapter LoRA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: build the routing
+metadata from the batch's token -> slot ids, then one fused shrink+expand
+(lora_linear) per target module, adding onto a base output already in HBM.
+Adapters are registered before timing (registration is once per adapter, off the
+per-step path).  Inputs are seeded synthetic tensors shaped like the workload.
+
+To keep the 256 MB Infinity Cache (and the L2) from serving repeated steps, the
+timed loop rotates over M independent instances (pools, routing, x, y, ids) whose
+algorithmic traffic adds up to at least --rotate-mib.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA tokens/sec and shrink+expand HBM GB/s (% peak), d=k=4096 r=16 multi-adapter"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ accounting
+def step_accounting(W, mfma_min: int, use_mfma: bool):
+    """Algorithmic HBM bytes per step, per kernel family, from the routing counts.
+
+    Per module, for every slot with tokens and rank r > 0: the shrink must read the
+    slot's A at its true rank (r * k elements per present slice) and each of its
+    tokens' x rows once (k elements); the expand must read B at its true rank
+    (r * d_n per present slice) and read and write each token's output row once
+    (2 * sum d_n).  No-LoRA tokens, padding rows and the rank-space intermediate are
+    not counted.  Segments of at least mfma_min tokens count toward the matrix-core
+    kernels when those are in use.
+    """
+    import numpy as np
+    wb = 2 if W.dtype == "bf16" else 4
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    counts = np.bincount(keys, minlength=W.S + 1)
+    acc = {"shrink_decode": 0, "expand_decode": 0, "shrink_mfma": 0, "expand_mfma": 0}
+    flops = 0
+    for mod in W.modules:
+        D = sum(mod.slices)
+        for s, r in W.ranks.items():
+            L = int(counts[s])
+            if L == 0 or r == 0:
+                continue
+            fam = "mfma" if (use_mfma and L >= mfma_min) else "decode"
+            acc[f"shrink_{fam}"] += r * mod.k * len(mod.slices) * wb + L * mod.k * wb
+            acc[f"expand_{fam}"] += r * D * wb + 2 * L * D * wb
+            flops += 2 * L * r * (mod.k * len(mod.slices) + D)
+    return acc, flops
+
+
+# -------------------------------------------------------------------- workload
+class Instance:
+    """One independent copy of the step's device state."""
+
+    def __init__(self, rx, torch, W, dev_src, ydt):
+        self.mods = []
+        self.routing = rx.Routing(0, W.T, W.S)
+        self.ids = torch.from_numpy(W.ids.astype("int32")).cuda()
+        for m, src in zip(W.modules, dev_src):
+            pool = rx.Pool(0, W.S, W.Rmax, m.k, m.slices, rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32, W.T)
+            for s, r in W.ranks.items():
+                pool.register(s, src["A"][s], src["B"][s], W.alpha[s], r, W.rslora, W.adapter_scale,
+                              device_src=True)
+            x = src["x"].clone()
+            y = src["y"].clone()
+            self.mods.append((pool, x, y))
+        self.calls = [(p.handle, x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0)) for p, x, y in self.mods]
+
+    def close(self):
+        for p, _, _ in self.mods:
+            p.close()
+        self.routing.close()
+
+
+def upload_sources(torch, W):
+    import numpy as np
+
+    def dev(a):
+        if a is None:
+            return None
+        if W.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    out = []
+    for m in W.modules:
+        src = {"A": {s: [dev(a) for a in m.A[s]] for s in W.ranks},
+               "B": {s: [dev(b) for b in m.B[s]] for s in W.ranks},
+               "x": dev(m.x)}
+        if m.y_base is not None:
+            src["y"] = dev(m.y_base)
+        else:  # base output of the caller's own base GEMM (not part of the library)
+            W0 = dev(m.W0)
+            src["y"] = (src["x"].float() @ W0.float().T).to(src["x"].dtype)
+        out.append(src)
+    return out
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_adapter_gemm_build_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload_name: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when the
+    counters are missing or were taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name, {}).get(kernel)
+    if not e or e.get("source_digest") != source_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- cpu baseline
+def cpu_baseline(W, seconds: float):
+    """The oracle as it stands (per-token float64 definition), timed on this host."""
+    import numpy as np
+    import oracle.lora_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    mods = []
+    for m in W.modules:
+        conv = (lambda a: None if a is None else O.bf16_bits_to_f64(a)) if W.dtype == "bf16" else \
+               (lambda a: None if a is None else np.asarray(a, dtype=np.float64))
+        ads = {s: O.Adapter(rank=r, A=[conv(a) for a in m.A[s]], B=[conv(b) for b in m.B[s]], alpha=W.alpha[s],
+                            rslora=W.rslora, adapter_scale=W.adapter_scale) for s, r in W.ranks.items()}
+        yb = conv(m.y_base) if m.y_base is not None else np.zeros((W.T, sum(m.slices)))
+        mods.append((conv(m.x), yb, ads, m.slices))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for x, yb, ads, slices in mods:
+            O.lora_apply(x, yb, ads, slices, W.ids, W.S, W.dtype, max_rank=W.Rmax)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * W.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole {W.name} batch ({W.T} tokens, {len(W.modules)} module(s)) through "
+                      f"oracle.lora_apply (float64 per-token definition), repeated {reps} times in {el:.1f} s"}
+
+
+# ------------------------------------------------------------------------ main
+def run(args):
+    import numpy as np
+    import torch
+
+    import rank_adapter_gemm_build_amd as rx
+    from synthetic import workload
+
+    torch.cuda.set_device(0)
+    W = workload(args.workload)
+    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0" and rx_has_mfma(rx)
+    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "32"))
+    acc, flops = step_accounting(W, mfma_min, use_mfma)
+    step_bytes = sum(acc.values())
+    log(f"workload {W.name}: T={W.T} S={W.S} modules={[m.name for m in W.modules]} "
+        f"algorithmic bytes/step={step_bytes / 1e6:.2f} MB")
+    M = max(2, min(args.max_instances, math.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes, 1))))
+    src = upload_sources(torch, W)
+    insts = []
+    for i in range(M):
+        insts.append(Instance(rx, torch, W, src, None))
+    torch.cuda.synchronize()
+    log(f"{M} rotation instances registered")
+    stream = torch.cuda.current_stream().cuda_stream
+    ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
+    lib, T = rx.lib, W.T
+
+    def step(i):
+        inst = insts[i % M]
+        st = lib.lora_build_routing(inst.routing.handle, inst.ids.data_ptr(), T, stream)
+        if st:
+            raise rx.LoraError(st, "lora_build_routing")
+        for pool, xp, ldx, yp, ldy in inst.calls:
+            st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, stream)
+            if st:
+                raise rx.LoraError(st, "lora_linear")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us/step)")
+
+    # per-kernel durations: same steps again, each launch stamped by its own events
+    rx.lora_timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    rep = rx.lora_timing_report()
+    rx.lora_timing_enable(False)
+    kern = {k: {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps} for k, (ms, n) in rep.items() if n}
+    log("kernels: " + ", ".join(f"{k} {v['avg_us']:.2f} us" for k, v in kern.items()))
+
+    # dominant kernel: most time per step among the shrink/expand kernels
+    cand = {k: v for k, v in kern.items() if k in acc}
+    dom = max(cand, key=lambda k: cand[k]["avg_us"] * cand[k]["launches_per_step"])
+    per_launch = acc[dom] / cand[dom]["launches_per_step"]
+    achieved = per_launch / (cand[dom]["avg_us"] * 1e-6) / 1e9
+    traffic = load_traffic(dom, W.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
+                "bytes_per_launch": int(per_launch), "avg_launch_us": round(cand[dom]["avg_us"], 3)}
+
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": W.dtype, "data": "synthetic",
+        "config": {"workload": W.name, "tokens": T, "slots": W.S, "k": [m.k for m in W.modules],
+                   "slices": [m.slices for m in W.modules], "ranks": sorted(set(W.ranks.values())),
+                   "max_lora_rank": W.Rmax, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+                  "step_flops": flops, "kernels": kern, "rotation_instances": M,
+                  "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "source_digest": source_digest()},
+    }
+    for inst in insts:
+        inst.close()
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def rx_has_mfma(rx) -> bool:
+    return False
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: decode, 8 slots, T=64, k=d=4096, r=16)")
+    ap.add_argument("--rotate-mib", type=float, default=1024.0)
+    ap.add_argument("--max-instances", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no cross-GPU sharding or collectives)", file=sys.stderr)
+        sys.exit(2)
+    out = run(args)
+    line = json.dumps(out)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+/*
+ * raxlora.h - C ABI of the MI355X (gfx950) batched multi-adapter LoRA library.
+ *
+ * The library applies, for every token t with its own adapter slot i(t) in a
+ * resident pool,
+ *
+ *     y[t] += s_i * B_i (A_i x[t])            (the base output W0 x[t] is the caller's)
+ *
+ * as a shrink (x -> rank space through lora_a = A) and an expand (rank space ->
+ * output through lora_b = B), driven by per-batch routing metadata.
+ *
+ * Passages this interface follows (page title, then section):
+ *   [llama.cpp] "llama.cpp 源码完全拆解(十六):LoRA 适配器——低秩补丁如何挂进 ggml 计算图"
+ *   [TRT-LLM]   "TensorRT-LLM 源码完全拆解(二十一):LoRA 服务——adapter 池、批内多适配器与
+ *               前向替换的完整链路"
+ *   [vLLM-deep] "vLLM LoRA 实现深度解析"
+ *   [vLLM-book] "第16章 LoRA 适配器热切换：一个引擎承载多个微调"
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major.  x is [T, k] with row stride ldx elements, y is
+ *     [T, D] with D = sum of the slice widths and row stride ldy.  A adapter's
+ *     A (shrink) is [rank, k] and its B (expand) is [d_n, rank] per output slice,
+ *     as PEFT stores lora_a / lora_b ([vLLM-deep] §3.3).
+ *   - "device pointer" means memory on the pool's GPU; "host pointer" ordinary
+ *     process memory.  The library never takes ownership of caller memory.
+ *   - Calls that take a hipStream_t only enqueue work on that stream (no host
+ *     synchronisation) unless documented as synchronous.  The caller keeps its
+ *     buffers alive until that work has completed.
+ *   - Every call returns LORA_OK (0) or a negative lora_status; nothing throws
+ *     across the ABI.  lora_last_error() gives a message for the calling thread.
+ *     Argument checks run before any HIP call, so a rejected call has no effect.
+ *   - Alignment: k and every slice width must be multiples of 8, ldx and ldy
+ *     multiples of 8 elements, and x, y, u 16-byte aligned (the kernels move 16
+ *     bytes per lane; [TRT-LLM] "前向替换" notes the grouped kernels assume K, N of
+ *     at least 8).  Otherwise LORA_ERR_ALIGN.
+ *   - Thread safety: distinct objects may be used from distinct threads.  One
+ *     pool or routing object must not be mutated (register/unregister/build) while
+ *     work that reads it may still run on another stream.  lora_linear and
+ *     lora_shrink use a workspace owned by the pool, so two of them on one pool
+ *     must not overlap in time (same stream is always safe).
+ */
+#ifndef RAXLORA_H
+#define RAXLORA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lora_pool lora_pool;
+typedef struct lora_routing lora_routing;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+typedef int lora_status;
+#define LORA_OK                0
+#define LORA_ERR_INVALID_ARG  (-1)   /* null handle or pointer, non-finite value, bad flag   */
+#define LORA_ERR_SHAPE        (-2)   /* sizes or strides inconsistent                         */
+#define LORA_ERR_DTYPE        (-3)   /* input dtype differs from the pool's                   */
+#define LORA_ERR_RANK         (-4)   /* rank outside [1, max_lora_rank]                       */
+#define LORA_ERR_SLOT         (-5)   /* slot outside [0, max_slots)                           */
+#define LORA_ERR_CAPACITY     (-6)   /* more tokens than the object was created for           */
+#define LORA_ERR_HIP          (-7)   /* a HIP runtime call failed                             */
+#define LORA_ERR_OOM          (-8)   /* device allocation failed                              */
+#define LORA_ERR_NO_DEVICE    (-9)   /* no usable GPU / device index out of range             */
+#define LORA_ERR_ALIGN        (-10)  /* alignment rule above violated                         */
+#define LORA_ERR_STATE        (-11)  /* object used out of order (e.g. routing never built)   */
+
+/* register_adapter flags */
+#define LORA_SRC_DEVICE   1u   /* A_slices / B_slices are device pointers (else host)          */
+#define LORA_PREMULTIPLY  2u   /* fold the scale into B at registration                        */
+
+/* Limits fixed at build time. */
+#define LORA_MAX_SLICES    8
+#define LORA_MAX_SLOTS     1024
+#define LORA_MAX_RANK      256
+
+/* Message for the last failing call on this thread ("" if none). Never NULL. */
+const char* lora_last_error(void);
+/* Static name of a status code. */
+const char* lora_status_string(lora_status status);
+
+/*
+ * Scale of the low-rank branch ([llama.cpp] "缩放系数到底乘在哪": adapter_scale *
+ * alpha / rank, or adapter_scale alone when alpha is 0, i.e. absent; [TRT-LLM]
+ * "LoraManager 的加载流水线" step 4 and [vLLM-deep] §1 "rsLoRA 变体": alpha/sqrt(rank)
+ * when rslora is set).  Computed in double as adapter_scale*alpha, divided by rank
+ * or sqrt(rank), and rounded once to float.  Pure host function, no device needed.
+ * Errors: out_scale NULL -> INVALID_ARG; rank < 1 -> RANK; alpha or adapter_scale
+ * not finite, or a non-finite result -> INVALID_ARG.
+ */
+lora_status lora_compute_scale(float alpha, int rank, int rslora, float adapter_scale,
+                               float* out_scale);
+
+/*
+ * Create a pool of max_slots adapter slots for one target module (one linear
+ * layer, or a packed group such as q/k/v or gate/up with num_slices output
+ * slices of widths slice_out[0..num_slices)), like one layer's stacked LoRA
+ * buffers ([vLLM-deep] §9: lora_a_stacked [max_loras, max_lora_rank, in],
+ * lora_b_stacked [max_loras, out, max_lora_rank]).  max_lora_rank fixes the
+ * padding of every slot ([TRT-LLM] "LoraConfig": a workspace bound, not
+ * enlargeable later).  max_tokens bounds T for lora_linear / lora_shrink (it
+ * sizes the pool-owned split-K workspace).  All slots start empty (rank 0).
+ * slice_out is a host array, read during the call.  The pool owns its device
+ * memory (allocated on `device` here) until lora_pool_destroy.
+ * Errors: out/slice_out NULL -> INVALID_ARG; max_slots outside [1, LORA_MAX_SLOTS],
+ * max_lora_rank outside [1, LORA_MAX_RANK], in_features < 1, num_slices outside
+ * [1, LORA_MAX_SLICES], a slice width < 1, max_tokens < 1 -> SHAPE; bad wdtype ->
+ * DTYPE; in_features or a width not a multiple of 8 -> ALIGN; device missing ->
+ * NO_DEVICE; allocation -> OOM.
+ */
+lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank,
+                             int in_features, const int* slice_out, int num_slices,
+                             lora_dtype wdtype, int max_tokens);
+
+/* Free the pool.  All work that uses it must have completed.  NULL is a no-op. */
+lora_status lora_pool_destroy(lora_pool* pool);
+
+/*
+ * Load an adapter into `slot` ([vLLM-deep] §5.3 set_lora(index, A, B): the
+ * activation step writes the slot's buffers; [TRT-LLM] "AdapterSlotManager":
+ * slots are fixed, their contents swapped).
+ *   A_slices[n]: [rank, in_features] row-major, B_slices[n]: [slice_out[n], rank]
+ *   row-major, both in the pool dtype.  A NULL pair marks a missing slice, which
+ *   contributes nothing ([TRT-LLM] "LoraConfig": missing q/k/v padded with
+ *   zeros); exactly one of the pair NULL is INVALID_ARG.
+ *   Scale: see lora_compute_scale.  With LORA_PREMULTIPLY the pool stores
+ *   round(s * B) (float32 product, one round to the pool dtype) and applies 1
+ *   afterwards ([vLLM-deep] §1 "推理优化:预合并 scaling"); otherwise it stores B and
+ *   multiplies the finished branch by s ([llama.cpp] "真正的核心").
+ * With LORA_SRC_DEVICE the sources are device pointers and the copy is enqueued
+ * on `stream`; otherwise they are host pointers and the call returns after the
+ * copy has completed.  Re-registering a slot overwrites it in stream order.
+ * Errors: pool NULL -> INVALID_ARG; slot -> SLOT; rank outside [1, max_lora_rank]
+ * -> RANK; non-finite alpha / adapter_scale -> INVALID_ARG; unknown flag bit ->
+ * INVALID_ARG; HIP failure -> HIP.
+ */
+lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* A_slices,
+                                  const void* const* B_slices, float alpha, int rank, int rslora,
+                                  float adapter_scale, unsigned flags, hipStream_t stream);
+
+/* Empty `slot`: rank 0, so tokens still routed to it contribute nothing ([TRT-LLM]
+ * "一次 decode 批次的路由": an empty slot has rank 0 and null pointers).  Enqueued on
+ * `stream`.  Errors: pool NULL -> INVALID_ARG; slot -> SLOT. */
+lora_status lora_unregister_adapter(lora_pool* pool, int slot, hipStream_t stream);
+
+/* Host mirror of a slot's table entry (synchronous, no device access): rank,
+ * scale still applied after the branch (1 when pre-multiplied), mask of present
+ * slices, and the byte offsets of the slot's A and rank-major B blocks from the
+ * pool base.  Any out pointer may be NULL. */
+lora_status lora_pool_slot_info(const lora_pool* pool, int slot, int* rank, float* scale,
+                                uint32_t* slice_mask, uint64_t* a_offset, uint64_t* bt_offset);
+
+/* Copy a slot's stored slice back to host memory (synchronous; for tests):
+ * A_host [max_lora_rank, in_features] and Bt_host [max_lora_rank, slice_out[slice]]
+ * (B transposed, rank-major), both in the pool dtype, rows >= rank zero.
+ * Either pointer may be NULL. */
+lora_status lora_pool_read_slot(const lora_pool* pool, int slot, int slice, void* A_host,
+                                void* Bt_host);
+
+/*
+ * Routing metadata for one batch ([vLLM-book] §16.4.3 LoRAKernelMeta;
+ * [TRT-LLM] "一次 decode 批次的路由": sorted_ids, per-slot counts and offsets in
+ * fixed-address buffers).  The object owns fixed-address device buffers sized for
+ * max_tokens tokens and max_slots slots, so the same addresses serve every batch.
+ * Errors: out NULL -> INVALID_ARG; max_tokens < 1 or max_slots outside
+ * [1, LORA_MAX_SLOTS] -> SHAPE; NO_DEVICE / OOM as for pools.
+ */
+lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, int max_slots);
+lora_status lora_routing_destroy(lora_routing* routing);
+
+/*
+ * Build the routing for T tokens from token_slot_ids[T] (device, int32): a slot
+ * in [0, max_slots), or -1 for no LoRA.  Any other id is routed as -1 and
+ * counted as invalid.  Key(t) = id, or S = max_slots for no LoRA (the sentinel
+ * slot of [TRT-LLM] "AdapterSlotManager").  Produces, on the device:
+ *   counts[S+1], seg_offsets[S+2] (exclusive prefix, [0] = 0, [S] = LoRA tokens,
+ *   [S+1] = T), sorted_ids[T] (token indices grouped by key, ascending within a
+ *   key), active slots (keys < S with tokens, ascending) and their number.
+ * Enqueued on `stream`; T = 0 is allowed (ids may then be NULL).
+ * Errors: routing NULL, or ids NULL with T > 0 -> INVALID_ARG; T < 0 -> SHAPE;
+ * T > max_tokens -> CAPACITY.
+ */
+lora_status lora_build_routing(lora_routing* routing, const int32_t* token_slot_ids, int T,
+                               hipStream_t stream);
+
+/* Copy the last routing back to host memory (synchronous; for tests and
+ * diagnostics).  counts[S+1], seg_offsets[S+2], sorted_ids[T], active_slots[S]
+ * (entries past num_active unspecified); any pointer may be NULL.
+ * Errors: STATE if the routing was never built. */
+lora_status lora_routing_query(const lora_routing* routing, int32_t* counts, int32_t* seg_offsets,
+                               int32_t* sorted_ids, int32_t* active_slots, int* num_active,
+                               int* n_invalid);
+
+/*
+ * Shrink ([vLLM-book] §16.4.2 lora_shrink on lora_a; [vLLM-deep] §6):
+ *   u[n][t][j] = sum_c A_slot(t)[n][j][c] * x[t][c]      (fp32 accumulate)
+ * x: device [T, in_features] in the pool dtype (else DTYPE, [TRT-LLM] "三种输入
+ * dtype": input and cache dtype must match).  u: device fp32 [num_slices, T,
+ * max_lora_rank], caller-owned; written for LoRA tokens of non-empty slots and
+ * j < rank (zero for a missing slice); other entries are left as they were.
+ * Errors: INVALID_ARG (NULL), STATE (routing not built), SHAPE (ldx < in_features,
+ * routing S != pool S), CAPACITY (T > pool max_tokens), ALIGN.
+ */
+lora_status lora_shrink(const lora_pool* pool, const lora_routing* routing, const void* x,
+                        int ldx, float* u, hipStream_t stream);
+
+/*
+ * Expand and add ([vLLM-book] §16.4.2 lora_expand on lora_b; [TRT-LLM] "前向替换":
+ * the correction is added in place onto the base output):
+ *   y[t][o_n + i] = round_y( y[t][o_n + i] + s * sum_j B_slot(t)[n][i][j] * u[n][t][j] )
+ * with fp32 arithmetic and one rounding to ydtype.  u as written by lora_shrink.
+ * y: device [T, D], in/out, ydtype = the pool dtype or LORA_F32.  Rows of no-LoRA
+ * tokens, of empty or zero-scale slots, and columns of missing slices are not
+ * written.  Errors as lora_shrink, plus DTYPE for an unsupported ydtype.
+ */
+lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, const float* u,
+                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
+
+/*
+ * Fused shrink + expand onto the caller's base output ([TRT-LLM] "前向替换":
+ * forward_with_base adds the LoRA result onto the base projection; [vLLM-book]
+ * §16.4.4 add_lora_linear).  Same result as lora_shrink then lora_expand, with the
+ * intermediate kept in the pool's workspace (split along k, partial sums added in
+ * a fixed order, so repeated calls are bitwise identical).  Long same-slot
+ * segments of bf16 pools go to the matrix-core (MFMA) kernels.
+ * Errors as lora_expand.
+ */
+lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
+
+/*
+ * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
+ * lora_build_routing, lora_shrink, lora_expand and lora_linear launch is started
+ * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start
+ * and end, on the stream it runs on.  lora_timing_report waits for the recorded
+ * events, writes per kernel id (0 routing, 1 shrink_decode, 2 expand_decode,
+ * 3 reduce_splits, 4 shrink_mfma, 5 expand_mfma) the summed milliseconds and the
+ * number of launches into total_ms[0..max_kernels) and launches[0..max_kernels), and
+ * clears the record.  lora_timing_kernel_name gives the name of an id ("" if none).
+ * Errors: INVALID_ARG for NULL arrays with max_kernels > 0; HIP if an event fails.
+ */
+lora_status lora_timing_enable(int on);
+lora_status lora_timing_report(double* total_ms, int* launches, int max_kernels);
+const char* lora_timing_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAXLORA_H */

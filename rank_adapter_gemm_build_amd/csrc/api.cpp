@@ -1,0 +1,693 @@
+// Host side of the C ABI declared in include/raxlora.h: argument checks, object
+// lifetimes, and kernel dispatch.  Every argument check runs before the first HIP
+// call, so a rejected call changes nothing and needs no device.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using rax::SlotEntry;
+
+struct lora_pool {
+  int device = 0;
+  int S = 0, Rmax = 0, k = 0, N = 0, D = 0, max_tokens = 0;
+  int d[LORA_MAX_SLICES] = {0};
+  int o[LORA_MAX_SLICES] = {0};
+  int tile0[LORA_MAX_SLICES + 1] = {0};
+  lora_dtype wdtype = LORA_BF16;
+  size_t esize = 2;
+  void* A = nullptr;
+  void* Bt = nullptr;
+  void* Bk = nullptr;
+  SlotEntry* table = nullptr;
+  float* ws = nullptr;        // split-K partials [kMaxSplit][N][max_tokens][Rmax]
+  std::vector<SlotEntry> mirror;
+};
+
+struct lora_routing {
+  int device = 0;
+  int max_tokens = 0, S = 0, mfma_min = rax::kDefaultMfmaMinSeg, tile_m = rax::kMfmaTileM;
+  int max_tiles = 0;
+  int* buf = nullptr;
+  int *counts = nullptr, *offs = nullptr, *sorted = nullptr, *active = nullptr, *tiles = nullptr,
+      *meta = nullptr;
+  int T = -1;  // tokens of the last build; -1 = never built
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lora_status fail(lora_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+lora_status ok() {
+  g_last_error.clear();
+  return LORA_OK;
+}
+
+lora_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? LORA_ERR_OOM : LORA_ERR_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+// Make `device` current for the scope, restoring the previous device after.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int device) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != device) err = hipSetDevice(device);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+lora_status check_device(int device) {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0) return fail(LORA_ERR_NO_DEVICE, "no GPU available (%s)", hipGetErrorString(e));
+  if (device < 0 || device >= n) return fail(LORA_ERR_NO_DEVICE, "device %d out of range [0, %d)", device, n);
+  return LORA_OK;
+}
+
+// ------------------------------------------------------------- kernel timing
+// When enabled, each hot-path launch takes a pair of events that hipExtLaunchKernel
+// stamps at the kernel's own start and end; lora_timing_report adds them up.
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing_records;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+rax::KTimer timer_for(int kernel) {
+  rax::KTimer t;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on) return t;
+  t.start = take_event();
+  t.stop = take_event();
+  if (!t.start || !t.stop) return rax::KTimer{};
+  g_timing_records.push_back(TimingRecord{kernel, t.start, t.stop});
+  return t;
+}
+
+const char* const kKernelNames[rax::kKernelCount] = {"routing", "shrink_decode", "expand_decode",
+                                                     "reduce_splits", "shrink_mfma", "expand_mfma"};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+rax::PoolView pool_view(const lora_pool* p) {
+  rax::PoolView v{};
+  v.A = p->A;
+  v.Bt = p->Bt;
+  v.Bk = p->Bk;
+  v.table = p->table;
+  v.S = p->S;
+  v.Rmax = p->Rmax;
+  v.k = p->k;
+  v.N = p->N;
+  v.D = p->D;
+  v.n_ctiles = p->tile0[p->N];
+  for (int n = 0; n < rax::kMaxSlices; ++n) {
+    v.d[n] = n < p->N ? p->d[n] : 0;
+    v.o[n] = n < p->N ? p->o[n] : 0;
+  }
+  for (int n = 0; n <= rax::kMaxSlices; ++n) v.tile0[n] = n <= p->N ? p->tile0[n] : p->tile0[p->N];
+  return v;
+}
+
+rax::RouteView route_view(const lora_routing* r) {
+  rax::RouteView v{};
+  v.counts = r->counts;
+  v.offs = r->offs;
+  v.sorted = r->sorted;
+  v.active = r->active;
+  v.tiles = r->tiles;
+  v.meta = r->meta;
+  v.S = r->S;
+  v.T = r->T;
+  v.mfma_min = r->mfma_min;
+  v.tile_m = r->tile_m;
+  v.max_tiles = r->max_tiles;
+  return v;
+}
+
+int chunk_width(lora_dtype t) { return 64 * (t == LORA_BF16 ? 8 : 4); }
+
+// k-split of the shrink: kDefaultSplit splits (or RAXLORA_NSPLIT) where k allows,
+// each at most kMaxChunksPerSplit 16-byte steps per lane (x stays in registers).
+// lora_pool_create guarantees k <= kMaxSplit * kMaxChunksPerSplit * chunk width.
+int choose_kc(const lora_pool* p) {
+  const int cw = chunk_width(p->wdtype);
+  const int steps = (p->k + cw - 1) / cw;
+  int nsplit = env_int("RAXLORA_NSPLIT", rax::kDefaultSplit);
+  if (nsplit < 1) nsplit = 1;
+  if (nsplit > steps) nsplit = steps;
+  int per = (steps + nsplit - 1) / nsplit;
+  if (per > rax::kMaxChunksPerSplit) per = rax::kMaxChunksPerSplit;
+  return per * cw;
+}
+
+// Common checks of shrink / expand / linear.
+lora_status check_pair(const lora_pool* pool, const lora_routing* routing) {
+  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
+  if (routing->T < 0) return fail(LORA_ERR_STATE, "routing was never built");
+  if (routing->S != pool->S)
+    return fail(LORA_ERR_SHAPE, "routing has %d slots, pool has %d", routing->S, pool->S);
+  if (routing->device != pool->device)
+    return fail(LORA_ERR_INVALID_ARG, "routing on device %d, pool on device %d", routing->device, pool->device);
+  if (routing->T > pool->max_tokens)
+    return fail(LORA_ERR_CAPACITY, "T = %d exceeds the pool's max_tokens = %d", routing->T, pool->max_tokens);
+  return LORA_OK;
+}
+
+lora_status check_x(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx) {
+  if (routing->T > 0 && !x) return fail(LORA_ERR_INVALID_ARG, "x is NULL");
+  if (ldx < pool->k) return fail(LORA_ERR_SHAPE, "ldx = %d < in_features = %d", ldx, pool->k);
+  if (ldx % 8 != 0 || !aligned16(x)) return fail(LORA_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
+  return LORA_OK;
+}
+
+lora_status check_y(const lora_pool* pool, const lora_routing* routing, const void* y, int ldy,
+                    lora_dtype ydtype) {
+  if (routing->T > 0 && !y) return fail(LORA_ERR_INVALID_ARG, "y is NULL");
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown ydtype %d", (int)ydtype);
+  if (ydtype != pool->wdtype && ydtype != LORA_F32)
+    return fail(LORA_ERR_DTYPE, "y must be the pool dtype or float32");
+  if (ldy < pool->D) return fail(LORA_ERR_SHAPE, "ldy = %d < output width %d", ldy, pool->D);
+  if (ldy % 8 != 0 || !aligned16(y)) return fail(LORA_ERR_ALIGN, "y must be 16-byte aligned with ldy a multiple of 8");
+  return LORA_OK;
+}
+
+// Workspace of split partials: [nsplit][N][max_tokens][Rmax], rows by sorted position.
+rax::UView workspace_view(const lora_pool* p, int kc) {
+  const int nsplit = (p->k + kc - 1) / kc;
+  return rax::UView{p->ws, (long long)p->N * p->max_tokens * p->Rmax, (long long)p->max_tokens * p->Rmax,
+                    p->Rmax, nsplit, 0};
+}
+
+// The caller's u: [N][T][Rmax], rows by token index, one split.
+rax::UView caller_u_view(const lora_pool* p, const lora_routing* r, float* u) {
+  return rax::UView{u, 0, (long long)r->T * p->Rmax, p->Rmax, 1, 1};
+}
+
+bool use_mfma(const lora_pool* pool) {
+  return rax::kHaveMfmaPath && pool->wdtype == LORA_BF16 && env_int("RAXLORA_DISABLE_MFMA", 0) == 0;
+}
+
+lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                       const rax::UView& U, int kc, hipStream_t stream) {
+  const rax::PoolView P = pool_view(pool);
+  const rax::RouteView R = route_view(routing);
+  const int mf = use_mfma(pool) ? 1 : 0;
+  hipError_t e = rax::launch_shrink(pool->wdtype, P, R, x, ldx, U, kc, mf, stream, timer_for(rax::kKShrink));
+  if (e != hipSuccess) return hip_fail(e, "shrink launch");
+  if (mf && routing->T >= routing->mfma_min) {
+    e = rax::launch_shrink_mfma(P, R, x, ldx, U, kc, stream, timer_for(rax::kKShrinkMfma));
+    if (e != hipSuccess) return hip_fail(e, "matrix-core shrink launch");
+  }
+  return LORA_OK;
+}
+
+lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const rax::UView& U,
+                       void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
+  const rax::PoolView P = pool_view(pool);
+  const rax::RouteView R = route_view(routing);
+  const int mf = use_mfma(pool) ? 1 : 0;
+  hipError_t e = rax::launch_expand(pool->wdtype, ydtype, P, R, U, y, ldy, mf, stream, timer_for(rax::kKExpand));
+  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  if (mf && routing->T >= routing->mfma_min) {
+    e = rax::launch_expand_mfma(ydtype, P, R, U, y, ldy, stream, timer_for(rax::kKExpandMfma));
+    if (e != hipSuccess) return hip_fail(e, "matrix-core expand launch");
+  }
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_last_error(void) { return g_last_error.c_str(); }
+
+const char* lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
+    case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE";
+    case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE";
+    case LORA_ERR_RANK: return "LORA_ERR_RANK";
+    case LORA_ERR_SLOT: return "LORA_ERR_SLOT";
+    case LORA_ERR_CAPACITY: return "LORA_ERR_CAPACITY";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+    case LORA_ERR_OOM: return "LORA_ERR_OOM";
+    case LORA_ERR_NO_DEVICE: return "LORA_ERR_NO_DEVICE";
+    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN";
+    case LORA_ERR_STATE: return "LORA_ERR_STATE";
+    default: return "LORA_ERR_UNKNOWN";
+  }
+}
+
+lora_status lora_compute_scale(float alpha, int rank, int rslora, float adapter_scale, float* out_scale) {
+  if (!out_scale) return fail(LORA_ERR_INVALID_ARG, "out_scale is NULL");
+  if (rank < 1) return fail(LORA_ERR_RANK, "rank %d < 1", rank);
+  if (!std::isfinite(alpha) || !std::isfinite(adapter_scale))
+    return fail(LORA_ERR_INVALID_ARG, "alpha and adapter_scale must be finite");
+  const double a = alpha, c = adapter_scale;
+  double sigma;
+  if (a == 0.0)
+    sigma = c;                                   // alpha absent: the caller's scale alone
+  else if (rslora)
+    sigma = c * a / std::sqrt((double)rank);     // rank-stabilised
+  else
+    sigma = c * a / (double)rank;
+  const float s = (float)sigma;
+  if (!std::isfinite(s)) return fail(LORA_ERR_INVALID_ARG, "scale overflows float");
+  *out_scale = s;
+  return ok();
+}
+
+lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank,
+                             int in_features, const int* slice_out, int num_slices,
+                             lora_dtype wdtype, int max_tokens) {
+  if (!out || !slice_out) return fail(LORA_ERR_INVALID_ARG, "out and slice_out must not be NULL");
+  *out = nullptr;
+  if (max_slots < 1 || max_slots > LORA_MAX_SLOTS)
+    return fail(LORA_ERR_SHAPE, "max_slots %d outside [1, %d]", max_slots, LORA_MAX_SLOTS);
+  if (max_lora_rank < 1 || max_lora_rank > LORA_MAX_RANK)
+    return fail(LORA_ERR_SHAPE, "max_lora_rank %d outside [1, %d]", max_lora_rank, LORA_MAX_RANK);
+  if (in_features < 1) return fail(LORA_ERR_SHAPE, "in_features %d < 1", in_features);
+  if (num_slices < 1 || num_slices > LORA_MAX_SLICES)
+    return fail(LORA_ERR_SHAPE, "num_slices %d outside [1, %d]", num_slices, LORA_MAX_SLICES);
+  if (max_tokens < 1) return fail(LORA_ERR_SHAPE, "max_tokens %d < 1", max_tokens);
+  if (wdtype != LORA_F32 && wdtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown wdtype %d", (int)wdtype);
+  long long D = 0;
+  for (int n = 0; n < num_slices; ++n) {
+    if (slice_out[n] < 1) return fail(LORA_ERR_SHAPE, "slice %d width %d < 1", n, slice_out[n]);
+    if (slice_out[n] % 8) return fail(LORA_ERR_ALIGN, "slice %d width %d not a multiple of 8", n, slice_out[n]);
+    D += slice_out[n];
+  }
+  if (D > (1LL << 30)) return fail(LORA_ERR_SHAPE, "total output width too large");
+  if (in_features % 8) return fail(LORA_ERR_ALIGN, "in_features %d not a multiple of 8", in_features);
+  if (in_features > rax::kMaxSplit * rax::kMaxChunksPerSplit * chunk_width(wdtype))
+    return fail(LORA_ERR_SHAPE, "in_features %d above the supported %d", in_features,
+                rax::kMaxSplit * rax::kMaxChunksPerSplit * chunk_width(wdtype));
+
+  lora_status st = check_device(device);
+  if (st != LORA_OK) return st;
+  DeviceGuard g(device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+
+  lora_pool* p = new lora_pool();
+  p->device = device;
+  p->S = max_slots;
+  p->Rmax = max_lora_rank;
+  p->k = in_features;
+  p->N = num_slices;
+  p->max_tokens = max_tokens;
+  p->wdtype = wdtype;
+  p->esize = wdtype == LORA_BF16 ? 2 : 4;
+  int o = 0, tiles = 0;
+  for (int n = 0; n < num_slices; ++n) {
+    p->d[n] = slice_out[n];
+    p->o[n] = o;
+    p->tile0[n] = tiles;
+    o += slice_out[n];
+    tiles += (slice_out[n] + rax::kTileCols - 1) / rax::kTileCols;
+  }
+  p->D = o;
+  p->tile0[num_slices] = tiles;
+  p->mirror.assign(max_slots, SlotEntry{0, 0.f, 0u, 0});
+
+  const size_t a_bytes = (size_t)max_slots * num_slices * max_lora_rank * in_features * p->esize;
+  const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
+  const size_t ws_bytes = (size_t)rax::kMaxSplit * num_slices * max_tokens * max_lora_rank * sizeof(float);
+  hipError_t e;
+  if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
+      (e = hipMalloc(&p->Bk, b_bytes)) != hipSuccess ||
+      (e = hipMalloc((void**)&p->table, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
+      (e = hipMalloc((void**)&p->ws, ws_bytes)) != hipSuccess) {
+    lora_pool_destroy(p);
+    return hip_fail(e, "pool allocation");
+  }
+  // empty slots read as rank 0; weights start at zero so padding rows are inert
+  if ((e = hipMemset(p->A, 0, a_bytes)) != hipSuccess || (e = hipMemset(p->Bt, 0, b_bytes)) != hipSuccess ||
+      (e = hipMemset(p->Bk, 0, b_bytes)) != hipSuccess ||
+      (e = hipMemset(p->table, 0, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    lora_pool_destroy(p);
+    return hip_fail(e, "pool initialisation");
+  }
+  *out = p;
+  return ok();
+}
+
+lora_status lora_pool_destroy(lora_pool* p) {
+  if (!p) return ok();
+  DeviceGuard g(p->device);
+  if (p->A) (void)hipFree(p->A);
+  if (p->Bt) (void)hipFree(p->Bt);
+  if (p->Bk) (void)hipFree(p->Bk);
+  if (p->table) (void)hipFree(p->table);
+  if (p->ws) (void)hipFree(p->ws);
+  delete p;
+  return ok();
+}
+
+lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* A_slices,
+                                  const void* const* B_slices, float alpha, int rank, int rslora,
+                                  float adapter_scale, unsigned flags, hipStream_t stream) {
+  if (!pool) return fail(LORA_ERR_INVALID_ARG, "pool is NULL");
+  if (slot < 0 || slot >= pool->S) return fail(LORA_ERR_SLOT, "slot %d outside [0, %d)", slot, pool->S);
+  if (rank < 1 || rank > pool->Rmax)
+    return fail(LORA_ERR_RANK, "rank %d outside [1, max_lora_rank = %d]", rank, pool->Rmax);
+  if (flags & ~(LORA_SRC_DEVICE | LORA_PREMULTIPLY)) return fail(LORA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (!A_slices || !B_slices) return fail(LORA_ERR_INVALID_ARG, "A_slices and B_slices must not be NULL");
+  uint32_t mask = 0;
+  for (int n = 0; n < pool->N; ++n) {
+    const bool a = A_slices[n] != nullptr, b = B_slices[n] != nullptr;
+    if (a != b) return fail(LORA_ERR_INVALID_ARG, "slice %d: lora_a and lora_b must both be given or both be NULL", n);
+    if (a) mask |= 1u << n;
+  }
+  float s = 0.f;
+  lora_status st = lora_compute_scale(alpha, rank, rslora, adapter_scale, &s);
+  if (st != LORA_OK) return st;
+  const bool premul = (flags & LORA_PREMULTIPLY) != 0;
+  const bool on_device = (flags & LORA_SRC_DEVICE) != 0;
+
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const size_t es = pool->esize;
+  std::vector<void*> staging;
+  auto cleanup = [&]() {
+    for (void* q : staging) (void)hipFree(q);
+  };
+  hipError_t e = hipSuccess;
+  for (int n = 0; n < pool->N; ++n) {
+    const void* a_src = A_slices[n];
+    const void* b_src = B_slices[n];
+    if (a_src && !on_device) {
+      const size_t abytes = (size_t)rank * pool->k * es, bbytes = (size_t)pool->d[n] * rank * es;
+      void *da = nullptr, *db = nullptr;
+      if ((e = hipMalloc(&da, abytes)) != hipSuccess) { cleanup(); return hip_fail(e, "staging"); }
+      staging.push_back(da);
+      if ((e = hipMalloc(&db, bbytes)) != hipSuccess) { cleanup(); return hip_fail(e, "staging"); }
+      staging.push_back(db);
+      if ((e = hipMemcpy(da, a_src, abytes, hipMemcpyHostToDevice)) != hipSuccess ||
+          (e = hipMemcpy(db, b_src, bbytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        cleanup();
+        return hip_fail(e, "copy of adapter weights");
+      }
+      a_src = da;
+      b_src = db;
+    }
+    char* A_dst = static_cast<char*>(pool->A) + (((size_t)slot * pool->N + n) * pool->Rmax) * pool->k * es;
+    char* Bt_dst = static_cast<char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[n]) * es;
+    char* Bk_dst = static_cast<char*>(pool->Bk) + ((size_t)slot * pool->D + pool->o[n]) * pool->Rmax * es;
+    e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bt_dst, Bk_dst, rank, pool->Rmax,
+                               pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, stream);
+    if (e != hipSuccess) { cleanup(); return hip_fail(e, "pack launch"); }
+  }
+  const SlotEntry entry{rank, premul ? 1.0f : s, mask, 0};
+  e = rax::launch_set_slot(pool->table, slot, entry, stream);
+  if (e != hipSuccess) { cleanup(); return hip_fail(e, "slot table update"); }
+  if (!staging.empty()) {
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) { cleanup(); return hip_fail(e, "registration sync"); }
+    cleanup();
+  }
+  pool->mirror[slot] = entry;
+  return ok();
+}
+
+lora_status lora_unregister_adapter(lora_pool* pool, int slot, hipStream_t stream) {
+  if (!pool) return fail(LORA_ERR_INVALID_ARG, "pool is NULL");
+  if (slot < 0 || slot >= pool->S) return fail(LORA_ERR_SLOT, "slot %d outside [0, %d)", slot, pool->S);
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const SlotEntry entry{0, 0.f, 0u, 0};
+  hipError_t e = rax::launch_set_slot(pool->table, slot, entry, stream);
+  if (e != hipSuccess) return hip_fail(e, "slot table update");
+  pool->mirror[slot] = entry;
+  return ok();
+}
+
+lora_status lora_pool_slot_info(const lora_pool* pool, int slot, int* rank, float* scale,
+                                uint32_t* slice_mask, uint64_t* a_offset, uint64_t* bt_offset) {
+  if (!pool) return fail(LORA_ERR_INVALID_ARG, "pool is NULL");
+  if (slot < 0 || slot >= pool->S) return fail(LORA_ERR_SLOT, "slot %d outside [0, %d)", slot, pool->S);
+  const SlotEntry& e = pool->mirror[slot];
+  if (rank) *rank = e.rank;
+  if (scale) *scale = e.scale;
+  if (slice_mask) *slice_mask = e.slice_mask;
+  if (a_offset) *a_offset = (uint64_t)slot * pool->N * pool->Rmax * pool->k * pool->esize;
+  if (bt_offset) *bt_offset = (uint64_t)slot * pool->Rmax * pool->D * pool->esize;
+  return ok();
+}
+
+lora_status lora_pool_read_slot(const lora_pool* pool, int slot, int slice, void* A_host, void* Bt_host) {
+  if (!pool) return fail(LORA_ERR_INVALID_ARG, "pool is NULL");
+  if (slot < 0 || slot >= pool->S) return fail(LORA_ERR_SLOT, "slot %d outside [0, %d)", slot, pool->S);
+  if (slice < 0 || slice >= pool->N) return fail(LORA_ERR_SHAPE, "slice %d outside [0, %d)", slice, pool->N);
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const size_t es = pool->esize;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (A_host) {
+    const char* src = static_cast<const char*>(pool->A) + (((size_t)slot * pool->N + slice) * pool->Rmax) * pool->k * es;
+    if ((e = hipMemcpy(A_host, src, (size_t)pool->Rmax * pool->k * es, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "copy A");
+  }
+  if (Bt_host) {
+    const char* src = static_cast<const char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[slice]) * es;
+    if ((e = hipMemcpy2D(Bt_host, (size_t)pool->d[slice] * es, src, (size_t)pool->D * es,
+                         (size_t)pool->d[slice] * es, pool->Rmax, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "copy Bt");
+  }
+  return ok();
+}
+
+lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, int max_slots) {
+  if (!out) return fail(LORA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_tokens < 1) return fail(LORA_ERR_SHAPE, "max_tokens %d < 1", max_tokens);
+  if (max_slots < 1 || max_slots > LORA_MAX_SLOTS)
+    return fail(LORA_ERR_SHAPE, "max_slots %d outside [1, %d]", max_slots, LORA_MAX_SLOTS);
+  lora_status st = check_device(device);
+  if (st != LORA_OK) return st;
+  DeviceGuard g(device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  lora_routing* r = new lora_routing();
+  r->device = device;
+  r->max_tokens = max_tokens;
+  r->S = max_slots;
+  r->mfma_min = env_int("RAXLORA_MFMA_MIN_SEG", rax::kDefaultMfmaMinSeg);
+  if (r->mfma_min < 1) r->mfma_min = 1;
+  r->tile_m = rax::kMfmaTileM;
+  // sum over long segments of ceil(len / tile_m) <= T / tile_m + (number of long segments)
+  r->max_tiles = max_tokens / r->tile_m + 1 + max_slots;
+  const size_t words = (size_t)(max_slots + 1) + (max_slots + 2) + max_tokens + max_slots +
+                       3 * (size_t)r->max_tiles + rax::kMetaWords;
+  hipError_t e = hipMalloc((void**)&r->buf, words * sizeof(int));
+  if (e != hipSuccess) {
+    delete r;
+    return hip_fail(e, "routing allocation");
+  }
+  if ((e = hipMemset(r->buf, 0, words * sizeof(int))) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
+    (void)hipFree(r->buf);
+    delete r;
+    return hip_fail(e, "routing initialisation");
+  }
+  int* w = r->buf;
+  r->counts = w; w += max_slots + 1;
+  r->offs = w; w += max_slots + 2;
+  r->sorted = w; w += max_tokens;
+  r->active = w; w += max_slots;
+  r->tiles = w; w += 3 * r->max_tiles;
+  r->meta = w;
+  *out = r;
+  return ok();
+}
+
+lora_status lora_routing_destroy(lora_routing* r) {
+  if (!r) return ok();
+  DeviceGuard g(r->device);
+  if (r->buf) (void)hipFree(r->buf);
+  delete r;
+  return ok();
+}
+
+lora_status lora_build_routing(lora_routing* r, const int32_t* ids, int T, hipStream_t stream) {
+  if (!r) return fail(LORA_ERR_INVALID_ARG, "routing is NULL");
+  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
+  if (T > r->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, r->max_tokens);
+  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
+  DeviceGuard g(r->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  hipError_t e = rax::launch_routing(ids, T, r->S, r->mfma_min, r->tile_m, r->max_tiles, r->counts,
+                                     r->offs, r->sorted, r->active, r->tiles, r->meta, stream,
+                                     timer_for(rax::kKRouting));
+  if (e != hipSuccess) return hip_fail(e, "routing launch");
+  r->T = T;
+  return ok();
+}
+
+lora_status lora_routing_query(const lora_routing* r, int32_t* counts, int32_t* seg_offsets,
+                               int32_t* sorted_ids, int32_t* active_slots, int* num_active,
+                               int* n_invalid) {
+  if (!r) return fail(LORA_ERR_INVALID_ARG, "routing is NULL");
+  if (r->T < 0) return fail(LORA_ERR_STATE, "routing was never built");
+  DeviceGuard g(r->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  int meta[rax::kMetaWords];
+  if ((e = hipMemcpy(meta, r->meta, sizeof meta, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "copy meta");
+  if (counts && (e = hipMemcpy(counts, r->counts, (r->S + 1) * sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy counts");
+  if (seg_offsets && (e = hipMemcpy(seg_offsets, r->offs, (r->S + 2) * sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy offsets");
+  if (sorted_ids && r->T > 0 &&
+      (e = hipMemcpy(sorted_ids, r->sorted, (size_t)r->T * sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy sorted ids");
+  if (active_slots && (e = hipMemcpy(active_slots, r->active, r->S * sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy active slots");
+  if (num_active) *num_active = meta[rax::kMetaActive];
+  if (n_invalid) *n_invalid = meta[rax::kMetaInvalid];
+  return ok();
+}
+
+lora_status lora_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                        float* u, hipStream_t stream) {
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_x(pool, routing, x, ldx)) != LORA_OK) return st;
+  if (routing->T > 0 && !u) return fail(LORA_ERR_INVALID_ARG, "u is NULL");
+  if (!aligned16(u)) return fail(LORA_ERR_ALIGN, "u must be 16-byte aligned");
+  if (routing->T == 0) return ok();
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  // split partials into the workspace, then added in split order into the caller's
+  // u [N][T][Rmax] (rows by token index)
+  const int kc = choose_kc(pool);
+  const rax::UView W = workspace_view(pool, kc);
+  st = run_shrink(pool, routing, x, ldx, W, kc, stream);
+  if (st != LORA_OK) return st;
+  const rax::UView U = caller_u_view(pool, routing, u);
+  hipError_t e = rax::launch_reduce_splits(pool_view(pool), route_view(routing), W, U, stream,
+                                           timer_for(rax::kKReduce));
+  if (e != hipSuccess) return hip_fail(e, "split reduction launch");
+  return ok();
+}
+
+lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, const float* u, void* y,
+                        int ldy, lora_dtype ydtype, hipStream_t stream) {
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_y(pool, routing, y, ldy, ydtype)) != LORA_OK) return st;
+  if (routing->T > 0 && !u) return fail(LORA_ERR_INVALID_ARG, "u is NULL");
+  if (!aligned16(u)) return fail(LORA_ERR_ALIGN, "u must be 16-byte aligned");
+  if (routing->T == 0) return ok();
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const rax::UView U = caller_u_view(pool, routing, const_cast<float*>(u));
+  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
+}
+
+lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_x(pool, routing, x, ldx)) != LORA_OK) return st;
+  if ((st = check_y(pool, routing, y, ldy, ydtype)) != LORA_OK) return st;
+  if (routing->T == 0) return ok();
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const int kc = choose_kc(pool);
+  const rax::UView W = workspace_view(pool, kc);
+  if ((st = run_shrink(pool, routing, x, ldx, W, kc, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
+}
+
+lora_status lora_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = on != 0;
+  return ok();
+}
+
+const char* lora_timing_kernel_name(int kernel) {
+  return (kernel >= 0 && kernel < rax::kKernelCount) ? kKernelNames[kernel] : "";
+}
+
+lora_status lora_timing_report(double* total_ms, int* launches, int max_kernels) {
+  if (max_kernels < 0 || (max_kernels > 0 && (!total_ms || !launches)))
+    return fail(LORA_ERR_INVALID_ARG, "total_ms and launches must hold max_kernels entries");
+  std::vector<TimingRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    recs.swap(g_timing_records);
+  }
+  for (int i = 0; i < max_kernels; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  lora_status st = LORA_OK;
+  for (const TimingRecord& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == LORA_OK) st = hip_fail(e, "timing event");
+    if (e == hipSuccess && r.kernel < max_kernels) {
+      total_ms[r.kernel] += ms;
+      launches[r.kernel] += 1;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (const TimingRecord& r : recs) {
+      g_free_events.push_back(r.start);
+      g_free_events.push_back(r.stop);
+    }
+  }
+  return st == LORA_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// Device helpers for the LoRA kernels: number formats, 16-byte lane loads, the
+// wave reduce-scatter and XCD-aware block numbering.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+// Launch through hipExtLaunchKernelGGL when the timer carries events (the events are
+// then stamped at the kernel's own start and end), else a plain launch.
+#define RAX_LAUNCH(tm, kernel, grid, block, shmem, stream, ...)                                  \
+  do {                                                                                         \
+    if ((tm).start)                                                                            \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm).start, (tm).stop, 0u,      \
+                            __VA_ARGS__);                                                      \
+    else                                                                                       \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                     \
+  } while (0)
+
+namespace rax {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bfloat16
+// bfloat16 is the upper half of a float32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// -------------------------------------------------------------- lane chunks
+// Every lane moves 16 bytes per load: 8 bf16 or 4 fp32 elements.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { static constexpr int kPerChunk = 8; };
+template <> struct Elem<float> { static constexpr int kPerChunk = 4; };
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// v if ok else zero, component-wise (a ternary on the whole vector makes the compiler
+// pick between two stack copies through scratch memory)
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool ok) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+// 16-byte chunk -> 8 floats (bf16 pairs), or 4 floats into two chunks for fp32
+__device__ __forceinline__ void unpack8(uint4 w, float (&v)[8]) {
+  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+  v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+  v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// acc + <a, b> over one 16-byte chunk
+__device__ __forceinline__ float chunk_dot(uint4 a, uint4 b, float acc, uint16_t) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float chunk_dot(uint4 a, uint4 b, float acc, float) {
+  acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+  acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  return acc;
+}
+
+// 8 consecutive elements starting at p (16-byte aligned) as floats; zeros if !ok
+__device__ __forceinline__ void load8f(const uint16_t* p, bool ok, float (&v)[8]) {
+  uint4 w = ok ? ld16(p) : make_uint4(0, 0, 0, 0);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void load8f(const float* p, bool ok, float (&v)[8]) {
+  uint4 a = ok ? ld16(p) : make_uint4(0, 0, 0, 0);
+  uint4 b = ok ? ld16(p + 4) : make_uint4(0, 0, 0, 0);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ void store8f(uint16_t* p, const float (&v)[8]) {
+  st16(p, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])));
+}
+__device__ __forceinline__ void store8f(float* p, const float (&v)[8]) {
+  st16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
+  st16(p + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])));
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Reduce-scatter across the 64 lanes of a wave: on entry every lane holds 64
+// partial values v[0..64); on exit v[0] of lane l holds the sum over all lanes of
+// entry value l.  Six exchange stages with partners 32, 16, 8, 4, 2, 1 lanes away:
+// at the stage of width H a lane keeps the half of its values whose index bit H
+// equals its own lane bit H and adds the partner's copy of that half, so the work
+// halves at every stage (63 exchanges in all instead of 64 six-step reductions).
+// The two cross-row stages use the gfx950 lane-swap instructions (v_permlane32_swap
+// swaps the upper 32 lanes of its first operand with the lower 32 lanes of its
+// second; v_permlane16_swap does the same for odd and even 16-lane rows), so one
+// swap hands each lane both addends; the in-row stages use DPP lane moves (row
+// mirror, half-row mirror, and two quad permutations: any pairing across the two
+// halves of the group works, all four are involutions).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int H>
+__device__ __forceinline__ void reduce_scatter_stage(float (&v)[64], int lane) {
+#if defined(RAX_REDUCE_WITH_SHUFFLES)
+  const bool upper = (lane & H) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = upper ? v[i] : v[i + H];
+    const float keep = upper ? v[i + H] : v[i];
+    v[i] = keep + __shfl_xor(send, H);
+  }
+#else
+  if constexpr (H == 32 || H == 16) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const auto r = (H == 32)
+          ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + H]), false, false)
+          : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + H]), false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    constexpr int CTRL = H == 8 ? 0x140 : H == 4 ? 0x141 : H == 2 ? 0x4E : 0xB1;
+    const bool upper = (lane & H) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = upper ? v[i] : v[i + H];
+      const float keep = upper ? v[i + H] : v[i];
+      v[i] = keep + dpp_move<CTRL>(send);
+    }
+  }
+#endif
+}
+
+__device__ __forceinline__ void reduce_scatter64(float (&v)[64]) {
+  const int lane = lane_id();
+  reduce_scatter_stage<32>(v, lane);
+  reduce_scatter_stage<16>(v, lane);
+  reduce_scatter_stage<8>(v, lane);
+  reduce_scatter_stage<4>(v, lane);
+  reduce_scatter_stage<2>(v, lane);
+  reduce_scatter_stage<1>(v, lane);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+// Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Renumber so that consecutive logical indices share an XCD and its L2: with the
+// grid padded to 8 * per blocks, logical = (b % 8) * per + b / 8 is a bijection on
+// [0, 8 * per); callers skip logical indices past their item count.
+__device__ __forceinline__ int xcd_logical_block(int b, int per) {
+  return (b & 7) * per + (b >> 3);
+}
+
+}  // namespace rax

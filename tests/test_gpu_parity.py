@@ -1,0 +1,404 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: routing and index metadata bit-exact; fp32 max-abs error <= 1e-4; bf16
+normwise relative error <= 2e-2 with fp32 accumulation, checked on the branch
+output delta (base 0) and on y; exact-integer inputs bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle.lora_oracle as O
+from synthetic import small_case, workload
+
+from lora_cases import (bits, check_close, from_device, make_pool, make_routing, oracle_adapters,
+                         to_device, to_f64, y_base_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import rank_adapter_gemm_build_amd as m
+    return m
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ routing
+def _routing_case(rx, ids, S, max_tokens=None):
+    import torch
+    T = len(ids)
+    R = rx.Routing(0, max_tokens or max(T, 1), S)
+    t = torch.tensor(np.asarray(ids, dtype=np.int32), device="cuda")
+    R.build(t)
+    got = R.query()
+    ref = O.route_by_counting(list(ids), S)
+    assert np.array_equal(got["counts"], ref.counts)
+    assert np.array_equal(got["seg_offsets"], ref.seg_offsets)
+    assert np.array_equal(got["sorted_ids"], ref.sorted_ids)
+    assert np.array_equal(got["active_slots"], ref.active_slots)
+    assert got["num_active"] == ref.num_active and got["n_invalid"] == ref.n_invalid
+    R.close()
+
+
+def test_routing_golden(rx):
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "routing_cases.json")) as f:
+        for c in json.load(f)["cases"]:
+            _routing_case(rx, c["ids"], c["S"])
+
+
+@pytest.mark.parametrize("T,S,seed", [(1, 1, 0), (7, 3, 1), (64, 8, 2), (1000, 64, 3), (4096, 128, 4),
+                                      (3333, 1024, 5), (20000, 17, 6), (513, 2, 7)])
+def test_routing_random(rx, T, S, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, S, size=T)
+    bad = rng.random(T) < 0.05
+    ids[bad] = rng.choice([S, S + 3, -2, -77], size=int(bad.sum()))
+    _log(f"routing T={T} S={S}")
+    _routing_case(rx, ids, S)
+
+
+def test_routing_edges(rx):
+    _routing_case(rx, [], 4)                       # empty batch
+    _routing_case(rx, [-1] * 100, 4)               # no LoRA token
+    _routing_case(rx, [3] * 777, 4)                # one segment
+    _routing_case(rx, list(range(16)) * 4, 16, max_tokens=64)   # T == max_tokens
+    _routing_case(rx, sorted(np.random.default_rng(9).integers(0, 32, 4352).tolist()), 32)  # prefill-like
+
+
+@pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
+def test_routing_workloads(rx, num):
+    W = workload(num)
+    _routing_case(rx, W.ids.tolist(), W.S)
+
+
+# -------------------------------------------------------------- registration
+@pytest.mark.parametrize("dtype,premultiply", [("bf16", False), ("bf16", True), ("f32", False), ("f32", True)])
+def test_registration_bit_exact(rx, dtype, premultiply):
+    W = small_case(11, T=8, S=4, k=136, slices=[40, 24], Rmax=12, dtype=dtype, alpha_scale=3.0,
+                   rslora=True)
+    mod = W.modules[0]
+    pool = make_pool(rx, W, mod, premultiply=premultiply)
+    ads = oracle_adapters(W, mod, premultiply=premultiply)
+    for s, r in W.ranks.items():
+        info = pool.slot_info(s)
+        assert info["rank"] == r
+        want_s = 1.0 if premultiply else float(O.lora_scale(W.alpha[s], r, W.rslora, W.adapter_scale))
+        assert np.float32(info["scale"]).view(np.uint32) == np.float32(want_s).view(np.uint32)
+        for n, d in enumerate(mod.slices):
+            A, Bt = pool.read_slot(s, n)
+            Bn, _ = O.effective_b(ads[s], n, dtype)
+            assert np.array_equal(to_f64(A[:r], dtype), to_f64(mod.A[s][n], dtype))
+            assert not to_f64(A[r:], dtype).any()
+            assert np.array_equal(to_f64(Bt[:r], dtype), Bn.T), (s, n)
+            assert not to_f64(Bt[r:], dtype).any()
+    pool.unregister(1)
+    assert pool.slot_info(1)["rank"] == 0
+    pool.close()
+
+
+def test_registration_device_sources_match_host(rx):
+    import torch
+    W = small_case(12, T=8, S=3, k=64, slices=[32], Rmax=8)
+    mod = W.modules[0]
+    p1 = make_pool(rx, W, mod, device_src=False)
+    p2 = make_pool(rx, W, mod, device_src=True)
+    torch.cuda.synchronize()
+    for s in W.ranks:
+        a1, b1 = p1.read_slot(s, 0)
+        a2, b2 = p2.read_slot(s, 0)
+        assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+    p1.close(); p2.close()
+
+
+# ------------------------------------------------------------------ linear
+SMALL = [
+    # seed, T, S, k, slices, Rmax, dtype, invalid
+    (21, 37, 5, 520, [136, 24], 16, "bf16", 3),
+    (22, 64, 8, 4096, [4096], 16, "bf16", 0),
+    (23, 19, 3, 1032, [520], 64, "bf16", 2),
+    (24, 45, 6, 264, [40, 8, 16], 9, "f32", 2),
+    (25, 5, 2, 8, [8], 4, "f32", 0),
+    (26, 130, 4, 2056, [1544], 32, "bf16", 0),
+    (27, 300, 9, 1024, [1024, 512], 24, "bf16", 5),
+    (28, 33, 4, 14336, [4096], 16, "bf16", 0),
+]
+
+
+def _run_linear(rx, W, mod, y0_bits, ydtype, premultiply=False):
+    import torch
+    pool = make_pool(rx, W, mod, premultiply=premultiply)
+    R, ids = make_routing(rx, W)
+    x = to_device(mod.x, W.dtype)
+    y = to_device(y0_bits, ydtype)
+    rx.linear(pool, R, x, y)
+    torch.cuda.synchronize()
+    out = y
+    pool.close(); R.close()
+    return out
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"seed{c[0]}" for c in SMALL])
+@pytest.mark.parametrize("premultiply", [False, True])
+def test_linear_small(rx, case, premultiply):
+    seed, T, S, k, slices, Rmax, dtype, invalid = case
+    _log(f"linear seed={seed} T={T} S={S} k={k} slices={slices} Rmax={Rmax} {dtype} pre={premultiply}")
+    W = small_case(seed, T=T, S=S, k=k, slices=slices, Rmax=Rmax, dtype=dtype, invalid=invalid)
+    mod = W.modules[0]
+    ads = oracle_adapters(W, mod, premultiply=premultiply)
+    x64 = to_f64(mod.x, dtype)
+    D = sum(slices)
+    # branch alone (base 0), output in fp32 for bf16 pools to isolate the branch error
+    zero = np.zeros((T, D), dtype=np.float32)
+    y = _run_linear(rx, W, mod, zero, "f32", premultiply)
+    ref = O.lora_apply(x64, np.zeros((T, D)), ads, slices, W.ids, S, dtype, max_rank=Rmax)
+    check_close(from_device(y), ref, dtype, "delta")
+    # onto a base output in the pool dtype
+    yb = mod.y_base
+    y = _run_linear(rx, W, mod, yb, dtype, premultiply)
+    ref = O.lora_apply(x64, to_f64(yb, dtype), ads, slices, W.ids, S, dtype, max_rank=Rmax)
+    check_close(from_device(y), ref, dtype, "y")
+    # rows with no LoRA are bit-untouched
+    keys = np.where((W.ids >= 0) & (W.ids < S), W.ids, S)
+    rows = keys == S
+    assert np.array_equal(bits(y)[rows], (yb.view(np.uint32) if dtype == "f32" else yb)[rows])
+
+
+def _integer_workload(seed, T, S, k, slices, Rmax, dtype):
+    """Small integers: every partial sum and output is exact in fp32 and in bf16."""
+    rng = np.random.default_rng(seed)
+    W = small_case(seed, T=T, S=S, k=k, slices=slices, Rmax=Rmax, dtype=dtype,
+                   ranks={s: int(rng.integers(1, min(Rmax, 4) + 1)) for s in range(S)})
+    enc = (lambda a: O.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))) if dtype == "bf16" else \
+          (lambda a: np.asarray(a, dtype=np.float32))
+    mod = W.modules[0]
+    for s, r in W.ranks.items():
+        for n, d in enumerate(slices):
+            A = np.zeros((r, k))
+            for j in range(r):
+                cols = rng.choice(k, size=min(8, k), replace=False)
+                A[j, cols] = rng.integers(-1, 2, size=len(cols))
+            mod.A[s][n] = enc(A)
+            mod.B[s][n] = enc(rng.integers(-1, 2, size=(d, r)))
+        W.alpha[s] = 2.0 * r        # scale 2 (a power of two)
+    mod.x = enc(rng.integers(-2, 3, size=(T, k)))
+    mod.y_base = enc(rng.integers(-64, 65, size=(T, sum(slices))))
+    return W
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("premultiply", [False, True])
+def test_exact_integer_inputs_bit_exact(rx, dtype, premultiply):
+    W = _integer_workload(31, T=77, S=6, k=1040, slices=[520, 64], Rmax=8, dtype=dtype)
+    mod = W.modules[0]
+    ads = oracle_adapters(W, mod, premultiply=premultiply)
+    y = _run_linear(rx, W, mod, mod.y_base, dtype, premultiply)
+    ref = O.lora_apply(to_f64(mod.x, dtype), to_f64(mod.y_base, dtype), ads, mod.slices, W.ids, W.S, dtype,
+                       max_rank=W.Rmax)
+    assert np.abs(ref).max() < 256
+    assert np.array_equal(from_device(y), ref)
+
+
+def test_identity_adapter_closed_form(rx):
+    """A = [I | 0], B = [I ; 0], s = 1: the branch copies x[:, :r] into y[:, :r]."""
+    import torch
+    T, k, d, r = 20, 64, 48, 8
+    W = small_case(41, T=T, S=2, k=k, slices=[d], Rmax=r, dtype="bf16", ranks={0: r, 1: r}, p_nolora=0.0)
+    mod = W.modules[0]
+    A = np.zeros((r, k), dtype=np.float32); A[:, :r] = np.eye(r)
+    B = np.zeros((d, r), dtype=np.float32); B[:r] = np.eye(r)
+    for s in (0, 1):
+        mod.A[s] = [O.f32_to_bf16_bits(A)]
+        mod.B[s] = [O.f32_to_bf16_bits(B)]
+        W.alpha[s] = float(r)
+    y = _run_linear(rx, W, mod, np.zeros((T, d), dtype=np.float32), "f32")
+    want = np.zeros((T, d)); want[:, :r] = to_f64(mod.x, "bf16")[:, :r]
+    assert np.array_equal(from_device(y), want)
+
+
+def test_shrink_and_expand_standalone(rx):
+    import torch
+    W = small_case(51, T=90, S=7, k=2048, slices=[264, 512], Rmax=16, invalid=2)
+    mod = W.modules[0]
+    N, D = len(mod.slices), sum(mod.slices)
+    pool = make_pool(rx, W, mod)
+    R, ids = make_routing(rx, W)
+    x = to_device(mod.x, "bf16")
+    u = torch.full((N, W.T, W.Rmax), float("nan"), device="cuda")
+    rx.shrink(pool, R, x, u)
+    torch.cuda.synchronize()
+    ads = oracle_adapters(W, mod)
+    u_ref, mask = O.shrink_per_token(to_f64(mod.x, "bf16"), ads, mod.slices, W.ids, W.S, W.Rmax)
+    ug = u.double().cpu().numpy()
+    assert not np.isnan(ug[mask]).any()
+    err = np.abs(ug[mask] - u_ref[mask]).max() / np.abs(u_ref[mask]).max()
+    assert err < 1e-4, err     # fp32 accumulation of exact bf16 products
+    # expand from the oracle's u (rounded to fp32) onto a base
+    u_in = torch.from_numpy(np.where(mask, u_ref, 0.0).astype(np.float32)).cuda()
+    y = to_device(mod.y_base, "bf16")
+    rx.expand(pool, R, u_in, y)
+    torch.cuda.synchronize()
+    delta, touched = O.expand_per_token(np.where(mask, u_ref, 0.0), ads, mod.slices, W.ids, W.S, "bf16")
+    ref = to_f64(mod.y_base, "bf16") + delta
+    check_close(from_device(y), ref, "bf16", "expand")
+    # shrink then expand equals the fused call, bit for bit
+    y1 = to_device(mod.y_base, "bf16")
+    rx.expand(pool, R, u, y1)
+    y2 = to_device(mod.y_base, "bf16")
+    rx.linear(pool, R, x, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    pool.close(); R.close()
+
+
+def test_untouched_rows_and_columns(rx):
+    """No-LoRA rows, empty slots, zero-scale slots and missing slices stay bit-identical."""
+    import torch
+    W = small_case(61, T=120, S=6, k=512, slices=[64, 128, 32], Rmax=8, invalid=4)
+    mod = W.modules[0]
+    mod.A[2][1] = None; mod.B[2][1] = None           # slot 2: slice 1 missing
+    pool = make_pool(rx, W, mod)
+    pool.unregister(3)                                 # slot 3 empty
+    a, b = mod.A[4], mod.B[4]
+    pool.register(4, a, b, W.alpha[4], W.ranks[4], adapter_scale=0.0)   # slot 4 unloaded by scale 0
+    R, ids = make_routing(rx, W)
+    y = to_device(mod.y_base, "bf16")
+    rx.linear(pool, R, to_device(mod.x, "bf16"), y)
+    torch.cuda.synchronize()
+    got, base = bits(y), mod.y_base
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    for key in (W.S, 3, 4):
+        rows = keys == key
+        assert np.array_equal(got[rows], base[rows]), key
+    rows = keys == 2
+    assert np.array_equal(got[rows][:, 64:192], base[rows][:, 64:192])
+    assert not np.array_equal(got[rows][:, :64], base[rows][:, :64])
+    pool.close(); R.close()
+
+
+def test_determinism_and_rerun(rx):
+    import torch
+    W = small_case(71, T=256, S=64, k=4096, slices=[4096, 1024, 1024], Rmax=16)
+    mod = W.modules[0]
+    pool = make_pool(rx, W, mod)
+    R, ids = make_routing(rx, W)
+    x = to_device(mod.x, "bf16")
+    outs = []
+    for _ in range(3):
+        y = to_device(mod.y_base, "bf16")
+        rx.linear(pool, R, x, y)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    pool.close(); R.close()
+
+
+def test_reregister_smaller_rank(rx):
+    import torch
+    W = small_case(81, T=40, S=3, k=256, slices=[64], Rmax=16, ranks={0: 16, 1: 8, 2: 3}, p_nolora=0.0)
+    mod = W.modules[0]
+    pool = make_pool(rx, W, mod)
+    # slot 0 re-registered with rank 5
+    rng = np.random.default_rng(5)
+    A = O.f32_to_bf16_bits(rng.standard_normal((5, 256)).astype(np.float32) / 16)
+    B = O.f32_to_bf16_bits(rng.standard_normal((64, 5)).astype(np.float32) / 2)
+    pool.register(0, [A], [B], 10.0, 5)
+    W.ranks[0] = 5; mod.A[0] = [A]; mod.B[0] = [B]; W.alpha[0] = 10.0
+    R, ids = make_routing(rx, W)
+    y = to_device(mod.y_base, "bf16")
+    rx.linear(pool, R, to_device(mod.x, "bf16"), y)
+    torch.cuda.synchronize()
+    ads = oracle_adapters(W, mod)
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), to_f64(mod.y_base, "bf16"), ads, [64], W.ids, 3, "bf16", 16)
+    check_close(from_device(y), ref, "bf16", "y")
+    pool.close(); R.close()
+
+
+# ------------------------------------------------------------- errors on GPU
+def test_error_paths_on_device(rx):
+    import torch
+    W = small_case(91, T=16, S=4, k=64, slices=[32], Rmax=8)
+    mod = W.modules[0]
+    pool = make_pool(rx, W, mod, max_tokens=16)
+    R = rx.Routing(0, 64, 4)
+    ids = torch.zeros(32, dtype=torch.int32, device="cuda")
+    R.build(ids)
+    x = torch.zeros(32, 64, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(32, 32, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rx.LoraError) as e:
+        rx.linear(pool, R, x, y)                       # T = 32 > pool max_tokens = 16
+    assert e.value.status == rx.LORA_ERR_CAPACITY
+    R16 = rx.Routing(0, 16, 4)
+    with pytest.raises(rx.LoraError) as e:
+        R16.build(ids)                                 # T = 32 > routing max_tokens
+    assert e.value.status == rx.LORA_ERR_CAPACITY
+    R16.build(ids[:16])
+    R5 = rx.Routing(0, 16, 5)
+    R5.build(ids[:16])
+    with pytest.raises(rx.LoraError) as e:
+        rx.linear(pool, R5, x[:16], y[:16])            # slot count mismatch
+    assert e.value.status == rx.LORA_ERR_SHAPE
+    xb = torch.zeros(16 * 64 + 8, dtype=torch.bfloat16, device="cuda")[1:1 + 16 * 64].view(16, 64)
+    with pytest.raises(rx.LoraError) as e:
+        rx.linear(pool, R16, xb, y[:16])               # misaligned x
+    assert e.value.status == rx.LORA_ERR_ALIGN
+    with pytest.raises(rx.LoraError) as e:
+        rx.lora_linear(pool.handle, R16.handle, x.data_ptr(), 64, y.data_ptr(), 32, 7)
+    assert e.value.status == rx.LORA_ERR_DTYPE
+    a = np.zeros((9, 64), dtype=np.uint16); b = np.zeros((32, 9), dtype=np.uint16)
+    with pytest.raises(rx.LoraError) as e:
+        pool.register(0, [a], [b], 1.0, 9)             # rank above max_lora_rank
+    assert e.value.status == rx.LORA_ERR_RANK
+    with pytest.raises(rx.LoraError) as e:
+        pool.register(4, [a[:4]], [b[:, :4].copy()], 1.0, 4)   # slot out of range
+    assert e.value.status == rx.LORA_ERR_SLOT
+    with pytest.raises(rx.LoraError) as e:
+        rx.lora_register_adapter(pool.handle, 0, [a.ctypes.data], [0], 1.0, 4, False, 1.0, 0)
+    assert e.value.status == rx.LORA_ERR_INVALID_ARG   # half-missing slice
+    for o in (pool, R, R16, R5):
+        o.close()
+
+
+# ------------------------------------------------------ workloads at full size
+def _sample_rows(W, rng, n=48):
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    pick = set(rng.choice(W.T, size=min(n, W.T), replace=False).tolist())
+    for s in np.unique(keys)[:2]:                    # every token of two segments too
+        pick |= set(np.nonzero(keys == s)[0][:200].tolist())
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
+def test_workload_parity(rx, num):
+    """Each workload at its full size, in the launch configuration the benchmark
+    times; all rows checked where the oracle is quick, sampled rows otherwise."""
+    import torch
+    W = workload(num)
+    rng = np.random.default_rng(100 + num)
+    R, ids = make_routing(rx, W)
+    for mod in W.modules:
+        _log(f"workload {num} module {mod.name} k={mod.k} slices={mod.slices} T={W.T}")
+        pool = make_pool(rx, W, mod)
+        yb = y_base_of(W, mod)
+        y = to_device(yb, W.dtype)
+        rx.linear(pool, R, to_device(mod.x, W.dtype), y)
+        torch.cuda.synchronize()
+        rows = np.arange(W.T) if num <= 2 else _sample_rows(W, rng)
+        ads = oracle_adapters(W, mod)
+        x64 = to_f64(mod.x, W.dtype)[rows]
+        ref = O.lora_apply(x64, to_f64(yb, W.dtype)[rows], ads, mod.slices, W.ids[rows], W.S, W.dtype,
+                           max_rank=W.Rmax)
+        got = from_device(y)[rows]
+        check_close(got, ref, W.dtype, f"workload {num} {mod.name} y")
+        if num == 2:
+            W0 = to_f64(mod.W0, W.dtype)
+            merged = O.merged_apply(to_f64(mod.x, W.dtype), W0, ads, mod.slices, W.ids, W.S, W.dtype)
+            check_close(got, merged, W.dtype, "merged-weight form")
+        pool.close()
+    R.close()
