@@ -51,7 +51,8 @@ def step_accounting(W, mfma_min: int, use_mfma: bool):
     wb = 2 if W.dtype == "bf16" else 4
     keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
     counts = np.bincount(keys, minlength=W.S + 1)
-    acc = {"shrink_decode": 0, "expand_decode": 0, "shrink_mfma": 0, "expand_mfma": 0}
+    acc = {"shrink": 0, "expand": 0}
+    split = {"shrink_decode": 0, "expand_decode": 0, "shrink_mfma": 0, "expand_mfma": 0}
     flops = 0
     for mod in W.modules:
         D = sum(mod.slices)
@@ -60,10 +61,14 @@ def step_accounting(W, mfma_min: int, use_mfma: bool):
             if L == 0 or r == 0:
                 continue
             fam = "mfma" if (use_mfma and L >= mfma_min) else "decode"
-            acc[f"shrink_{fam}"] += r * mod.k * len(mod.slices) * wb + L * mod.k * wb
-            acc[f"expand_{fam}"] += r * D * wb + 2 * L * D * wb
+            sb = r * mod.k * len(mod.slices) * wb + L * mod.k * wb
+            eb = r * D * wb + 2 * L * D * wb
+            acc["shrink"] += sb
+            acc["expand"] += eb
+            split[f"shrink_{fam}"] += sb
+            split[f"expand_{fam}"] += eb
             flops += 2 * L * r * (mod.k * len(mod.slices) + D)
-    return acc, flops
+    return acc, flops, split
 
 
 # -------------------------------------------------------------------- workload
@@ -178,9 +183,9 @@ def run(args):
 
     torch.cuda.set_device(0)
     W = workload(args.workload)
-    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0" and rx_has_mfma(rx)
-    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "32"))
-    acc, flops = step_accounting(W, mfma_min, use_mfma)
+    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0"
+    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "16"))
+    acc, flops, by_path = step_accounting(W, mfma_min, use_mfma)
     step_bytes = sum(acc.values())
     log(f"workload {W.name}: T={W.T} S={W.S} modules={[m.name for m in W.modules]} "
         f"algorithmic bytes/step={step_bytes / 1e6:.2f} MB")
@@ -252,7 +257,7 @@ def run(args):
                    "max_lora_rank": W.Rmax, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
-                  "step_flops": flops, "kernels": kern, "rotation_instances": M,
+                  "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
                   "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "source_digest": source_digest()},
     }
     for inst in insts:
@@ -263,10 +268,6 @@ def run(args):
     else:
         out["cpu_baseline"] = None
     return out
-
-
-def rx_has_mfma(rx) -> bool:
-    return False
 
 
 def main():

@@ -76,6 +76,7 @@ typedef int lora_status;
 #define LORA_MAX_SLICES    8
 #define LORA_MAX_SLOTS     1024
 #define LORA_MAX_RANK      256
+#define LORA_MAX_IN_FEATURES 65536
 
 /* Message for the last failing call on this thread ("" if none). Never NULL. */
 const char* lora_last_error(void);
@@ -102,12 +103,14 @@ lora_status lora_compute_scale(float alpha, int rank, int rslora, float adapter_
  * lora_b_stacked [max_loras, out, max_lora_rank]).  max_lora_rank fixes the
  * padding of every slot ([TRT-LLM] "LoraConfig": a workspace bound, not
  * enlargeable later).  max_tokens bounds T for lora_linear / lora_shrink (it
- * sizes the pool-owned split-K workspace).  All slots start empty (rank 0).
+ * sizes the pool-owned rank-space workspace: k-split partial sums, up to 16 x
+ * num_slices x max_tokens x max_lora_rank fp32).  All slots start empty (rank 0).
  * slice_out is a host array, read during the call.  The pool owns its device
  * memory (allocated on `device` here) until lora_pool_destroy.
  * Errors: out/slice_out NULL -> INVALID_ARG; max_slots outside [1, LORA_MAX_SLOTS],
  * max_lora_rank outside [1, LORA_MAX_RANK], in_features < 1, num_slices outside
- * [1, LORA_MAX_SLICES], a slice width < 1, max_tokens < 1 -> SHAPE; bad wdtype ->
+ * [1, LORA_MAX_SLICES], a slice width < 1, max_tokens < 1, in_features above
+ * LORA_MAX_IN_FEATURES -> SHAPE; bad wdtype ->
  * DTYPE; in_features or a width not a multiple of 8 -> ALIGN; device missing ->
  * NO_DEVICE; allocation -> OOM.
  */
@@ -223,9 +226,10 @@ lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, cons
  * Fused shrink + expand onto the caller's base output ([TRT-LLM] "前向替换":
  * forward_with_base adds the LoRA result onto the base projection; [vLLM-book]
  * §16.4.4 add_lora_linear).  Same result as lora_shrink then lora_expand, with the
- * intermediate kept in the pool's workspace (split along k, partial sums added in
- * a fixed order, so repeated calls are bitwise identical).  Long same-slot
- * segments of bf16 pools go to the matrix-core (MFMA) kernels.
+ * intermediate kept in the pool's workspace as k-split partial sums, added in
+ * split order by the expand, so repeated calls are bitwise identical (and equal
+ * to lora_shrink then lora_expand).  Long same-slot segments of bf16 pools go to
+ * the matrix cores (MFMA).  Two kernel launches per call.
  * Errors as lora_expand.
  */
 lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
@@ -236,8 +240,10 @@ lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, cons
  * lora_build_routing, lora_shrink, lora_expand and lora_linear launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start
  * and end, on the stream it runs on.  lora_timing_report waits for the recorded
- * events, writes per kernel id (0 routing, 1 shrink_decode, 2 expand_decode,
- * 3 reduce_splits, 4 shrink_mfma, 5 expand_mfma) the summed milliseconds and the
+ * events, writes per kernel id (0 routing, 1 shrink, 2 expand, 3 finish_u: the
+ * pass of lora_shrink that adds the k-split partial sums into the caller's u;
+ * the shrink and expand launches cover both short and long segments) the summed
+ * milliseconds and the
  * number of launches into total_ms[0..max_kernels) and launches[0..max_kernels), and
  * clears the record.  lora_timing_kernel_name gives the name of an id ("" if none).
  * Errors: INVALID_ARG for NULL arrays with max_kernels > 0; HIP if an event fails.

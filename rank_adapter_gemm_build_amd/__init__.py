@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libraxlora.so")
 
 LORA_F32, LORA_BF16 = 0, 1
 LORA_SRC_DEVICE, LORA_PREMULTIPLY = 1, 2
-LORA_MAX_SLICES, LORA_MAX_SLOTS, LORA_MAX_RANK = 8, 1024, 256
+LORA_MAX_SLICES, LORA_MAX_SLOTS, LORA_MAX_RANK, LORA_MAX_IN_FEATURES = 8, 1024, 256, 65536
 
 STATUS = {
     0: "LORA_OK", -1: "LORA_ERR_INVALID_ARG", -2: "LORA_ERR_SHAPE", -3: "LORA_ERR_DTYPE",
@@ -51,7 +51,7 @@ SIGNATURES = {
     "lora_timing_kernel_name": (C.c_char_p, [_I]),
 }
 
-KERNEL_NAMES = ["routing", "shrink_decode", "expand_decode", "reduce_splits", "shrink_mfma", "expand_mfma"]
+KERNEL_NAMES = ["routing", "shrink", "expand", "finish_u"]
 
 
 def _load():

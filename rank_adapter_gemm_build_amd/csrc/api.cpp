@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -18,17 +19,20 @@ using rax::SlotEntry;
 
 struct lora_pool {
   int device = 0;
-  int S = 0, Rmax = 0, k = 0, N = 0, D = 0, max_tokens = 0;
+  int S = 0, Rmax = 0, Rk = 0, k = 0, N = 0, D = 0, max_tokens = 0;
   int d[LORA_MAX_SLICES] = {0};
   int o[LORA_MAX_SLICES] = {0};
   int tile0[LORA_MAX_SLICES + 1] = {0};
+  int mblk0[LORA_MAX_SLICES + 1] = {0};
   lora_dtype wdtype = LORA_BF16;
   size_t esize = 2;
   void* A = nullptr;
   void* Bt = nullptr;
   void* Bk = nullptr;
   SlotEntry* table = nullptr;
-  float* ws = nullptr;        // split-K partials [kMaxSplit][N][max_tokens][Rmax]
+  float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rmax] by sorted position
+  int nsplit = 1, ns = 1;     // decode shrink: k splits, chunk steps per split (fixed by k)
+  int kq = 1;                 // matrix-core shrink: k groups per tile
   std::vector<SlotEntry> mirror;
 };
 
@@ -37,8 +41,8 @@ struct lora_routing {
   int max_tokens = 0, S = 0, mfma_min = rax::kDefaultMfmaMinSeg, tile_m = rax::kMfmaTileM;
   int max_tiles = 0;
   int* buf = nullptr;
-  int *counts = nullptr, *offs = nullptr, *sorted = nullptr, *active = nullptr, *tiles = nullptr,
-      *meta = nullptr;
+  int *counts = nullptr, *offs = nullptr, *sorted = nullptr, *active = nullptr, *meta = nullptr;
+  int4 *desc = nullptr, *tiles = nullptr;
   int T = -1;  // tokens of the last build; -1 = never built
 };
 
@@ -122,8 +126,7 @@ rax::KTimer timer_for(int kernel) {
   return t;
 }
 
-const char* const kKernelNames[rax::kKernelCount] = {"routing", "shrink_decode", "expand_decode",
-                                                     "reduce_splits", "shrink_mfma", "expand_mfma"};
+const char* const kKernelNames[rax::kKernelCount] = {"routing", "shrink", "expand", "finish_u"};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -141,15 +144,20 @@ rax::PoolView pool_view(const lora_pool* p) {
   v.table = p->table;
   v.S = p->S;
   v.Rmax = p->Rmax;
+  v.Rk = p->Rk;
   v.k = p->k;
   v.N = p->N;
   v.D = p->D;
   v.n_ctiles = p->tile0[p->N];
+  v.n_mblocks = p->mblk0[p->N];
   for (int n = 0; n < rax::kMaxSlices; ++n) {
     v.d[n] = n < p->N ? p->d[n] : 0;
     v.o[n] = n < p->N ? p->o[n] : 0;
   }
-  for (int n = 0; n <= rax::kMaxSlices; ++n) v.tile0[n] = n <= p->N ? p->tile0[n] : p->tile0[p->N];
+  for (int n = 0; n <= rax::kMaxSlices; ++n) {
+    v.tile0[n] = n <= p->N ? p->tile0[n] : p->tile0[p->N];
+    v.mblk0[n] = n <= p->N ? p->mblk0[n] : p->mblk0[p->N];
+  }
   return v;
 }
 
@@ -159,6 +167,7 @@ rax::RouteView route_view(const lora_routing* r) {
   v.offs = r->offs;
   v.sorted = r->sorted;
   v.active = r->active;
+  v.desc = r->desc;
   v.tiles = r->tiles;
   v.meta = r->meta;
   v.S = r->S;
@@ -171,19 +180,20 @@ rax::RouteView route_view(const lora_routing* r) {
 
 int chunk_width(lora_dtype t) { return 64 * (t == LORA_BF16 ? 8 : 4); }
 
-// k-split of the shrink: kDefaultSplit splits (or RAXLORA_NSPLIT) where k allows,
-// each at most kMaxChunksPerSplit 16-byte steps per lane (x stays in registers).
-// lora_pool_create guarantees k <= kMaxSplit * kMaxChunksPerSplit * chunk width.
-int choose_kc(const lora_pool* p) {
-  const int cw = chunk_width(p->wdtype);
-  const int steps = (p->k + cw - 1) / cw;
-  int nsplit = env_int("RAXLORA_NSPLIT", rax::kDefaultSplit);
-  if (nsplit < 1) nsplit = 1;
-  if (nsplit > steps) nsplit = steps;
-  int per = (steps + nsplit - 1) / nsplit;
-  if (per > rax::kMaxChunksPerSplit) per = rax::kMaxChunksPerSplit;
-  return per * cw;
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// k split of the decode shrink, fixed by the pool's shape: one wave-wide 16-byte chunk
+// step per split while k has at most kMaxSplit of them (so a short batch still has
+// k / chunk width waves per 16 rank rows), else the fewest equal splits of at most
+// kMaxSplit.  The matrix-core shrink splits a tile's k over 2 wave groups from
+// k >= 2048 (64 steps of 32) on.
+void choose_split(lora_pool* p) {
+  const int chunks = ceil_div(p->k, chunk_width(p->wdtype));
+  p->ns = ceil_div(chunks, rax::kMaxSplit);
+  p->nsplit = ceil_div(chunks, p->ns);
+  p->kq = p->k >= 2048 ? 2 : 1;
 }
+
 
 // Common checks of shrink / expand / linear.
 lora_status check_pair(const lora_pool* pool, const lora_routing* routing) {
@@ -216,14 +226,13 @@ lora_status check_y(const lora_pool* pool, const lora_routing* routing, const vo
   return LORA_OK;
 }
 
-// Workspace of split partials: [nsplit][N][max_tokens][Rmax], rows by sorted position.
-rax::UView workspace_view(const lora_pool* p, int kc) {
-  const int nsplit = (p->k + kc - 1) / kc;
+// The pool's workspace: [nsplit][N][max_tokens][Rmax], rows by sorted position.
+rax::UView workspace_view(const lora_pool* p) {
   return rax::UView{p->ws, (long long)p->N * p->max_tokens * p->Rmax, (long long)p->max_tokens * p->Rmax,
-                    p->Rmax, nsplit, 0};
+                    p->Rmax, p->nsplit, 0};
 }
 
-// The caller's u: [N][T][Rmax], rows by token index, one split.
+// The caller's u: finished values [N][T][Rmax], rows by token index.
 rax::UView caller_u_view(const lora_pool* p, const lora_routing* r, float* u) {
   return rax::UView{u, 0, (long long)r->T * p->Rmax, p->Rmax, 1, 1};
 }
@@ -232,31 +241,44 @@ bool use_mfma(const lora_pool* pool) {
   return rax::kHaveMfmaPath && pool->wdtype == LORA_BF16 && env_int("RAXLORA_DISABLE_MFMA", 0) == 0;
 }
 
+// Launch shape of a call, from host-known sizes only (T, S, the pool's shape): the
+// expected segment length T / S sets how many waves share one segment's token tiles
+// (segments of at least mfma_min tokens go to the matrix cores when those are on),
+// and the matrix-core tile slots cover the tiles a batch of T tokens produces in the
+// common case (the kernels loop over any excess).
+rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
+  rax::Plan pl{};
+  pl.nsplit = pool->nsplit;
+  pl.ns = pool->ns;
+  pl.kq = pool->kq;
+  pl.use_mfma = use_mfma(pool) && r->T >= r->mfma_min ? 1 : 0;
+  int mean = std::max(1, ceil_div(r->T, r->S));
+  if (pl.use_mfma) mean = std::min(mean, r->mfma_min - 1);
+  const int tok = 4;                                   // tokens per decode pass, both kernels
+  pl.ntg = std::max(1, std::min(expand ? 4 : 8, ceil_div(mean, tok)));
+  pl.nrb = ceil_div(pool->N * pool->Rmax, 16);
+  // one-wave decode units: four per expand block, 4 * kq per shrink block
+  pl.n_dec_blocks = expand ? ceil_div(pool->tile0[pool->N] * pool->S * pl.ntg, 4)
+                           : ceil_div(pool->S * pl.nrb * pl.nsplit * pl.ntg, 4 * pl.kq);
+  pl.tile_slots = std::max(1, std::min(r->max_tiles, ceil_div(r->T, r->tile_m) + 16));
+  return pl;
+}
+
 lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
-                       const rax::UView& U, int kc, hipStream_t stream) {
-  const rax::PoolView P = pool_view(pool);
-  const rax::RouteView R = route_view(routing);
-  const int mf = use_mfma(pool) ? 1 : 0;
-  hipError_t e = rax::launch_shrink(pool->wdtype, P, R, x, ldx, U, kc, mf, stream, timer_for(rax::kKShrink));
+                       const rax::UView& U, hipStream_t stream) {
+  const rax::Plan pl = make_plan(pool, routing, false);
+  hipError_t e = rax::launch_shrink(pool->wdtype, pool_view(pool), route_view(routing), x, ldx, U, pl,
+                                    stream, timer_for(rax::kKShrink));
   if (e != hipSuccess) return hip_fail(e, "shrink launch");
-  if (mf && routing->T >= routing->mfma_min) {
-    e = rax::launch_shrink_mfma(P, R, x, ldx, U, kc, stream, timer_for(rax::kKShrinkMfma));
-    if (e != hipSuccess) return hip_fail(e, "matrix-core shrink launch");
-  }
   return LORA_OK;
 }
 
 lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const rax::UView& U,
                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
-  const rax::PoolView P = pool_view(pool);
-  const rax::RouteView R = route_view(routing);
-  const int mf = use_mfma(pool) ? 1 : 0;
-  hipError_t e = rax::launch_expand(pool->wdtype, ydtype, P, R, U, y, ldy, mf, stream, timer_for(rax::kKExpand));
+  const rax::Plan pl = make_plan(pool, routing, true);
+  hipError_t e = rax::launch_expand(pool->wdtype, ydtype, pool_view(pool), route_view(routing), U, y, ldy,
+                                    pl, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "expand launch");
-  if (mf && routing->T >= routing->mfma_min) {
-    e = rax::launch_expand_mfma(ydtype, P, R, U, y, ldy, stream, timer_for(rax::kKExpandMfma));
-    if (e != hipSuccess) return hip_fail(e, "matrix-core expand launch");
-  }
   return LORA_OK;
 }
 
@@ -325,9 +347,8 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   }
   if (D > (1LL << 30)) return fail(LORA_ERR_SHAPE, "total output width too large");
   if (in_features % 8) return fail(LORA_ERR_ALIGN, "in_features %d not a multiple of 8", in_features);
-  if (in_features > rax::kMaxSplit * rax::kMaxChunksPerSplit * chunk_width(wdtype))
-    return fail(LORA_ERR_SHAPE, "in_features %d above the supported %d", in_features,
-                rax::kMaxSplit * rax::kMaxChunksPerSplit * chunk_width(wdtype));
+  if (in_features > LORA_MAX_IN_FEATURES)
+    return fail(LORA_ERR_SHAPE, "in_features %d above LORA_MAX_IN_FEATURES = %d", in_features, LORA_MAX_IN_FEATURES);
 
   lora_status st = check_device(device);
   if (st != LORA_OK) return st;
@@ -338,29 +359,35 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   p->device = device;
   p->S = max_slots;
   p->Rmax = max_lora_rank;
+  p->Rk = (max_lora_rank + rax::kMfmaK - 1) / rax::kMfmaK * rax::kMfmaK;
   p->k = in_features;
   p->N = num_slices;
   p->max_tokens = max_tokens;
   p->wdtype = wdtype;
   p->esize = wdtype == LORA_BF16 ? 2 : 4;
-  int o = 0, tiles = 0;
+  int o = 0, tiles = 0, mblocks = 0;
   for (int n = 0; n < num_slices; ++n) {
     p->d[n] = slice_out[n];
     p->o[n] = o;
     p->tile0[n] = tiles;
+    p->mblk0[n] = mblocks;
     o += slice_out[n];
     tiles += (slice_out[n] + rax::kTileCols - 1) / rax::kTileCols;
+    mblocks += (slice_out[n] + rax::kMfmaCols - 1) / rax::kMfmaCols;
   }
   p->D = o;
   p->tile0[num_slices] = tiles;
+  p->mblk0[num_slices] = mblocks;
   p->mirror.assign(max_slots, SlotEntry{0, 0.f, 0u, 0});
 
   const size_t a_bytes = (size_t)max_slots * num_slices * max_lora_rank * in_features * p->esize;
   const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
-  const size_t ws_bytes = (size_t)rax::kMaxSplit * num_slices * max_tokens * max_lora_rank * sizeof(float);
+  const size_t bk_bytes = (size_t)max_slots * p->Rk * p->D * p->esize;
+  choose_split(p);
+  const size_t ws_bytes = (size_t)p->nsplit * num_slices * max_tokens * max_lora_rank * sizeof(float);
   hipError_t e;
   if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
-      (e = hipMalloc(&p->Bk, b_bytes)) != hipSuccess ||
+      (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
       (e = hipMalloc((void**)&p->table, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
       (e = hipMalloc((void**)&p->ws, ws_bytes)) != hipSuccess) {
     lora_pool_destroy(p);
@@ -368,7 +395,7 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   }
   // empty slots read as rank 0; weights start at zero so padding rows are inert
   if ((e = hipMemset(p->A, 0, a_bytes)) != hipSuccess || (e = hipMemset(p->Bt, 0, b_bytes)) != hipSuccess ||
-      (e = hipMemset(p->Bk, 0, b_bytes)) != hipSuccess ||
+      (e = hipMemset(p->Bk, 0, bk_bytes)) != hipSuccess ||
       (e = hipMemset(p->table, 0, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
       (e = hipDeviceSynchronize()) != hipSuccess) {
     lora_pool_destroy(p);
@@ -386,6 +413,7 @@ lora_status lora_pool_destroy(lora_pool* p) {
   if (p->Bk) (void)hipFree(p->Bk);
   if (p->table) (void)hipFree(p->table);
   if (p->ws) (void)hipFree(p->ws);
+
   delete p;
   return ok();
 }
@@ -439,9 +467,9 @@ lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* 
     }
     char* A_dst = static_cast<char*>(pool->A) + (((size_t)slot * pool->N + n) * pool->Rmax) * pool->k * es;
     char* Bt_dst = static_cast<char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[n]) * es;
-    char* Bk_dst = static_cast<char*>(pool->Bk) + ((size_t)slot * pool->D + pool->o[n]) * pool->Rmax * es;
+    char* Bk_dst = static_cast<char*>(pool->Bk) + ((size_t)slot * pool->D + pool->o[n]) * pool->Rk * es;
     e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bt_dst, Bk_dst, rank, pool->Rmax,
-                               pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, stream);
+                               pool->Rk, pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, stream);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "pack launch"); }
   }
   const SlotEntry entry{rank, premul ? 1.0f : s, mask, 0};
@@ -522,8 +550,10 @@ lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, 
   r->tile_m = rax::kMfmaTileM;
   // sum over long segments of ceil(len / tile_m) <= T / tile_m + (number of long segments)
   r->max_tiles = max_tokens / r->tile_m + 1 + max_slots;
-  const size_t words = (size_t)(max_slots + 1) + (max_slots + 2) + max_tokens + max_slots +
-                       3 * (size_t)r->max_tiles + rax::kMetaWords;
+  // layout: meta, desc[S], tiles[max_tiles] (16-byte entries first, so they stay
+  // 16-byte aligned), then counts[S+1], offs[S+2], sorted[max_tokens], active[S]
+  const size_t words = rax::kMetaWords + 4 * (size_t)max_slots + 4 * (size_t)r->max_tiles +
+                       (size_t)(max_slots + 1) + (max_slots + 2) + max_tokens + max_slots;
   hipError_t e = hipMalloc((void**)&r->buf, words * sizeof(int));
   if (e != hipSuccess) {
     delete r;
@@ -535,12 +565,13 @@ lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, 
     return hip_fail(e, "routing initialisation");
   }
   int* w = r->buf;
+  r->meta = w; w += rax::kMetaWords;
+  r->desc = reinterpret_cast<int4*>(w); w += 4 * max_slots;
+  r->tiles = reinterpret_cast<int4*>(w); w += 4 * r->max_tiles;
   r->counts = w; w += max_slots + 1;
   r->offs = w; w += max_slots + 2;
   r->sorted = w; w += max_tokens;
-  r->active = w; w += max_slots;
-  r->tiles = w; w += 3 * r->max_tiles;
-  r->meta = w;
+  r->active = w;
   *out = r;
   return ok();
 }
@@ -561,7 +592,7 @@ lora_status lora_build_routing(lora_routing* r, const int32_t* ids, int T, hipSt
   DeviceGuard g(r->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   hipError_t e = rax::launch_routing(ids, T, r->S, r->mfma_min, r->tile_m, r->max_tiles, r->counts,
-                                     r->offs, r->sorted, r->active, r->tiles, r->meta, stream,
+                                     r->offs, r->sorted, r->active, r->desc, r->tiles, r->meta, stream,
                                      timer_for(rax::kKRouting));
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   r->T = T;
@@ -603,16 +634,13 @@ lora_status lora_shrink(const lora_pool* pool, const lora_routing* routing, cons
   if (routing->T == 0) return ok();
   DeviceGuard g(pool->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-  // split partials into the workspace, then added in split order into the caller's
-  // u [N][T][Rmax] (rows by token index)
-  const int kc = choose_kc(pool);
-  const rax::UView W = workspace_view(pool, kc);
-  st = run_shrink(pool, routing, x, ldx, W, kc, stream);
-  if (st != LORA_OK) return st;
-  const rax::UView U = caller_u_view(pool, routing, u);
-  hipError_t e = rax::launch_reduce_splits(pool_view(pool), route_view(routing), W, U, stream,
-                                           timer_for(rax::kKReduce));
-  if (e != hipSuccess) return hip_fail(e, "split reduction launch");
+  // split partials into the workspace, then finished in split order into the caller's u
+  const rax::UView W = workspace_view(pool);
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
+  const rax::Plan pl = make_plan(pool, routing, false);
+  hipError_t e = rax::launch_finish_u(pool_view(pool), route_view(routing), W, caller_u_view(pool, routing, u),
+                                      pl, stream, timer_for(rax::kKFinish));
+  if (e != hipSuccess) return hip_fail(e, "finish launch");
   return ok();
 }
 
@@ -640,9 +668,8 @@ lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, cons
   if (routing->T == 0) return ok();
   DeviceGuard g(pool->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-  const int kc = choose_kc(pool);
-  const rax::UView W = workspace_view(pool, kc);
-  if ((st = run_shrink(pool, routing, x, ldx, W, kc, stream)) != LORA_OK) return st;
+  const rax::UView W = workspace_view(pool);
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
   if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
   return ok();
 }

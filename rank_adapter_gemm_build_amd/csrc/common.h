@@ -4,8 +4,9 @@
 //   A   [S][N][Rmax][k]     shrink weights as given (rows j >= rank are zero)
 //   Bt  [S][Rmax][D]        expand weights, B transposed to rank-major rows; slice n
 //                           occupies columns [o_n, o_n + d_n) of every rank row
-//   Bk  [S][D][Rmax]        expand weights with the rank contiguous (B as given,
-//                           padded): the matrix-core operand layout
+//   Bk  [S][D][Rk]          expand weights with the rank contiguous (B as given,
+//                           rows padded to Rk = Rmax rounded up to 32): the
+//                           matrix-core operand layout
 //   table [S]               rank, scale, present-slice mask per slot
 // Slots are addressed by fixed strides, so no pointer table is needed: the
 // address of slot s is base + s * stride, formed in 64-bit arithmetic.
@@ -19,16 +20,17 @@
 namespace rax {
 
 constexpr int kMaxSlices = LORA_MAX_SLICES;
-constexpr int kMaxSplit = 32;      // k-splits of the shrink (partials in the workspace)
-constexpr int kDefaultSplit = 8;   // splits used when k allows
-constexpr int kMaxChunksPerSplit = 4;  // 16-byte lane chunks per split (x held in registers)
+constexpr int kMaxSplit = 16;         // k splits of a decode shrink (partial sums per split)
 constexpr int kColsPerLane = 8;    // expand: output columns owned by one lane
 constexpr int kTileCols = 64 * kColsPerLane;  // expand: columns of one wave tile
 constexpr int kRoutingThreads = 512;
 constexpr int kRoutingWaves = kRoutingThreads / 64;
 constexpr int kMfmaTileM = 64;     // tokens per matrix-core tile of a long segment
-constexpr int kDefaultMfmaMinSeg = 32;  // segments at least this long use matrix cores
-constexpr bool kHaveMfmaPath = false;   // matrix-core kernels compiled in
+constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
+constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block
+constexpr int kMfmaColBlocksPerGroup = 8;  // expand blocks one workgroup sweeps per staged u tile
+constexpr int kDefaultMfmaMinSeg = 16;  // segments at least this long use matrix cores
+constexpr bool kHaveMfmaPath = true;    // matrix-core kernels compiled in
 
 struct SlotEntry {
   int32_t rank;         // 0 = empty slot
@@ -46,10 +48,11 @@ struct PoolView {
   const void* Bt;
   const void* Bk;
   const SlotEntry* table;
-  int S, Rmax, k, N, D, n_ctiles;
+  int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks;
   int d[kMaxSlices];
   int o[kMaxSlices];
   int tile0[kMaxSlices + 1];  // first expand column tile of each slice; tile0[N] = n_ctiles
+  int mblk0[kMaxSlices + 1];  // first matrix-core column block of each slice; mblk0[N] = n_mblocks
 };
 
 struct RouteView {
@@ -57,19 +60,38 @@ struct RouteView {
   const int* offs;     // [S+2]
   const int* sorted;   // [T]
   const int* active;   // [S]
-  const int* tiles;    // [max_tiles][3]: slot, first sorted position, length
+  const int4* desc;    // [S]: per active slot (slot, tokens, first sorted position, 0)
+  const int4* tiles;   // [max_tiles]: per matrix-core tile (slot, first sorted position, length, 0)
   const int* meta;     // [kMetaWords]
   int S, T, mfma_min, tile_m, max_tiles;
 };
 
-// Rank-space intermediate u: element (split q, slice n, row, j) at
-// p + q*q_stride + n*n_stride + row*row_stride + j, where row is the token index
-// (by_token) or the token's position in sorted order.
+// Rank-space values u (fp32): partial sum of k split s for (slice n, row, rank j)
+// at p[s * split_stride + n * n_stride + row * row_stride + j], s < nsplit; the value
+// is the sum of its nsplit partials in split order.  Rows are token indices when
+// by_token is set (the caller's finished [N][T][Rmax] buffer, nsplit = 1), sorted
+// positions otherwise (the pool's workspace [nsplit][N][max_tokens][Rmax]).  Tokens
+// of matrix-core segments always hold their finished value in split 0.
 struct UView {
   float* p;
-  long long q_stride, n_stride, row_stride;
-  int nsplit;
-  int by_token;
+  long long split_stride, n_stride, row_stride;
+  int nsplit, by_token;
+};
+
+// Launch shape of one shrink or expand call.
+//   shrink: blocks of 4 * kq waves; the first n_dec_blocks hold one-wave decode units
+//           (one active slot, k split s of nsplit, one block of 16 rank rows, token
+//           tiles tg, tg + ntg, ...; split s takes the wave-wide 16-byte chunk steps
+//           c = s + nsplit * m, m < ns), the rest are matrix-core tile slots, where
+//           wave w takes the 16-token group w % 4 over the k range w / 4 of kq parts.
+//   expand: blocks of 4 waves; the first n_dec_blocks hold four one-wave decode items
+//           each, the rest are matrix-core tile slots.
+struct Plan {
+  int nsplit, ns, kq;      // shrink: k splits, chunk steps per split, k groups (MFMA)
+  int nrb, ntg;            // decode: 16-row blocks, token-tile groups
+  int n_dec_blocks;        // blocks of the decode part
+  int tile_slots;          // matrix-core part: tiles handled in parallel
+  int use_mfma;            // long segments go to the matrix-core part
 };
 
 // Optional per-launch timing: when start is non-null the kernel is launched with
@@ -80,26 +102,24 @@ struct KTimer {
 };
 
 // kernels the timing facility reports, in this order
-enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKReduce, kKShrinkMfma, kKExpandMfma, kKernelCount };
+enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKFinish, kKernelCount };
 
 // launchers (device code in the .hip files); all return the launch status
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
-                          int* counts, int* offs, int* sorted, int* active, int* tiles, int* meta,
-                          hipStream_t stream, const KTimer& tm);
+                          int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
+                          int* meta, hipStream_t stream, const KTimer& tm);
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
-                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int k, int d, int D,
-                             float scale, int premultiply, hipStream_t stream);
+                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
+                             int D, float scale, int premultiply, hipStream_t stream);
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream);
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
-                         const UView& U, int kc, int use_mfma, hipStream_t stream, const KTimer& tm);
+                         const UView& U, const Plan& plan, hipStream_t stream, const KTimer& tm);
+
 hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
-                         const UView& U, void* y, int ldy, int use_mfma, hipStream_t stream,
+                         const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,
                          const KTimer& tm);
-hipError_t launch_reduce_splits(const PoolView& P, const RouteView& R, const UView& W, const UView& U,
-                                hipStream_t stream, const KTimer& tm);
-hipError_t launch_shrink_mfma(const PoolView& P, const RouteView& R, const void* x, int ldx,
-                              const UView& U, int kc, hipStream_t stream, const KTimer& tm);
-hipError_t launch_expand_mfma(int ydtype, const PoolView& P, const RouteView& R, const UView& U,
-                              void* y, int ldy, hipStream_t stream, const KTimer& tm);
+// finished u of a standalone shrink: workspace partials -> caller's [N][T][Rmax]
+hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W, const UView& U,
+                           const Plan& plan, hipStream_t stream, const KTimer& tm);
 
 }  // namespace rax

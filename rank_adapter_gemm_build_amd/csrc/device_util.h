@@ -160,6 +160,11 @@ __device__ __forceinline__ void reduce_scatter64(float (&v)[64]) {
   reduce_scatter_stage<1>(v, lane);
 }
 
+// Keep the compiler from moving instructions across this point: used between a
+// phase that issues a batch of independent loads and the phase that consumes them,
+// so all of the batch is in flight before the first wait.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = lane_id();
 #pragma unroll
@@ -174,6 +179,22 @@ __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
   return x;
+}
+
+// A rank-space value finished from its k-split partial sums p[0], p[stride], ...:
+// added in split order, starting from split 0, wherever it is computed (the expand
+// and the standalone shrink's finishing pass), so the two agree bitwise.  All loads
+// are issued before the first addition.
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, long long stride, int nsplit) {
+  float pv[kMaxSplit];
+#pragma unroll
+  for (int q = 0; q < kMaxSplit; ++q)
+    if (q < nsplit) pv[q] = p[q * stride];
+  float v = pv[0];
+#pragma unroll
+  for (int q = 1; q < kMaxSplit; ++q)
+    if (q < nsplit) v += pv[q];
+  return v;
 }
 
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).

@@ -27,21 +27,21 @@ __global__ void pack_a_kernel(const T* __restrict__ src, T* __restrict__ dst, lo
 }
 
 // B slice [d][rank] -> Bt rows [Rmax][D] (columns [0, d) of the slice) and
-// Bk [d][Rmax]; entries j >= rank are zero.  Optional fold of the scale: one fp32
+// Bk [d][Rk]; entries j >= rank are zero.  Optional fold of the scale: one fp32
 // product rounded once to T.
 template <typename T>
 __global__ void pack_b_kernel(const T* __restrict__ src, T* __restrict__ bt, T* __restrict__ bk,
-                              int rank, int Rmax, int d, int D, float scale, int premultiply) {
+                              int rank, int Rmax, int Rk, int d, int D, float scale, int premultiply) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d) return;
-  for (int j = 0; j < Rmax; ++j) {
+  for (int j = 0; j < Rk; ++j) {
     T v = T(0);
     if (src != nullptr && j < rank) {
       v = src[(long long)i * rank + j];
       if (premultiply) from_f(scale * to_f(v), v);
     }
-    bt[(long long)j * D + i] = v;
-    bk[(long long)i * Rmax + j] = v;
+    if (j < Rmax) bt[(long long)j * D + i] = v;
+    bk[(long long)i * Rk + j] = v;
   }
 }
 
@@ -49,7 +49,7 @@ __global__ void set_slot_kernel(SlotEntry* table, int slot, SlotEntry entry) { t
 
 template <typename T>
 static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* Bt_dst, void* Bk_dst,
-                       int rank, int Rmax, int k, int d, int D, float scale, int premultiply,
+                       int rank, int Rmax, int Rk, int k, int d, int D, float scale, int premultiply,
                        hipStream_t stream) {
   const long long n_all = (long long)Rmax * k, n_src = (long long)rank * k;
   const int blocks_a = (int)((n_all + 255) / 256 < 4096 ? (n_all + 255) / 256 : 4096);
@@ -59,18 +59,18 @@ static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* 
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_b_kernel<T>, dim3((d + 255) / 256), dim3(256), 0, stream,
                      static_cast<const T*>(B_src), static_cast<T*>(Bt_dst), static_cast<T*>(Bk_dst),
-                     rank, Rmax, d, D, scale, premultiply);
+                     rank, Rmax, Rk, d, D, scale, premultiply);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
-                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int k, int d, int D,
-                             float scale, int premultiply, hipStream_t stream) {
+                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
+                             int D, float scale, int premultiply, hipStream_t stream) {
   if (wdtype == LORA_BF16)
-    return pack<uint16_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, k, d, D, scale,
+    return pack<uint16_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                           premultiply, stream);
-  return pack<float>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, k, d, D, scale, premultiply,
-                     stream);
+  return pack<float>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
+                     premultiply, stream);
 }
 
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream) {

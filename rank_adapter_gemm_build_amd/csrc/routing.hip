@@ -14,8 +14,10 @@
 // totals into the segment offsets.  Pass 3 lets every wave walk its chunk in token
 // order, 64 tokens at a time; lanes holding the same key are grouped with ballots and
 // ranked by lane order, so each key's tokens land in increasing token order: the
-// result is the unique stable order, identical on every run.  The active-slot list and
-// the matrix-core tile list are compacted in slot order by one wave.
+// result is the unique stable order, identical on every run.  The active-slot list, a
+// 16-byte descriptor per active slot (slot, tokens, first sorted position) that lets a
+// kernel start from a single load, and the matrix-core tile list are compacted in slot
+// order by one wave.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -25,7 +27,8 @@ namespace rax {
 __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
     const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
     int* __restrict__ counts, int* __restrict__ offs, int* __restrict__ sorted,
-    int* __restrict__ active, int* __restrict__ tiles, int* __restrict__ meta) {
+    int* __restrict__ active, int4* __restrict__ desc, int4* __restrict__ tiles,
+    int* __restrict__ meta) {
   extern __shared__ int lds[];
   const int K = S + 1;                         // keys 0..S-1 are slots, S is "no LoRA"
   int* hist = lds;                             // [kRoutingWaves][K]
@@ -117,17 +120,17 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
       const int key = b + lane;
       const int c = key < S ? start[key + 1] - start[key] : 0;
       const unsigned long long ma = __ballot(c > 0);
-      if (c > 0) active[nact + __popcll(ma & ((1ull << lane) - 1ull))] = key;
+      if (c > 0) {
+        const int e = nact + __popcll(ma & ((1ull << lane) - 1ull));
+        active[e] = key;
+        desc[e] = make_int4(key, c, start[key], 0);
+      }
       nact += __popcll(ma);
       const int nt = (c > 0 && c >= mfma_min) ? (c + tile_m - 1) / tile_m : 0;
       const int incl = wave_inclusive_scan(nt);
       for (int i = 0; i < nt; ++i) {
         const int e = ntiles + incl - nt + i;
-        if (e < max_tiles) {
-          tiles[3 * e + 0] = key;
-          tiles[3 * e + 1] = start[key] + i * tile_m;
-          tiles[3 * e + 2] = min(tile_m, c - i * tile_m);
-        }
+        if (e < max_tiles) tiles[e] = make_int4(key, start[key] + i * tile_m, min(tile_m, c - i * tile_m), 0);
       }
       ntiles += __shfl(incl, 63);
     }
@@ -142,11 +145,11 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
 }
 
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
-                          int* counts, int* offs, int* sorted, int* active, int* tiles, int* meta,
-                          hipStream_t stream, const KTimer& tm) {
+                          int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
+                          int* meta, hipStream_t stream, const KTimer& tm) {
   const size_t lds = (size_t)(kRoutingWaves * (S + 1) + (S + 1) + 4) * sizeof(int);
   RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(kRoutingThreads), (uint32_t)lds, stream, ids, T, S,
-             mfma_min, tile_m, max_tiles, counts, offs, sorted, active, tiles, meta);
+             mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, meta);
   return hipGetLastError();
 }
 

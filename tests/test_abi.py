@@ -41,7 +41,7 @@ def test_header_constants_match_binding():
         assert int(defs[name]) == code, name
     assert int(defs["LORA_SRC_DEVICE"].rstrip("u")) == rx.LORA_SRC_DEVICE
     assert int(defs["LORA_PREMULTIPLY"].rstrip("u")) == rx.LORA_PREMULTIPLY
-    for n in ("LORA_MAX_SLICES", "LORA_MAX_SLOTS", "LORA_MAX_RANK"):
+    for n in ("LORA_MAX_SLICES", "LORA_MAX_SLOTS", "LORA_MAX_RANK", "LORA_MAX_IN_FEATURES"):
         assert int(defs[n]) == getattr(rx, n)
 
 

@@ -402,3 +402,49 @@ def test_workload_parity(rx, num):
             check_close(got, merged, W.dtype, "merged-weight form")
         pool.close()
     R.close()
+
+
+# ------------------------------------------------------ matrix-core segments
+@pytest.mark.parametrize("segments,Rmax,slices", [
+    ([16, 17, 63, 64, 65, 300], 64, [4096]),          # around the tile size, mixed ranks
+    ([128, 33, 200], 16, [4096, 1024, 1024]),          # packed slices
+    ([40, 7, 90, 3, 129], 40, [520]),                  # rank not a multiple of 32, ragged d
+    ([513], 8, [8200]),                                # one long segment, rank 8
+])
+def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
+    import os
+    import torch
+    W = small_case(300 + len(segments), T=0, S=12, k=2056, slices=slices, Rmax=Rmax, segments=segments)
+    mod = W.modules[0]
+    _log(f"segments {segments} Rmax={Rmax} slices={slices} T={W.T}")
+    ads = oracle_adapters(W, mod)
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
+                       max_rank=Rmax)
+    outs = {}
+    for mode in ("mfma", "vector"):
+        if mode == "vector":
+            os.environ["RAXLORA_DISABLE_MFMA"] = "1"
+        try:
+            y = _run_linear(rx, W, mod, np.zeros((W.T, sum(slices)), dtype=np.float32), "f32")
+        finally:
+            os.environ.pop("RAXLORA_DISABLE_MFMA", None)
+        outs[mode] = from_device(y)
+        err = check_close(outs[mode], ref, "bf16", f"delta ({mode})")
+        _log(f"  {mode}: normwise rel err {err:.2e}")
+
+
+def test_shrink_matrix_cores_match_oracle(rx):
+    """u from the matrix-core shrink of long segments (standalone lora_shrink)."""
+    import torch
+    W = small_case(401, T=0, S=4, k=1024, slices=[256, 128], Rmax=32, segments=[70, 20, 150])
+    mod = W.modules[0]
+    pool = make_pool(rx, W, mod)
+    R, ids = make_routing(rx, W)
+    u = torch.full((2, W.T, 32), float("nan"), device="cuda")
+    rx.shrink(pool, R, to_device(mod.x, "bf16"), u)
+    torch.cuda.synchronize()
+    u_ref, mask = O.shrink_per_token(to_f64(mod.x, "bf16"), oracle_adapters(W, mod), mod.slices, W.ids, W.S, 32)
+    ug = u.double().cpu().numpy()
+    assert not np.isnan(ug[mask]).any()
+    assert np.abs(ug[mask] - u_ref[mask]).max() / np.abs(u_ref[mask]).max() < 1e-4
+    pool.close(); R.close()
