@@ -30,9 +30,8 @@ struct lora_pool {
   void* Bt = nullptr;
   void* Bk = nullptr;
   SlotEntry* table = nullptr;
-  float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rmax] by sorted position
+  float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rk] by sorted position
   int nsplit = 1, ns = 1;     // decode shrink: k splits, chunk steps per split (fixed by k)
-  int kq = 1;                 // matrix-core shrink: k groups per tile
   std::vector<SlotEntry> mirror;
 };
 
@@ -43,6 +42,7 @@ struct lora_routing {
   int* buf = nullptr;
   int *counts = nullptr, *offs = nullptr, *sorted = nullptr, *active = nullptr, *meta = nullptr;
   int4 *desc = nullptr, *tiles = nullptr;
+  int* rec = nullptr;
   int T = -1;  // tokens of the last build; -1 = never built
 };
 
@@ -169,6 +169,7 @@ rax::RouteView route_view(const lora_routing* r) {
   v.active = r->active;
   v.desc = r->desc;
   v.tiles = r->tiles;
+  v.rec = r->rec;
   v.meta = r->meta;
   v.S = r->S;
   v.T = r->T;
@@ -185,13 +186,11 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // k split of the decode shrink, fixed by the pool's shape: one wave-wide 16-byte chunk
 // step per split while k has at most kMaxSplit of them (so a short batch still has
 // k / chunk width waves per 16 rank rows), else the fewest equal splits of at most
-// kMaxSplit.  The matrix-core shrink splits a tile's k over 2 wave groups from
-// k >= 2048 (64 steps of 32) on.
+// kMaxSplit.
 void choose_split(lora_pool* p) {
   const int chunks = ceil_div(p->k, chunk_width(p->wdtype));
   p->ns = ceil_div(chunks, rax::kMaxSplit);
   p->nsplit = ceil_div(chunks, p->ns);
-  p->kq = p->k >= 2048 ? 2 : 1;
 }
 
 
@@ -226,10 +225,11 @@ lora_status check_y(const lora_pool* pool, const lora_routing* routing, const vo
   return LORA_OK;
 }
 
-// The pool's workspace: [nsplit][N][max_tokens][Rmax], rows by sorted position.
+// The pool's workspace: [nsplit][N][max_tokens][Rk], rows by sorted position (rows
+// padded to Rk, a multiple of 32 floats, so they can be read 16 bytes at a time).
 rax::UView workspace_view(const lora_pool* p) {
-  return rax::UView{p->ws, (long long)p->N * p->max_tokens * p->Rmax, (long long)p->max_tokens * p->Rmax,
-                    p->Rmax, p->nsplit, 0};
+  return rax::UView{p->ws, (long long)p->N * p->max_tokens * p->Rk, (long long)p->max_tokens * p->Rk, p->Rk,
+                    p->nsplit, 0};
 }
 
 // The caller's u: finished values [N][T][Rmax], rows by token index.
@@ -250,16 +250,15 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   rax::Plan pl{};
   pl.nsplit = pool->nsplit;
   pl.ns = pool->ns;
-  pl.kq = pool->kq;
+  pl.nrg = ceil_div(pool->N * pool->Rmax, 64);
   pl.use_mfma = use_mfma(pool) && r->T >= r->mfma_min ? 1 : 0;
   int mean = std::max(1, ceil_div(r->T, r->S));
   if (pl.use_mfma) mean = std::min(mean, r->mfma_min - 1);
   const int tok = 4;                                   // tokens per decode pass, both kernels
   pl.ntg = std::max(1, std::min(expand ? 4 : 8, ceil_div(mean, tok)));
   pl.nrb = ceil_div(pool->N * pool->Rmax, 16);
-  // one-wave decode units: four per expand block, 4 * kq per shrink block
-  pl.n_dec_blocks = expand ? ceil_div(pool->tile0[pool->N] * pool->S * pl.ntg, 4)
-                           : ceil_div(pool->S * pl.nrb * pl.nsplit * pl.ntg, 4 * pl.kq);
+  // one workgroup per decode unit
+  pl.n_dec_blocks = expand ? pool->tile0[pool->N] * pool->S * pl.ntg : pool->S * pl.nrb * pl.nsplit * pl.ntg;
   pl.tile_slots = std::max(1, std::min(r->max_tiles, ceil_div(r->T, r->tile_m) + 16));
   return pl;
 }
@@ -384,7 +383,7 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
   const size_t bk_bytes = (size_t)max_slots * p->Rk * p->D * p->esize;
   choose_split(p);
-  const size_t ws_bytes = (size_t)p->nsplit * num_slices * max_tokens * max_lora_rank * sizeof(float);
+  const size_t ws_bytes = (size_t)p->nsplit * num_slices * max_tokens * p->Rk * sizeof(float);
   hipError_t e;
   if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
       (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
@@ -550,10 +549,12 @@ lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, 
   r->tile_m = rax::kMfmaTileM;
   // sum over long segments of ceil(len / tile_m) <= T / tile_m + (number of long segments)
   r->max_tiles = max_tokens / r->tile_m + 1 + max_slots;
-  // layout: meta, desc[S], tiles[max_tiles] (16-byte entries first, so they stay
-  // 16-byte aligned), then counts[S+1], offs[S+2], sorted[max_tokens], active[S]
-  const size_t words = rax::kMetaWords + 4 * (size_t)max_slots + 4 * (size_t)r->max_tiles +
-                       (size_t)(max_slots + 1) + (max_slots + 2) + max_tokens + max_slots;
+  // layout: meta, rec[S] (128-byte records), desc[S], tiles[max_tiles] (16-byte
+  // entries first, so they stay 16-byte aligned), then counts[S+1], offs[S+2],
+  // sorted[max_tokens], active[S]
+  const size_t words = rax::kMetaWords + (size_t)rax::kRecInts * max_slots + 4 * (size_t)max_slots +
+                       4 * (size_t)r->max_tiles + (size_t)(max_slots + 1) + (max_slots + 2) + max_tokens +
+                       max_slots;
   hipError_t e = hipMalloc((void**)&r->buf, words * sizeof(int));
   if (e != hipSuccess) {
     delete r;
@@ -566,6 +567,7 @@ lora_status lora_routing_create(lora_routing** out, int device, int max_tokens, 
   }
   int* w = r->buf;
   r->meta = w; w += rax::kMetaWords;
+  r->rec = w; w += (size_t)rax::kRecInts * max_slots;
   r->desc = reinterpret_cast<int4*>(w); w += 4 * max_slots;
   r->tiles = reinterpret_cast<int4*>(w); w += 4 * r->max_tiles;
   r->counts = w; w += max_slots + 1;
@@ -592,7 +594,7 @@ lora_status lora_build_routing(lora_routing* r, const int32_t* ids, int T, hipSt
   DeviceGuard g(r->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   hipError_t e = rax::launch_routing(ids, T, r->S, r->mfma_min, r->tile_m, r->max_tiles, r->counts,
-                                     r->offs, r->sorted, r->active, r->desc, r->tiles, r->meta, stream,
+                                     r->offs, r->sorted, r->active, r->desc, r->tiles, r->rec, r->meta, stream,
                                      timer_for(rax::kKRouting));
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   r->T = T;

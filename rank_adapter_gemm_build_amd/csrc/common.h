@@ -25,11 +25,13 @@ constexpr int kColsPerLane = 8;    // expand: output columns owned by one lane
 constexpr int kTileCols = 64 * kColsPerLane;  // expand: columns of one wave tile
 constexpr int kRoutingThreads = 512;
 constexpr int kRoutingWaves = kRoutingThreads / 64;
-constexpr int kMfmaTileM = 64;     // tokens per matrix-core tile of a long segment
+constexpr int kMfmaTileM = 16;     // tokens per matrix-core tile of a long segment
 constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
 constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block
-constexpr int kMfmaColBlocksPerGroup = 8;  // expand blocks one workgroup sweeps per staged u tile
+constexpr int kMfmaColBlocksPerUnit = 4;   // 128-column blocks of one matrix-core expand unit
 constexpr int kDefaultMfmaMinSeg = 16;  // segments at least this long use matrix cores
+constexpr int kRecInts = 32;       // ints of one slot record: tokens, first position, 2 spare, token ids
+constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
 constexpr bool kHaveMfmaPath = true;    // matrix-core kernels compiled in
 
 struct SlotEntry {
@@ -62,6 +64,7 @@ struct RouteView {
   const int* active;   // [S]
   const int4* desc;    // [S]: per active slot (slot, tokens, first sorted position, 0)
   const int4* tiles;   // [max_tiles]: per matrix-core tile (slot, first sorted position, length, 0)
+  const int* rec;      // [S][kRecInts]: per slot (tokens, first sorted position, 0, 0, first token ids)
   const int* meta;     // [kMetaWords]
   int S, T, mfma_min, tile_m, max_tiles;
 };
@@ -78,18 +81,19 @@ struct UView {
   int nsplit, by_token;
 };
 
-// Launch shape of one shrink or expand call.
-//   shrink: blocks of 4 * kq waves; the first n_dec_blocks hold one-wave decode units
-//           (one active slot, k split s of nsplit, one block of 16 rank rows, token
-//           tiles tg, tg + ntg, ...; split s takes the wave-wide 16-byte chunk steps
-//           c = s + nsplit * m, m < ns), the rest are matrix-core tile slots, where
-//           wave w takes the 16-token group w % 4 over the k range w / 4 of kq parts.
-//   expand: blocks of 4 waves; the first n_dec_blocks hold four one-wave decode items
-//           each, the rest are matrix-core tile slots.
+// Launch shape of one shrink or expand call; every workgroup is one wave.
+//   shrink: the first n_dec_blocks are decode units (one active slot, k split s of
+//           nsplit, one block of 16 rank rows, token tiles tg, tg + ntg, ...; split s
+//           takes the wave-wide 16-byte chunk steps c = s + nsplit * m, m < ns), then
+//           tile_slots x nrg matrix-core units (tile slot, group of 64 rank rows).
+//   expand: the first n_dec_blocks are decode items (column tile, active slot, token
+//           tiles), then tile_slots x n_mblocks matrix-core units (tile slot, 128
+//           columns).  Tile slot ts takes tiles ts, ts + tile_slots, ...
 struct Plan {
-  int nsplit, ns, kq;      // shrink: k splits, chunk steps per split, k groups (MFMA)
+  int nsplit, ns;          // decode shrink: k splits, chunk steps per split
+  int nrg;                 // matrix-core shrink: groups of 64 rank rows (N * Rmax / 64)
   int nrb, ntg;            // decode: 16-row blocks, token-tile groups
-  int n_dec_blocks;        // blocks of the decode part
+  int n_dec_blocks;        // workgroups of the decode part
   int tile_slots;          // matrix-core part: tiles handled in parallel
   int use_mfma;            // long segments go to the matrix-core part
 };
@@ -107,7 +111,7 @@ enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKFinish, kKernelCount };
 // launchers (device code in the .hip files); all return the launch status
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
-                          int* meta, hipStream_t stream, const KTimer& tm);
+                          int* rec, int* meta, hipStream_t stream, const KTimer& tm);
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
                              void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
                              int D, float scale, int premultiply, hipStream_t stream);

@@ -14,10 +14,12 @@
 // totals into the segment offsets.  Pass 3 lets every wave walk its chunk in token
 // order, 64 tokens at a time; lanes holding the same key are grouped with ballots and
 // ranked by lane order, so each key's tokens land in increasing token order: the
-// result is the unique stable order, identical on every run.  The active-slot list, a
-// 16-byte descriptor per active slot (slot, tokens, first sorted position) that lets a
-// kernel start from a single load, and the matrix-core tile list are compacted in slot
-// order by one wave.
+// result is the unique stable order, identical on every run.  Every slot also gets a
+// 128-byte record (tokens, first sorted position, then its first kRecTokens token ids
+// in sorted order), so that a kernel unit of a short segment finds its token rows with
+// the same load that tells it the segment; the active-slot list, a 16-byte descriptor
+// per active slot (slot, tokens, first sorted position) and the matrix-core tile list
+// are compacted in slot order by one wave.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -28,12 +30,13 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
     const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
     int* __restrict__ counts, int* __restrict__ offs, int* __restrict__ sorted,
     int* __restrict__ active, int4* __restrict__ desc, int4* __restrict__ tiles,
-    int* __restrict__ meta) {
+    int* __restrict__ rec, int* __restrict__ meta) {
   extern __shared__ int lds[];
   const int K = S + 1;                         // keys 0..S-1 are slots, S is "no LoRA"
   int* hist = lds;                             // [kRoutingWaves][K]
   int* start = lds + kRoutingWaves * K;        // [K]: counts, then segment starts
   int* misc = start + K;                       // [4]
+  int* first = misc + 4;                       // [K]: first token of each segment
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   for (int i = tid; i < kRoutingWaves * K; i += kRoutingThreads) hist[i] = 0;
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
       const int c = start[key];
       start[key] = run;
       offs[key] = run;
+      if (key < S) *reinterpret_cast<int4*>(rec + (size_t)key * kRecInts) = make_int4(c, run, 0, 0);
       run += c;
     }
     if (lane == 63) offs[K] = incl;            // == T
@@ -106,11 +110,21 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
       if (valid && key == k0) {
         const int rank = __popcll(m & ((1ull << lane) - 1ull));
         sorted[start[k0] + base + rank] = t;
+        if (k0 < S && base + rank < kRecTokens) rec[(size_t)k0 * kRecInts + 4 + base + rank] = t;
+        if (base + rank == 0) first[k0] = t;
       }
       rem &= ~m;
     }
   }
   __syncthreads();
+
+  // record entries past a segment's tokens repeat its first token (token 0 for an
+  // empty segment), so that every entry names a valid row of the batch
+  for (int i = tid; i < S * kRecTokens; i += kRoutingThreads) {
+    const int key = i / kRecTokens, e = i - key * kRecTokens;
+    const int c = start[key + 1] - start[key];
+    if (e >= c) rec[(size_t)key * kRecInts + 4 + e] = c > 0 ? first[key] : 0;
+  }
 
   // lists, in slot order: active slots, and tiles of the segments long enough for
   // the matrix-core path (slot, first sorted position, length)
@@ -146,10 +160,10 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
 
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
-                          int* meta, hipStream_t stream, const KTimer& tm) {
-  const size_t lds = (size_t)(kRoutingWaves * (S + 1) + (S + 1) + 4) * sizeof(int);
+                          int* rec, int* meta, hipStream_t stream, const KTimer& tm) {
+  const size_t lds = (size_t)(kRoutingWaves * (S + 1) + 2 * (S + 1) + 4) * sizeof(int);
   RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(kRoutingThreads), (uint32_t)lds, stream, ids, T, S,
-             mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, meta);
+             mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, rec, meta);
   return hipGetLastError();
 }
 

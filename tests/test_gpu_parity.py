@@ -406,7 +406,7 @@ def test_workload_parity(rx, num):
 
 # ------------------------------------------------------ matrix-core segments
 @pytest.mark.parametrize("segments,Rmax,slices", [
-    ([16, 17, 63, 64, 65, 300], 64, [4096]),          # around the tile size, mixed ranks
+    ([16, 17, 31, 32, 33, 63, 64, 65, 300], 64, [4096]),  # around the tile size, mixed ranks
     ([128, 33, 200], 16, [4096, 1024, 1024]),          # packed slices
     ([40, 7, 90, 3, 129], 40, [520]),                  # rank not a multiple of 32, ragged d
     ([513], 8, [8200]),                                # one long segment, rank 8
