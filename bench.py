@@ -247,6 +247,42 @@ def run(args):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
                 "bytes_per_launch": int(per_launch), "avg_launch_us": round(cand[dom]["avg_us"], 3)}
 
+    # per-step distribution (events around each step) and the device's own floors:
+    # the shortest kernel (a one-element fill) and a plain copy of 512 MiB
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    pct = {f"p{q}": round(per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))], 3) for q in (10, 50, 90)}
+    tiny = torch.zeros(1, device="cuda")
+    src_c = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    dst_c = torch.empty_like(src_c)
+    for _ in range(5):
+        tiny.fill_(1.0)
+        dst_c.copy_(src_c)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(100):
+        tiny.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    floor_us = a.elapsed_time(b) * 10.0
+    a.record()
+    for _ in range(10):
+        dst_c.copy_(src_c)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src_c.numel() * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src_c, dst_c
+    log(f"per-step p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']} us; shortest-kernel floor {floor_us:.2f} us; "
+        f"copy ceiling {copy_gbps:.0f} GB/s")
+    roofline["copy_ceiling_gbps"] = round(copy_gbps, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -258,7 +294,8 @@ def run(args):
         "roofline": roofline,
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
-                  "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "source_digest": source_digest()},
+                  "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
+                  "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest()},
     }
     for inst in insts:
         inst.close()

@@ -251,6 +251,7 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   pl.nsplit = pool->nsplit;
   pl.ns = pool->ns;
   pl.nrg = ceil_div(pool->N * pool->Rmax, 64);
+  pl.xcd_group = std::max(1, std::min(64, env_int("RAXLORA_XCD_GROUP", 4)));
   pl.use_mfma = use_mfma(pool) && r->T >= r->mfma_min ? 1 : 0;
   int mean = std::max(1, ceil_div(r->T, r->S));
   if (pl.use_mfma) mean = std::min(mean, r->mfma_min - 1);

@@ -96,6 +96,7 @@ struct Plan {
   int n_dec_blocks;        // workgroups of the decode part
   int tile_slots;          // matrix-core part: tiles handled in parallel
   int use_mfma;            // long segments go to the matrix-core part
+  int xcd_group;           // consecutive units dealt to one XCD (1 = plain round-robin)
 };
 
 // Optional per-launch timing: when start is non-null the kernel is launched with

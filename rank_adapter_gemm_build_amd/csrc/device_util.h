@@ -197,12 +197,16 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, long lo
   return v;
 }
 
-// Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
-// Renumber so that consecutive logical indices share an XCD and its L2: with the
-// grid padded to 8 * per blocks, logical = (b % 8) * per + b / 8 is a bijection on
-// [0, 8 * per); callers skip logical indices past their item count.
-__device__ __forceinline__ int xcd_logical_block(int b, int per) {
-  return (b & 7) * per + (b >> 3);
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8),
+// and each XCD has its own L2.  The renumbering below deals logical units to the
+// XCDs in groups of g consecutive units (group q to XCD q % 8), so units that read
+// the same weights or rows (neighbours in the numbering) share one L2, while work
+// spread unevenly along the numbering still lands on every XCD.  It is a bijection
+// on [0, grid) when grid is a multiple of 8 * g; g = 1 is the identity.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_block(int b, int g) {
+  const int x = b % kXcds, i = b / kXcds;
+  return ((i / g) * kXcds + x) * g + i % g;
 }
 
 }  // namespace rax

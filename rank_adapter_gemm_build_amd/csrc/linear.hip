@@ -152,8 +152,9 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
 // One wave per workgroup: decode units first, then (tile slot, row group, k part) units.
 template <typename T>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
-                                                    int ldx, UView U, Plan plan) {
-  const int b = blockIdx.x;
+                                                    int ldx, UView U, Plan plan, int n_units) {
+  const int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
+  if (b >= n_units) return;
   if (b < plan.n_dec_blocks) {
     shrink_decode_unit<T>(P, R, x, ldx, U, plan, b);
     return;
@@ -172,15 +173,17 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
 template <typename T>
 static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, int ldx, const UView& U,
                             const Plan& plan, hipStream_t stream, const KTimer& tm) {
-  const int blocks = plan.n_dec_blocks + (plan.use_mfma ? plan.tile_slots * plan.nrg * plan.nsplit : 0);
-  RAX_LAUNCH(tm, shrink_kernel<T>, dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan);
+  const int units = plan.n_dec_blocks + (plan.use_mfma ? plan.tile_slots * plan.nrg * plan.nsplit : 0);
+  const int q = kXcds * plan.xcd_group;
+  const int blocks = (units + q - 1) / q * q;
+  RAX_LAUNCH(tm, shrink_kernel<T>, dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, units);
 }
 
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
                          const UView& U, const Plan& plan, hipStream_t stream, const KTimer& tm) {
   const int cw = 64 * (wdtype == LORA_BF16 ? 8 : 4);
   const int chunks = (P.k + cw - 1) / cw;
-  if (U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
+  if (plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
       plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
       plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
       (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)))
@@ -325,9 +328,10 @@ template <typename TW, typename TY>
 __device__ __forceinline__ void expand_decode_item(const PoolView& P, const RouteView& R, const UView& U,
                                                    TY* __restrict__ y, int ldy, const Plan& plan,
                                                    int item, float* __restrict__ usm) {
-  const int ct = item % P.n_ctiles;
-  const int rest = item / P.n_ctiles;
-  const int tg = rest % plan.ntg, s = rest / plan.ntg;
+  // token-tile siblings (same slot and columns, same rows of B^T) are neighbours
+  const int tg = item % plan.ntg;
+  const int rest = item / plan.ntg;
+  const int ct = rest % P.n_ctiles, s = rest / P.n_ctiles;
   // first round trip: record header, token ids of the first tile, slot-table entry
   // (tiles start every kExpandTok tokens; segments of 1 or 2 tokens have one tile)
   const int tt0 = tg * kExpandTok;
@@ -355,9 +359,10 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
 // One wave per workgroup: decode items first, then (tile slot, column-block group) units.
 template <typename TW, typename TY, int KSM>
 __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UView U,
-                                                    TY* __restrict__ y, int ldy, Plan plan) {
+                                                    TY* __restrict__ y, int ldy, Plan plan, int n_units) {
   extern __shared__ float smem[];
-  const int b = blockIdx.x;
+  const int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
+  if (b >= n_units) return;
   if (b < plan.n_dec_blocks) {
     expand_decode_item<TW, TY>(P, R, U, y, ldy, plan, b, smem);
     return;
@@ -374,13 +379,13 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UVi
 
 template <typename TY>
 static void launch_expand_bf16(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
-                               const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan,
+                               const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int units,
                                const KTimer& tm) {
   switch (ksm) {
-    case 1: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
-    case 2: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
-    case 4: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
-    default: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
+    case 1: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
+    case 2: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
+    case 4: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
+    default: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
   }
 }
 
@@ -393,25 +398,26 @@ size_t expand_smem_bytes(int wdtype, int Rmax, int use_mfma) {
 hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
                          const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,
                          const KTimer& tm) {
-  if (plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
+  if (plan.xcd_group < 1 || plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
       (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
       plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
       (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1)))
     return hipErrorInvalidValue;
   const int ng = (P.n_mblocks + kMfmaColBlocksPerUnit - 1) / kMfmaColBlocksPerUnit;
-  const int blocks = plan.n_dec_blocks + (plan.use_mfma ? ng * plan.tile_slots : 0);
-  const dim3 grid(blocks);
+  const int units = plan.n_dec_blocks + (plan.use_mfma ? ng * plan.tile_slots : 0);
+  const int q = kXcds * plan.xcd_group;
+  const dim3 grid((units + q - 1) / q * q);
   const uint32_t lds = (uint32_t)expand_smem_bytes(wdtype, P.Rmax, plan.use_mfma);
   if (wdtype == LORA_BF16) {
     // rank steps of 32 the matrix-core part keeps in registers: Rk / 32 rounded up to a power of 2
     const int ksm = P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8;
     if (ydtype == LORA_BF16)
-      launch_expand_bf16<uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, tm);
+      launch_expand_bf16<uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, units, tm);
     else
-      launch_expand_bf16<float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, tm);
+      launch_expand_bf16<float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, units, tm);
   } else {
     RAX_LAUNCH(tm, (expand_kernel<float, float, 1>), grid, dim3(64), lds, stream, P, R, U,
-               static_cast<float*>(y), ldy, plan);
+               static_cast<float*>(y), ldy, plan, units);
   }
   return hipGetLastError();
 }
