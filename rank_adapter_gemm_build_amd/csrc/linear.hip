@@ -241,18 +241,22 @@ template <> struct Row8<float> {
   }
 };
 
-// rank rows of B^T in flight per lane: 16 for bf16 pools (64 registers), 8 for fp32
-template <typename TW> struct ExpandRows { static constexpr int kBatch = sizeof(TW) == 2 ? 16 : 8; };
 
-// LDS floats per wave for the decode expand: kExpandTok tokens x the rank padded to 16
+// LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
 __host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }
 
-template <typename TW, typename TY, int LTE>
+// One decode expand item: column tile [c0, c0 + 512) of slice n, token tiles
+// tt0, tt0 + 4 * ntg, ... of slot s.  Every tile is processed as 4 tokens (rows past
+// the segment's end read a valid row and are not stored), so there is one code path.
+// The tile's rank-space values sit in LDS token-fastest (usm[4 j + i]), so one
+// 16-byte read gives rank j for all 4 tokens; rows of B^T are consumed 4 at a time
+// behind scheduling fences, which bounds how many values are live at once.
+template <typename TW, typename TY, int RB>
 __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const RouteView& R, const UView& U,
                                                     TY* __restrict__ y, int ldy, int s, const SlotEntry& e,
                                                     int n, int c0, int L, int p0, int tt0, int4 tq0, int ntg,
                                                     float* __restrict__ usm) {
-  constexpr int RB = ExpandRows<TW>::kBatch;
+  constexpr int LT = kExpandTok;
   const int lane = lane_id();
   const int r = e.rank, dn = P.d[n];
   const int rp = (r + RB - 1) / RB * RB;            // rank padded to the row batch
@@ -260,13 +264,14 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   const bool inb = col < dn;
   const int colc = min(col, dn - kColsPerLane);
   const TW* __restrict__ bt = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n] + colc;
-  for (int tt = tt0; tt < L; tt += ntg * LTE) {
-    const int nt = min(LTE, L - tt);
+  const float4* __restrict__ u4 = reinterpret_cast<const float4*>(usm);
+  for (int tt = tt0; tt < L; tt += ntg * LT) {
+    const int nt = min(LT, L - tt);
     const int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
     // one batch: the rank-space values of the tile (first: they are needed first),
     // the first RB rows of B^T, the token rows of y
-    for (int idx = lane; idx < LTE * rp; idx += 64) {
-      const int i = idx / rp, j = idx - i * rp;
+    for (int idx = lane; idx < LT * rp; idx += 64) {
+      const int j = idx >> 2, i = idx & 3;
       const bool ok = i < nt && j < r;
       const int ic = ok ? i : 0, jc = ok ? j : 0;
       const long long row = U.by_token ? (long long)R.sorted[p0 + tt + ic] : (long long)(p0 + tt + ic);
@@ -276,41 +281,50 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
     Row8<TW> b[RB];
 #pragma unroll
     for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jj < r ? jj : 0) * P.D);
-    Row8<TY> yv[LTE];
-    TY* yrow[LTE];
+    Row8<TY> yv[LT];
+    TY* yrow[LT];
 #pragma unroll
-    for (int i = 0; i < LTE; ++i) {
+    for (int i = 0; i < LT; ++i) {
       yrow[i] = y + (size_t)tok_at(tq, i) * ldy + P.o[n] + colc;
       yv[i].load(yrow[i]);
     }
     wave_lds_sync();
-    float acc[LTE][kColsPerLane];
+    float acc[LT][kColsPerLane];
 #pragma unroll
-    for (int i = 0; i < LTE; ++i)
+    for (int i = 0; i < LT; ++i)
 #pragma unroll
       for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = 0.f;
-    for (int jb = 0; jb < rp; jb += RB) {
-      if (jb > 0) {
+    // rows [jb, jb + RB) of B^T against the staged rank-space values
+    auto contract = [&](int jb) {
 #pragma unroll
-        for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jb + jj < r ? jb + jj : 0) * P.D);
+      for (int j4 = 0; j4 < RB; j4 += 4) {
+#pragma unroll
+        for (int jj = j4; jj < j4 + 4; ++jj) {
+          b[jj].keep(jb + jj < r);
+          float bf[kColsPerLane];
+          b[jj].get(bf);
+          const float4 uq = u4[jb + jj];
+          const float uv[LT] = {uq.x, uq.y, uq.z, uq.w};
+#pragma unroll
+          for (int i = 0; i < LT; ++i)
+#pragma unroll
+            for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = fmaf(bf[c], uv[i], acc[i][c]);
+        }
         sched_fence();
       }
+    };
+    sched_fence();
+    contract(0);
+    // ranks above RB: further batches of rows, each loaded after the previous is used
+    for (int jb = RB; jb < rp; jb += RB) {
 #pragma unroll
-      for (int jj = 0; jj < RB; ++jj) {
-        b[jj].keep(jb + jj < r);
-        float bf[kColsPerLane];
-        b[jj].get(bf);
-#pragma unroll
-        for (int i = 0; i < LTE; ++i) {
-          const float uij = usm[i * rp + jb + jj];
-#pragma unroll
-          for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = fmaf(bf[c], uij, acc[i][c]);
-        }
-      }
+      for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jb + jj < r ? jb + jj : 0) * P.D);
+      sched_fence();
+      contract(jb);
     }
     if (inb) {
 #pragma unroll
-      for (int i = 0; i < LTE; ++i) {
+      for (int i = 0; i < LT; ++i) {
         if (i < nt) {
           float v[kColsPerLane];
           yv[i].get(v);
@@ -333,7 +347,6 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   const int rest = item / plan.ntg;
   const int ct = rest % P.n_ctiles, s = rest / P.n_ctiles;
   // first round trip: record header, token ids of the first tile, slot-table entry
-  // (tiles start every kExpandTok tokens; segments of 1 or 2 tokens have one tile)
   const int tt0 = tg * kExpandTok;
   const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
   int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
@@ -348,12 +361,11 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
   if (!((e.slice_mask >> n) & 1u)) return;
   const int c0 = (ct - P.tile0[n]) * kTileCols;
-  if (L == 1)
-    expand_decode_tiles<TW, TY, 1>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
-  else if (L == 2)
-    expand_decode_tiles<TW, TY, 2>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
+  // rank rows of B^T per load batch: 16 for bf16 pools (64 registers), 8 for fp32
+  if (sizeof(TW) == 2)
+    expand_decode_tiles<TW, TY, 16>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
   else
-    expand_decode_tiles<TW, TY, kExpandTok>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
+    expand_decode_tiles<TW, TY, 8>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
 }
 
 // One wave per workgroup: decode items first, then (tile slot, column-block group) units.

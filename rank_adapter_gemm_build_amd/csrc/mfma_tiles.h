@@ -236,7 +236,7 @@ __device__ __forceinline__ void expand_mfma_block(const PoolView& P, const Route
                                                   float* __restrict__ ds) {
   constexpr int YC = 16 / sizeof(TY);             // y elements per 16-byte chunk
   constexpr int YCHUNKS = kMfmaTileM * kMfmaCols / YC / 64;  // y chunks per lane
-  constexpr int KP = KSM < 2 ? KSM : 2;           // rank steps per batch of B fragments
+  constexpr int KP = 1;                           // rank steps per batch of B fragments
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int dn = P.d[n];
   const uint16_t* __restrict__ bk = static_cast<const uint16_t*>(P.Bk) + ((size_t)slot * P.D + P.o[n]) * P.Rk;
