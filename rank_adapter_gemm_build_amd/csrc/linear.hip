@@ -44,34 +44,10 @@
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
+#include "decode_units.h"
 #include "mfma_tiles.h"
 
 namespace rax {
-
-constexpr int kShrinkRows = 16;   // rank rows per decode shrink unit
-constexpr int kShrinkTok = 4;     // tokens per decode shrink pass
-constexpr int kExpandTok = 4;     // tokens per decode expand pass (at most)
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Token ids at positions tt .. tt + 3 of slot s's segment: from the slot's routing
-// record when they are among its first kRecTokens (the record repeats the segment's
-// first token past its end), else from sorted_ids (position clamped into the
-// segment).  Entries at or past the segment's end name a valid row of the batch but
-// are not a token of the tile: callers read them and do not store them.
-__device__ __forceinline__ int4 segment_tokens(const RouteView& R, int s, int tt, int p0, int L) {
-  if (tt + 4 <= kRecTokens) return *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt);
-  const int last = p0 + L - 1;
-  return make_int4(R.sorted[min(p0 + tt, last)], R.sorted[min(p0 + tt + 1, last)], R.sorted[min(p0 + tt + 2, last)],
-                   R.sorted[min(p0 + tt + 3, last)]);
-}
-
-// element i (a compile-time constant after unrolling) of a token quad
-__device__ __forceinline__ int tok_at(const int4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // ------------------------------------------------------------ decode shrink
 template <typename T>
@@ -97,18 +73,7 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
   const int r = e.rank, F = P.N * r, fb = rb * kShrinkRows;
   if (r == 0 || fb >= F) return;                   // all of the above is uniform per wave
   const int lane = lane_id();
-  const T* __restrict__ Aslot = static_cast<const T*>(P.A) + (size_t)s * P.N * P.Rmax * P.k;
-  const T* arow[kShrinkRows];
-  bool rval[kShrinkRows];
-  {
-    int n = fb / r, j = fb - (fb / r) * r;
-#pragma unroll
-    for (int rr = 0; rr < kShrinkRows; ++rr) {
-      rval[rr] = fb + rr < F;
-      arow[rr] = Aslot + ((size_t)(rval[rr] ? n : 0) * P.Rmax + (rval[rr] ? j : 0)) * P.k;
-      if (++j == r) { j = 0; ++n; }
-    }
-  }
+  const ShrinkRows<T> A(P, s, r, fb);
   // this lane's output after the reduce-scatter: row fb + lane / 4, token lane % 4
   const int orr = lane / kShrinkTok, oi = lane - orr * kShrinkTok, of = fb + orr;
   const int on = of < F ? of / r : 0, oj = of < F ? of - on * r : 0;
@@ -120,32 +85,8 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
     const T* xrow[kShrinkTok];
 #pragma unroll
     for (int i = 0; i < kShrinkTok; ++i) xrow[i] = x + (size_t)tok_at(tq, i) * ldx;
-    float acc[64];
-#pragma unroll
-    for (int m = 0; m < 64; ++m) acc[m] = 0.f;
-    for (int c = 0; c < plan.ns; ++c) {
-      const int col = (sp + plan.nsplit * c) * CW + lane * E;
-      const bool inb = col < P.k;
-      const int colc = min(col, P.k - E);
-      // the x chunks and all 16 A rows of this chunk step in flight before the first product
-      uint4 xv[kShrinkTok], av[kShrinkRows];
-#pragma unroll
-      for (int i = 0; i < kShrinkTok; ++i) xv[i] = ld16(xrow[i] + colc);
-#pragma unroll
-      for (int rr = 0; rr < kShrinkRows; ++rr) av[rr] = ld16(arow[rr] + colc);
-      sched_fence();
-#pragma unroll
-      for (int i = 0; i < kShrinkTok; ++i) xv[i] = keep_if(xv[i], i < nt && inb);
-#pragma unroll
-      for (int rr = 0; rr < kShrinkRows; ++rr) {
-        const uint4 a = keep_if(av[rr], rval[rr]);
-#pragma unroll
-        for (int i = 0; i < kShrinkTok; ++i)
-          acc[rr * kShrinkTok + i] = chunk_dot(a, xv[i], acc[rr * kShrinkTok + i], T());
-      }
-    }
-    reduce_scatter64(acc);
-    if (of < F && oi < nt) uo[(long long)(p0 + tt + oi) * U.row_stride] = acc[0];   // rows by sorted position
+    const float v = shrink_block_partial<T>(P, A, xrow, nt, sp, plan.nsplit, plan.ns);
+    if (of < F && oi < nt) uo[(long long)(p0 + tt + oi) * U.row_stride] = v;   // rows by sorted position
   }
 }
 
@@ -223,54 +164,27 @@ hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W
 }
 
 // ------------------------------------------------------------ decode expand
-// 8 consecutive elements of a row, kept packed: one 16-byte chunk for bf16, two for fp32
-template <typename T> struct Row8;
-template <> struct Row8<uint16_t> {
-  uint4 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = ld16(p); }
-  __device__ __forceinline__ void keep(bool ok) { w = keep_if(w, ok); }
-  __device__ __forceinline__ void get(float (&v)[8]) const { unpack8(w, v); }
-};
-template <> struct Row8<float> {
-  uint4 a, b;
-  __device__ __forceinline__ void load(const float* p) { a = ld16(p); b = ld16(p + 4); }
-  __device__ __forceinline__ void keep(bool ok) { a = keep_if(a, ok); b = keep_if(b, ok); }
-  __device__ __forceinline__ void get(float (&v)[8]) const {
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
-  }
-};
-
-
 // LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
 __host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }
 
 // One decode expand item: column tile [c0, c0 + 512) of slice n, token tiles
-// tt0, tt0 + 4 * ntg, ... of slot s.  Every tile is processed as 4 tokens (rows past
-// the segment's end read a valid row and are not stored), so there is one code path.
-// The tile's rank-space values sit in LDS token-fastest (usm[4 j + i]), so one
-// 16-byte read gives rank j for all 4 tokens; rows of B^T are consumed 4 at a time
-// behind scheduling fences, which bounds how many values are live at once.
-template <typename TW, typename TY, int RB>
+// tt0, tt0 + 4 * ntg, ... of slot s.  Per tile: the tile's rank-space values (split
+// partials added in split order, from L2) are staged in the wave's LDS token-fastest,
+// then the B^T rows and y rows are issued, then the contraction.
+template <typename TW, typename TY>
 __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const RouteView& R, const UView& U,
                                                     TY* __restrict__ y, int ldy, int s, const SlotEntry& e,
                                                     int n, int c0, int L, int p0, int tt0, int4 tq0, int ntg,
                                                     float* __restrict__ usm) {
-  constexpr int LT = kExpandTok;
+  using Tile = ExpandTile<TW, TY>;
   const int lane = lane_id();
-  const int r = e.rank, dn = P.d[n];
-  const int rp = (r + RB - 1) / RB * RB;            // rank padded to the row batch
-  const int col = c0 + lane * kColsPerLane;
-  const bool inb = col < dn;
-  const int colc = min(col, dn - kColsPerLane);
-  const TW* __restrict__ bt = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n] + colc;
-  const float4* __restrict__ u4 = reinterpret_cast<const float4*>(usm);
-  for (int tt = tt0; tt < L; tt += ntg * LT) {
-    const int nt = min(LT, L - tt);
+  const int r = e.rank;
+  const int rp = (r + Tile::RB - 1) / Tile::RB * Tile::RB;   // rank padded to the row batch
+  const TW* __restrict__ bt_slot = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n];
+  for (int tt = tt0; tt < L; tt += ntg * kExpandTok) {
+    const int nt = min(kExpandTok, L - tt);
     const int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
-    // one batch: the rank-space values of the tile (first: they are needed first),
-    // the first RB rows of B^T, the token rows of y
-    for (int idx = lane; idx < LT * rp; idx += 64) {
+    for (int idx = lane; idx < kExpandTok * rp; idx += 64) {
       const int j = idx >> 2, i = idx & 3;
       const bool ok = i < nt && j < r;
       const int ic = ok ? i : 0, jc = ok ? j : 0;
@@ -278,62 +192,10 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
       const float v = sum_splits(U.p + n * U.n_stride + row * U.row_stride + jc, U.split_stride, U.nsplit);
       usm[idx] = ok ? v : 0.f;
     }
-    Row8<TW> b[RB];
-#pragma unroll
-    for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jj < r ? jj : 0) * P.D);
-    Row8<TY> yv[LT];
-    TY* yrow[LT];
-#pragma unroll
-    for (int i = 0; i < LT; ++i) {
-      yrow[i] = y + (size_t)tok_at(tq, i) * ldy + P.o[n] + colc;
-      yv[i].load(yrow[i]);
-    }
+    Tile tile;
+    tile.issue(P, bt_slot, y, ldy, n, c0, r, tq);
     wave_lds_sync();
-    float acc[LT][kColsPerLane];
-#pragma unroll
-    for (int i = 0; i < LT; ++i)
-#pragma unroll
-      for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = 0.f;
-    // rows [jb, jb + RB) of B^T against the staged rank-space values
-    auto contract = [&](int jb) {
-#pragma unroll
-      for (int j4 = 0; j4 < RB; j4 += 4) {
-#pragma unroll
-        for (int jj = j4; jj < j4 + 4; ++jj) {
-          b[jj].keep(jb + jj < r);
-          float bf[kColsPerLane];
-          b[jj].get(bf);
-          const float4 uq = u4[jb + jj];
-          const float uv[LT] = {uq.x, uq.y, uq.z, uq.w};
-#pragma unroll
-          for (int i = 0; i < LT; ++i)
-#pragma unroll
-            for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = fmaf(bf[c], uv[i], acc[i][c]);
-        }
-        sched_fence();
-      }
-    };
-    sched_fence();
-    contract(0);
-    // ranks above RB: further batches of rows, each loaded after the previous is used
-    for (int jb = RB; jb < rp; jb += RB) {
-#pragma unroll
-      for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jb + jj < r ? jb + jj : 0) * P.D);
-      sched_fence();
-      contract(jb);
-    }
-    if (inb) {
-#pragma unroll
-      for (int i = 0; i < LT; ++i) {
-        if (i < nt) {
-          float v[kColsPerLane];
-          yv[i].get(v);
-#pragma unroll
-          for (int c = 0; c < kColsPerLane; ++c) v[c] = v[c] + e.scale * acc[i][c];
-          store8f(yrow[i], v);
-        }
-      }
-    }
+    tile.finish(P, r, nt, e.scale, reinterpret_cast<const float4*>(usm));
     wave_lds_sync();
   }
 }
@@ -361,11 +223,7 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
   if (!((e.slice_mask >> n) & 1u)) return;
   const int c0 = (ct - P.tile0[n]) * kTileCols;
-  // rank rows of B^T per load batch: 16 for bf16 pools (64 registers), 8 for fp32
-  if (sizeof(TW) == 2)
-    expand_decode_tiles<TW, TY, 16>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
-  else
-    expand_decode_tiles<TW, TY, 8>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
+  expand_decode_tiles<TW, TY>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
 }
 
 // One wave per workgroup: decode items first, then (tile slot, column-block group) units.

@@ -89,11 +89,12 @@ __device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<NB>& f, bool 
   }
 }
 
-// Rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1); writes partial `part`.
+// Products of rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1): lane
+// holds D[token 4 * lk + i][row fr0 + 16 b + lr] in acc[b][i].
 template <int NB>
-__device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
-                                                 int ldx, const UView& U, int slot, int r, int p0, int len, int fr0,
-                                                 int part, int s0, int s1) {
+__device__ __forceinline__ void shrink_mfma_acc(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
+                                                int ldx, int slot, int r, int p0, int len, int fr0, int s0, int s1,
+                                                f32x4_t (&acc)[NB]) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int F = P.N * r;
   const bool tval = lr < len;
@@ -109,7 +110,6 @@ __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const RouteV
     const int n = fc / r, j = fc - n * r;
     arow[b] = Aslot + ((size_t)n * P.Rmax + j) * P.k;
   }
-  f32x4_t acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int last = max(s1 - 1, 0);
@@ -125,6 +125,25 @@ __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const RouteV
     shrink_mma_group<NB>(f1, tval, rval, sg + kMfmaGroup, s1, P.k, lk, acc);
     sched_fence();
   }
+}
+
+// k range [s0, s1) of the steps of 32 that part `part` of nsplit takes (contiguous parts)
+__device__ __forceinline__ void mfma_part_range(int k, int part, int nsplit, int& s0, int& s1) {
+  const int steps = (k + kMfmaK - 1) / kMfmaK;
+  const int per = (steps + nsplit - 1) / nsplit;
+  s0 = min(steps, part * per);
+  s1 = min(steps, s0 + per);
+}
+
+// Rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1); writes partial `part`.
+template <int NB>
+__device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
+                                                 int ldx, const UView& U, int slot, int r, int p0, int len, int fr0,
+                                                 int part, int s0, int s1) {
+  const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+  const int F = P.N * r;
+  f32x4_t acc[NB];
+  shrink_mfma_acc<NB>(P, R, x, ldx, slot, r, p0, len, fr0, s0, s1, acc);
   // lane holds D[token 4 * lk + i][row fr0 + 16 b + lr]; rows by sorted position
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -150,9 +169,8 @@ __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteV
   const SlotEntry e = P.table[slot];
   const int r = e.rank, F = P.N * r, fr0 = 64 * rg;
   if (r == 0 || fr0 >= F) return;
-  const int steps = (P.k + kMfmaK - 1) / kMfmaK;
-  const int per = (steps + nsplit - 1) / nsplit;
-  const int s0 = min(steps, part * per), s1 = min(steps, s0 + per);
+  int s0, s1;
+  mfma_part_range(P.k, part, nsplit, s0, s1);
   const int nb = min(4, (F - fr0 + 15) / 16);
   if (nb == 4)
     shrink_mfma_rows<4>(P, R, x, ldx, U, slot, r, p0, len, fr0, part, s0, s1);
@@ -165,6 +183,19 @@ __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteV
 }
 
 // ------------------------------------------------------------------ expand
+// 8 fp32 values as the bf16 pair hi = bf16(v), lo = bf16(v - hi), packed as MFMA operands
+__device__ __forceinline__ void u_hilo(const float (&v)[8], uint4& uh, uint4& ul) {
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t h0 = f32_to_bf16(v[2 * q]), h1 = f32_to_bf16(v[2 * q + 1]);
+    hi[q] = h0 | (h1 << 16);
+    lo[q] = f32_to_bf16(v[2 * q] - __uint_as_float(h0 << 16)) | (f32_to_bf16(v[2 * q + 1] - __uint_as_float(h1 << 16)) << 16);
+  }
+  uh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  ul = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
 // This lane's rank-space values of slice n for the u fragment rows of the tile
 // (token lr, ranks 32 ks + 8 lk .. +7), finished from their split partials in split
 // order, as bf16 hi + lo parts.  Zero past the rank and past the tile's length.
@@ -216,15 +247,7 @@ __device__ __forceinline__ void expand_u_frags(const RouteView& R, const UView& 
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = (lr < len && j0 + q < r) ? v[q] : 0.f;
     }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t h0 = f32_to_bf16(v[2 * q]), h1 = f32_to_bf16(v[2 * q + 1]);
-      hi[q] = h0 | (h1 << 16);
-      lo[q] = f32_to_bf16(v[2 * q] - __uint_as_float(h0 << 16)) | (f32_to_bf16(v[2 * q + 1] - __uint_as_float(h1 << 16)) << 16);
-    }
-    uh[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    ul[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    u_hilo(v, uh[ks], ul[ks]);
   }
 }
 
