@@ -23,8 +23,8 @@ constexpr int kMaxSlices = LORA_MAX_SLICES;
 constexpr int kMaxSplit = 16;         // k splits of a decode shrink (partial sums per split)
 constexpr int kColsPerLane = 8;    // expand: output columns owned by one lane
 constexpr int kTileCols = 64 * kColsPerLane;  // expand: columns of one wave tile
-constexpr int kRoutingThreads = 512;
-constexpr int kRoutingWaves = kRoutingThreads / 64;
+constexpr int kRoutingMaxThreads = 1024;   // routing workgroup: 16 waves (8 for large slot counts)
+constexpr int kRoutingStageBatch = 16;   // ids each routing thread loads in one batch
 constexpr int kMfmaTileM = 16;     // tokens per matrix-core tile of a long segment
 constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
 constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block

@@ -8,13 +8,17 @@
 // the counts, and requests without an adapter go to a sentinel slot after the real ones
 // (section "adapter 池:AdapterSlotManager").
 //
-// One workgroup of 8 waves.  The token range is cut into 8 contiguous chunks, one per
-// wave.  Pass 1 builds a per-wave histogram in LDS.  Pass 2 turns it, key by key, into
-// the start of each wave's run inside the key's segment, and one wave scans the key
-// totals into the segment offsets.  Pass 3 lets every wave walk its chunk in token
-// order, 64 tokens at a time; lanes holding the same key are grouped with ballots and
-// ranked by lane order, so each key's tokens land in increasing token order: the
-// result is the unique stable order, identical on every run.  Every slot also gets a
+// One workgroup of 8 waves (16 for large batches).  All ids are read once, in
+// one batch of independent loads, and kept in LDS as 16-bit keys (when the batch
+// fits; else each pass reads them again).  The token range is cut into contiguous
+// chunks, one per wave.  Pass 1 builds a per-wave histogram in LDS.  Pass 2 turns
+// it, key by key, into the start of each wave's run inside the key's segment, and
+// one wave scans the key totals into the segment offsets.  Pass 3 lets every wave
+// walk its chunk in token order, 64 tokens at a time; each lane finds the lanes
+// holding its key with one ballot per key bit (the intersection of the matching bit
+// masks) and ranks itself by lane order, so each key's tokens land in increasing
+// token order: the result is the unique stable
+// order, identical on every run.  Every slot also gets a
 // 128-byte record (tokens, first sorted position, then its first kRecTokens token ids
 // in sorted order), so that a kernel unit of a short segment finds its token rows with
 // the same load that tells it the segment; the active-slot list, a 16-byte descriptor
@@ -26,42 +30,90 @@
 
 namespace rax {
 
-__global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
-    const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
+// Lanes of this wave whose key equals this lane's (keys below 2^nbits; lanes with
+// key < 0 match nothing), as a 64-bit mask.
+__device__ __forceinline__ unsigned long long match_key(int key, int nbits) {
+  unsigned long long m = __ballot(key >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const unsigned long long bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return key >= 0 ? m : 0ull;
+}
+
+__global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
+    const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles, int stage,
     int* __restrict__ counts, int* __restrict__ offs, int* __restrict__ sorted,
     int* __restrict__ active, int4* __restrict__ desc, int4* __restrict__ tiles,
     int* __restrict__ rec, int* __restrict__ meta) {
   extern __shared__ int lds[];
+  const int NW = blockDim.x / 64, NT = blockDim.x;   // waves and threads of the workgroup
   const int K = S + 1;                         // keys 0..S-1 are slots, S is "no LoRA"
-  int* hist = lds;                             // [kRoutingWaves][K]
-  int* start = lds + kRoutingWaves * K;        // [K]: counts, then segment starts
+  int* hist = lds;                             // [NW][K]
+  int* start = lds + NW * K;                   // [K]: counts, then segment starts
   int* misc = start + K;                       // [4]
   int* first = misc + 4;                       // [K]: first token of each segment
+  uint16_t* key16 = reinterpret_cast<uint16_t*>(first + K);   // [T] when staged
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int nbits = 0;
+  while ((1 << nbits) <= S) ++nbits;           // keys 0..S fit in nbits bits
 
-  for (int i = tid; i < kRoutingWaves * K; i += kRoutingThreads) hist[i] = 0;
+  for (int i = tid; i < NW * K; i += NT) hist[i] = 0;
   if (tid < 4) misc[tid] = 0;
+  // all ids in batches of kRoutingStageBatch independent loads per thread; invalid ids counted
+  int invalid = 0;
+  if (stage) {
+    for (int b0 = 0; b0 < T; b0 += NT * kRoutingStageBatch) {
+      int v[kRoutingStageBatch];
+#pragma unroll
+      for (int q = 0; q < kRoutingStageBatch; ++q) {
+        const int t = b0 + q * NT + tid;
+        v[q] = t < T ? ids[t] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < kRoutingStageBatch; ++q) {
+        const int t = b0 + q * NT + tid;
+        if (t < T) {
+          const bool ok = v[q] >= 0 && v[q] < S;
+          invalid += (!ok && v[q] != -1) ? 1 : 0;
+          key16[t] = (uint16_t)(ok ? v[q] : S);
+        }
+      }
+    }
+  }
   __syncthreads();
 
-  const int chunk = (T + kRoutingWaves - 1) / kRoutingWaves;
+  const int chunk = (T + NW - 1) / NW;
   const int t0 = min(T, w * chunk), t1 = min(T, t0 + chunk);
-
-  // pass 1: per-wave histograms, invalid ids counted
-  int invalid = 0;
-  for (int t = t0 + lane; t < t1; t += 64) {
+  auto key_of = [&](int t) -> int {
+    if (stage) return key16[t];
     const int id = ids[t];
-    const bool ok = id >= 0 && id < S;
-    invalid += (!ok && id != -1) ? 1 : 0;
-    atomicAdd(&hist[w * K + (ok ? id : S)], 1);
+    return (id >= 0 && id < S) ? id : S;
+  };
+
+  // pass 1: per-wave histograms (one LDS add per distinct key of a group)
+  for (int g = t0; g < t1; g += 64) {
+    const int t = g + lane;
+    int key = -1;
+    if (t < t1) {
+      key = key_of(t);
+      if (!stage) {
+        const int id = ids[t];
+        invalid += (id < -1 || id >= S) ? 1 : 0;
+      }
+    }
+    const unsigned long long m = match_key(key, nbits);
+    if (key >= 0 && (m >> lane) == 1ull) atomicAdd(&hist[w * K + key], __popcll(m));   // last lane of its key
   }
   invalid = wave_sum(invalid);
   if (lane == 0 && invalid) atomicAdd(&misc[0], invalid);
   __syncthreads();
 
   // pass 2a: per key, exclusive prefix over the waves; key totals
-  for (int key = tid; key < K; key += kRoutingThreads) {
+  for (int key = tid; key < K; key += NT) {
     int run = 0;
-    for (int ww = 0; ww < kRoutingWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int h = hist[ww * K + key];
       hist[ww * K + key] = run;
       run += h;
@@ -93,34 +145,23 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
   // pass 3: stable scatter, each wave over its own chunk in token order
   for (int g = t0; g < t1; g += 64) {
     const int t = g + lane;
-    const bool valid = t < t1;
-    int key = -1;
-    if (valid) {
-      const int id = ids[t];
-      key = (id >= 0 && id < S) ? id : S;
-    }
-    unsigned long long rem = __ballot(valid);
-    while (rem) {
-      const int leader = __ffsll(rem) - 1;
-      const int k0 = __shfl(key, leader);
-      const unsigned long long m = __ballot(valid && key == k0);
-      int base = 0;
-      if (lane == leader) base = atomicAdd(&hist[w * K + k0], __popcll(m));
-      base = __shfl(base, leader);
-      if (valid && key == k0) {
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        sorted[start[k0] + base + rank] = t;
-        if (k0 < S && base + rank < kRecTokens) rec[(size_t)k0 * kRecInts + 4 + base + rank] = t;
-        if (base + rank == 0) first[k0] = t;
-      }
-      rem &= ~m;
+    const int key = t < t1 ? key_of(t) : -1;
+    const unsigned long long m = match_key(key, nbits);
+    if (key >= 0) {
+      const int base = hist[w * K + key];
+      const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
+      sorted[start[key] + rank] = t;
+      if (key < S && rank < kRecTokens) rec[(size_t)key * kRecInts + 4 + rank] = t;
+      if (rank == 0) first[key] = t;
+      // the key's last lane advances the wave's running offset (all lanes read it above)
+      if ((m >> lane) == 1ull) hist[w * K + key] = base + __popcll(m);
     }
   }
   __syncthreads();
 
   // record entries past a segment's tokens repeat its first token (token 0 for an
   // empty segment), so that every entry names a valid row of the batch
-  for (int i = tid; i < S * kRecTokens; i += kRoutingThreads) {
+  for (int i = tid; i < S * kRecTokens; i += NT) {
     const int key = i / kRecTokens, e = i - key * kRecTokens;
     const int c = start[key + 1] - start[key];
     if (e >= c) rec[(size_t)key * kRecInts + 4 + e] = c > 0 ? first[key] : 0;
@@ -161,9 +202,17 @@ __global__ __launch_bounds__(kRoutingThreads) void routing_kernel(
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm) {
-  const size_t lds = (size_t)(kRoutingWaves * (S + 1) + 2 * (S + 1) + 4) * sizeof(int);
-  RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(kRoutingThreads), (uint32_t)lds, stream, ids, T, S,
-             mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, rec, meta);
+  // 16 waves for large batches when their histograms leave room (the per-token passes
+  // are bound by the one CU's vector throughput), else 8 (fewer waves to start and
+  // synchronise); keys kept in LDS when they fit next to the histograms (64 KB in all)
+  const size_t fixed = (size_t)(2 * (S + 1) + 4) * sizeof(int);
+  const int nw = T >= 2048 && fixed + (size_t)16 * (S + 1) * sizeof(int) <= 32768 ? 16 : 8;
+  const size_t base = fixed + (size_t)nw * (S + 1) * sizeof(int);
+  const size_t keys = ((size_t)T * sizeof(uint16_t) + 15) / 16 * 16;
+  const int stage = base + keys <= 65536 ? 1 : 0;
+  const size_t lds = base + (stage ? keys : 0);
+  RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(64 * nw), (uint32_t)lds, stream, ids, T, S,
+             mfma_min, tile_m, max_tiles, stage, counts, offs, sorted, active, desc, tiles, rec, meta);
   return hipGetLastError();
 }
 
