@@ -150,6 +150,9 @@ rax::PoolView pool_view(const lora_pool* p) {
   v.D = p->D;
   v.n_ctiles = p->tile0[p->N];
   v.n_mblocks = p->mblk0[p->N];
+  v.n_mgroups = 0;
+  for (int n = 0; n < p->N; ++n)
+    v.n_mgroups += (p->mblk0[n + 1] - p->mblk0[n] + rax::kMfmaColBlocksPerUnit - 1) / rax::kMfmaColBlocksPerUnit;
   for (int n = 0; n < rax::kMaxSlices; ++n) {
     v.d[n] = n < p->N ? p->d[n] : 0;
     v.o[n] = n < p->N ? p->o[n] : 0;
@@ -244,8 +247,8 @@ bool use_mfma(const lora_pool* pool) {
 // Launch shape of a call, from host-known sizes only (T, S, the pool's shape): the
 // expected segment length T / S sets how many waves share one segment's token tiles
 // (segments of at least mfma_min tokens go to the matrix cores when those are on),
-// and the matrix-core tile slots cover the tiles a batch of T tokens produces in the
-// common case (the kernels loop over any excess).
+// and the matrix-core tile slots cover every tile a batch of T tokens can produce
+// (the kernels would loop over any excess).
 rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   rax::Plan pl{};
   pl.nsplit = pool->nsplit;
@@ -260,7 +263,8 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   pl.nrb = ceil_div(pool->N * pool->Rmax, 16);
   // one workgroup per decode unit
   pl.n_dec_blocks = expand ? pool->tile0[pool->N] * pool->S * pl.ntg : pool->S * pl.nrb * pl.nsplit * pl.ntg;
-  pl.tile_slots = std::max(1, std::min(r->max_tiles, ceil_div(r->T, r->tile_m) + 16));
+  // tiles <= T / tile_m + (segments of at least mfma_min tokens), rounded up
+  pl.tile_slots = std::max(1, std::min(r->max_tiles, ceil_div(r->T, r->tile_m) + std::min(r->S, ceil_div(r->T, r->mfma_min))));
   return pl;
 }
 
@@ -467,7 +471,8 @@ lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* 
     }
     char* A_dst = static_cast<char*>(pool->A) + (((size_t)slot * pool->N + n) * pool->Rmax) * pool->k * es;
     char* Bt_dst = static_cast<char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[n]) * es;
-    char* Bk_dst = static_cast<char*>(pool->Bk) + ((size_t)slot * pool->D + pool->o[n]) * pool->Rk * es;
+    char* Bk_dst = static_cast<char*>(pool->Bk) +
+                   ((size_t)slot * pool->D * pool->Rk + (size_t)pool->o[n] * rax::bk_stride(rank)) * es;
     e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bt_dst, Bk_dst, rank, pool->Rmax,
                                pool->Rk, pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, stream);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "pack launch"); }

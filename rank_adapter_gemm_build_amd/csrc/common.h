@@ -4,9 +4,11 @@
 //   A   [S][N][Rmax][k]     shrink weights as given (rows j >= rank are zero)
 //   Bt  [S][Rmax][D]        expand weights, B transposed to rank-major rows; slice n
 //                           occupies columns [o_n, o_n + d_n) of every rank row
-//   Bk  [S][D][Rk]          expand weights with the rank contiguous (B as given,
-//                           rows padded to Rk = Rmax rounded up to 32): the
-//                           matrix-core operand layout
+//   Bk  [S][D * Rk]         expand weights with the rank contiguous (B as given),
+//                           the matrix-core operand layout: slot s's region of
+//                           D * Rk elements (Rk = Rmax rounded up to 32) holds
+//                           column c at offset c * bk_stride(rank), the slot's rank
+//                           rounded up to 8 (entries past the rank zero)
 //   table [S]               rank, scale, present-slice mask per slot
 // Slots are addressed by fixed strides, so no pointer table is needed: the
 // address of slot s is base + s * stride, formed in 64-bit arithmetic.
@@ -28,8 +30,10 @@ constexpr int kRoutingStageBatch = 16;   // ids each routing thread loads in one
 constexpr int kMfmaTileM = 16;     // tokens per matrix-core tile of a long segment
 constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
 constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block
+// elements per column of a slot's Bk region: its rank rounded up to 8
+__host__ __device__ constexpr int bk_stride(int rank) { return (rank + 7) / 8 * 8; }
 constexpr int kMfmaColBlocksPerUnit = 4;   // 128-column blocks of one matrix-core expand unit
-constexpr int kDefaultMfmaMinSeg = 16;  // segments at least this long use matrix cores
+constexpr int kDefaultMfmaMinSeg = 4;   // segments at least this long use matrix cores (bf16 pools)
 constexpr int kRecInts = 32;       // ints of one slot record: tokens, first position, 2 spare, token ids
 constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
 constexpr bool kHaveMfmaPath = true;    // matrix-core kernels compiled in
@@ -50,7 +54,7 @@ struct PoolView {
   const void* Bt;
   const void* Bk;
   const SlotEntry* table;
-  int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks;
+  int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks, n_mgroups;
   int d[kMaxSlices];
   int o[kMaxSlices];
   int tile0[kMaxSlices + 1];  // first expand column tile of each slice; tile0[N] = n_ctiles

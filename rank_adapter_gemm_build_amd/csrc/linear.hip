@@ -90,12 +90,14 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
   }
 }
 
-// One wave per workgroup: decode units first, then (tile slot, row group, k part) units.
+// One wave per workgroup: matrix-core (tile slot, row group, k part) units, then decode units.
 template <typename T>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
                                                     int ldx, UView U, Plan plan, int n_units) {
-  const int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
+  int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
   if (b >= n_units) return;
+  // matrix-core units first: they carry the long segments, the longest chains
+  b = b < n_units - plan.n_dec_blocks ? b + plan.n_dec_blocks : b - (n_units - plan.n_dec_blocks);
   if (b < plan.n_dec_blocks) {
     shrink_decode_unit<T>(P, R, x, ldx, U, plan, b);
     return;
@@ -226,24 +228,25 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   expand_decode_tiles<TW, TY>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
 }
 
-// One wave per workgroup: decode items first, then (tile slot, column-block group) units.
+// One wave per workgroup: matrix-core (tile slot, column group) units, then decode items.
 template <typename TW, typename TY, int KSM>
 __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UView U,
                                                     TY* __restrict__ y, int ldy, Plan plan, int n_units) {
   extern __shared__ float smem[];
-  const int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
+  int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
   if (b >= n_units) return;
+  // matrix-core units first: they carry the long segments, the longest chains
+  b = b < n_units - plan.n_dec_blocks ? b + plan.n_dec_blocks : b - (n_units - plan.n_dec_blocks);
   if (b < plan.n_dec_blocks) {
     expand_decode_item<TW, TY>(P, R, U, y, ldy, plan, b, smem);
     return;
   }
   if constexpr (sizeof(TW) == 2) {
     const int m = b - plan.n_dec_blocks;
-    const int ng = (P.n_mblocks + kMfmaColBlocksPerUnit - 1) / kMfmaColBlocksPerUnit;
-    const int g = m % ng, ts = m / ng;
+    const int g = m % P.n_mgroups, ts = m / P.n_mgroups;
     const int ntiles = R.meta[kMetaTiles];
     for (int tile = ts; tile < ntiles; tile += plan.tile_slots)
-      expand_mfma_unit<TY, KSM>(P, R, U, y, ldy, tile, g * kMfmaColBlocksPerUnit, smem);
+      expand_mfma_unit<TY, KSM>(P, R, U, y, ldy, tile, g, smem);
   }
 }
 
@@ -273,8 +276,7 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
       plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
       (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1)))
     return hipErrorInvalidValue;
-  const int ng = (P.n_mblocks + kMfmaColBlocksPerUnit - 1) / kMfmaColBlocksPerUnit;
-  const int units = plan.n_dec_blocks + (plan.use_mfma ? ng * plan.tile_slots : 0);
+  const int units = plan.n_dec_blocks + (plan.use_mfma ? P.n_mgroups * plan.tile_slots : 0);
   const int q = kXcds * plan.xcd_group;
   const dim3 grid((units + q - 1) / q * q);
   const uint32_t lds = (uint32_t)expand_smem_bytes(wdtype, P.Rmax, plan.use_mfma);

@@ -24,15 +24,16 @@
 // together, double-buffered: the loads of group g + 1 are in flight while the
 // products of group g run.
 //
-// Expand unit (tile, group of kMfmaColBlocksPerUnit 128-column blocks):
-// D[token][col] = sum_j u[token][j] * B[col][j], from the pool's rank-contiguous copy
-// of B.  The wave first finishes its tokens' rank-space values (partials added in
-// split order) and keeps them as bf16 hi + lo parts (hi = bf16(u), lo = bf16(u - hi)),
-// two products per step, so u keeps about 16 mantissa bits instead of being rounded
-// to bf16; then, per column block, the B fragments and the tile's y chunks load in
-// one batch, and the 16 x 128 result goes through the wave's own LDS slice so that
-// the read-modify-write of y (the dominant traffic) moves 16 bytes per lane along
-// rows.
+// Expand unit (tile, group of up to kMfmaColBlocksPerUnit 128-column blocks of one
+// slice): D[token][col] = sum_j u[token][j] * B[col][j], from the pool's
+// rank-contiguous copy of B (stride: the slot's rank rounded up to 8, so a low-rank
+// slot of a mixed-rank pool reads no padding).  The wave finishes its tokens'
+// rank-space values (partials added in split order) and keeps them as bf16 hi + lo
+// parts (hi = bf16(u), lo = bf16(u - hi)), two products per step, so u keeps about 16
+// mantissa bits instead of being rounded to bf16.  Per column block the B fragments
+// and the tile's y chunks load in one batch, issued one block ahead of the products,
+// and the 16 x 128 result goes through the wave's own LDS slice so that the
+// read-modify-write of y (the dominant traffic) moves 16 bytes per lane along rows.
 #pragma once
 
 #include "device_util.h"
@@ -92,13 +93,11 @@ __device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<NB>& f, bool 
 // Products of rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1): lane
 // holds D[token 4 * lk + i][row fr0 + 16 b + lr] in acc[b][i].
 template <int NB>
-__device__ __forceinline__ void shrink_mfma_acc(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
-                                                int ldx, int slot, int r, int p0, int len, int fr0, int s0, int s1,
-                                                f32x4_t (&acc)[NB]) {
+__device__ __forceinline__ void shrink_mfma_acc(const PoolView& P, const uint16_t* __restrict__ xrow, int slot, int r,
+                                                int len, int fr0, int s0, int s1, f32x4_t (&acc)[NB]) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int F = P.N * r;
   const bool tval = lr < len;
-  const uint16_t* xrow = x + (size_t)R.sorted[p0 + min(lr, len - 1)] * ldx;
   const uint16_t* Aslot = static_cast<const uint16_t*>(P.A) + (size_t)slot * P.N * P.Rmax * P.k;
   const uint16_t* arow[NB];
   bool rval[NB];
@@ -137,13 +136,12 @@ __device__ __forceinline__ void mfma_part_range(int k, int part, int nsplit, int
 
 // Rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1); writes partial `part`.
 template <int NB>
-__device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
-                                                 int ldx, const UView& U, int slot, int r, int p0, int len, int fr0,
-                                                 int part, int s0, int s1) {
+__device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const uint16_t* __restrict__ xrow, const UView& U,
+                                                 int slot, int r, int p0, int len, int fr0, int part, int s0, int s1) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int F = P.N * r;
   f32x4_t acc[NB];
-  shrink_mfma_acc<NB>(P, R, x, ldx, slot, r, p0, len, fr0, s0, s1, acc);
+  shrink_mfma_acc<NB>(P, xrow, slot, r, len, fr0, s0, s1, acc);
   // lane holds D[token 4 * lk + i][row fr0 + 16 b + lr]; rows by sorted position
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -166,20 +164,22 @@ __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteV
                                                  int ldx, const UView& U, int tile, int rg, int part, int nsplit) {
   const int4 td = R.tiles[tile];
   const int slot = td.x, p0 = td.y, len = td.z;
+  // the slot-table entry and this lane's token id (token lane % 16) in one round trip
   const SlotEntry e = P.table[slot];
+  const uint16_t* __restrict__ xrow = x + (size_t)R.sorted[p0 + min(lane_id() & 15, len - 1)] * ldx;
   const int r = e.rank, F = P.N * r, fr0 = 64 * rg;
   if (r == 0 || fr0 >= F) return;
   int s0, s1;
   mfma_part_range(P.k, part, nsplit, s0, s1);
   const int nb = min(4, (F - fr0 + 15) / 16);
   if (nb == 4)
-    shrink_mfma_rows<4>(P, R, x, ldx, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<4>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else if (nb == 3)
-    shrink_mfma_rows<3>(P, R, x, ldx, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<3>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else if (nb == 2)
-    shrink_mfma_rows<2>(P, R, x, ldx, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<2>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else
-    shrink_mfma_rows<1>(P, R, x, ldx, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<1>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
 }
 
 // ------------------------------------------------------------------ expand
@@ -196,178 +196,301 @@ __device__ __forceinline__ void u_hilo(const float (&v)[8], uint4& uh, uint4& ul
   ul = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
-// This lane's rank-space values of slice n for the u fragment rows of the tile
-// (token lr, ranks 32 ks + 8 lk .. +7), finished from their split partials in split
-// order, as bf16 hi + lo parts.  Zero past the rank and past the tile's length.
-template <int KSM>
-__device__ __forceinline__ void expand_u_frags(const RouteView& R, const UView& U, int n, int p0, int len, int r,
-                                               int nks, uint4 (&uh)[KSM], uint4 (&ul)[KSM]) {
-  const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
-  const int t = min(lr, len - 1);
+constexpr int kUSplitBatch = 8;   // split partials of one u fragment loaded in one batch
+
+// This lane's u fragment of rank step ks (token lr, ranks 32 ks + 8 lk .. +7), from
+// the split partials of the workspace, NSB batches of kUSplitBatch splits (NSB *
+// kUSplitBatch >= nsplit): load() issues the first batch, finish() issues any
+// further one and adds all of them in split order.  Branch-free: a lane whose ranks
+// lie past the rank, or whose token lies past the tile, reads a clamped address of
+// the same row (a duplicate the memory pipeline merges); splits past nsplit re-read
+// the last one and are added as -0.0f, the exact identity of IEEE addition; values
+// of ranks past the rank and of tokens past the tile are zeroed at the end.
+template <int NSB>
+struct UPartials {
+  float4 pa[kUSplitBatch], pb[kUSplitBatch];
+  const float* base;
+  __device__ __forceinline__ void load_batch(const UView& U, int q0) {
 #pragma unroll
-  for (int ks = 0; ks < KSM; ++ks) {
-    float v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = 0.f;
-    if (ks < nks) {
-      const int j0 = ks * kMfmaK + 8 * lk;
-      if (!U.by_token) {
-        // workspace rows are padded to a multiple of 32 floats: two 16-byte loads per split
-        const float* base = U.p + n * U.n_stride + (long long)(p0 + t) * U.row_stride + j0;
-        for (int s0 = 0; s0 < U.nsplit; s0 += 4) {
-          float4 pa[4], pb[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int sq = min(s0 + q, U.nsplit - 1);
-            pa[q] = *reinterpret_cast<const float4*>(base + sq * U.split_stride);
-            pb[q] = *reinterpret_cast<const float4*>(base + sq * U.split_stride + 4);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (s0 + q < U.nsplit) {
-              if (s0 + q == 0) {
-                v[0] = pa[q].x; v[1] = pa[q].y; v[2] = pa[q].z; v[3] = pa[q].w;
-                v[4] = pb[q].x; v[5] = pb[q].y; v[6] = pb[q].z; v[7] = pb[q].w;
-              } else {
-                v[0] += pa[q].x; v[1] += pa[q].y; v[2] += pa[q].z; v[3] += pa[q].w;
-                v[4] += pb[q].x; v[5] += pb[q].y; v[6] += pb[q].z; v[7] += pb[q].w;
-              }
-            }
-          }
-        }
-      } else {
-        // the caller's finished u, rows by token, row stride Rmax
-        const float* base = U.p + n * U.n_stride + (long long)R.sorted[p0 + t] * U.row_stride;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int j = j0 + q;
-          v[q] = base[j < r ? j : 0];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = (lr < len && j0 + q < r) ? v[q] : 0.f;
+    for (int q = 0; q < kUSplitBatch; ++q) {
+      const long long off = (long long)min(q0 + q, U.nsplit - 1) * U.split_stride;
+      pa[q] = *reinterpret_cast<const float4*>(base + off);
+      pb[q] = *reinterpret_cast<const float4*>(base + off + 4);
     }
-    u_hilo(v, uh[ks], ul[ks]);
   }
+  __device__ __forceinline__ void load(const UView& U, int n, int p0, int len, int r, int ks) {
+    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    const int j0 = ks * kMfmaK + 8 * lk;
+    // j0 < r: j0 + 8 <= r rounded up to 8 <= row_stride, so the 8 floats stay in the row
+    base = U.p + n * U.n_stride + (long long)(p0 + min(lr, len - 1)) * U.row_stride + (j0 < r ? j0 : 0);
+    load_batch(U, 0);
+  }
+  __device__ __forceinline__ void add_batch(const UView& U, int q0, float (&v)[8]) const {
+#pragma unroll
+    for (int q = 0; q < kUSplitBatch; ++q) {
+      if (q0 + q == 0) {
+        v[0] = pa[0].x; v[1] = pa[0].y; v[2] = pa[0].z; v[3] = pa[0].w;
+        v[4] = pb[0].x; v[5] = pb[0].y; v[6] = pb[0].z; v[7] = pb[0].w;
+      } else {
+        const bool in = q0 + q < U.nsplit;
+        v[0] += in ? pa[q].x : -0.f; v[1] += in ? pa[q].y : -0.f; v[2] += in ? pa[q].z : -0.f;
+        v[3] += in ? pa[q].w : -0.f; v[4] += in ? pb[q].x : -0.f; v[5] += in ? pb[q].y : -0.f;
+        v[6] += in ? pb[q].z : -0.f; v[7] += in ? pb[q].w : -0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void finish(const UView& U, int len, int r, int ks, uint4& uh, uint4& ul) {
+    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    float v[8];
+    add_batch(U, 0, v);
+#pragma unroll
+    for (int b = 1; b < NSB; ++b) {
+      sched_fence();   // one batch of partials in registers at a time
+      load_batch(U, b * kUSplitBatch);
+      add_batch(U, b * kUSplitBatch, v);
+    }
+    const int j0 = ks * kMfmaK + 8 * lk;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (lr < len && j0 + q < r) ? v[q] : 0.f;
+    u_hilo(v, uh, ul);
+  }
+};
+
+// The same fragment from the caller's finished u (rows by token, row stride Rmax),
+// branch-free like UPartials (rank clamped into the row, zeroed after).
+__device__ __forceinline__ void u_frag_by_token(const RouteView& R, const UView& U, int n, int p0, int len, int r,
+                                                int ks, uint4& uh, uint4& ul) {
+  const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+  const int j0 = ks * kMfmaK + 8 * lk;
+  const float* base = U.p + n * U.n_stride + (long long)R.sorted[p0 + min(lr, len - 1)] * U.row_stride;
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = base[min(j0 + q, r - 1)];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = (lr < len && j0 + q < r) ? v[q] : 0.f;
+  u_hilo(v, uh, ul);
 }
 
-// One 128-column block (columns c0 .. c0 + 127 of slice n) of one tile.
-template <typename TY, int KSM>
-__device__ __forceinline__ void expand_mfma_block(const PoolView& P, const RouteView& R, TY* __restrict__ y, int ldy,
-                                                  int slot, float scale, int n, int c0, int p0, int len, int nks,
-                                                  const uint4 (&uh)[KSM], const uint4 (&ul)[KSM],
-                                                  float* __restrict__ ds) {
-  constexpr int YC = 16 / sizeof(TY);             // y elements per 16-byte chunk
-  constexpr int YCHUNKS = kMfmaTileM * kMfmaCols / YC / 64;  // y chunks per lane
-  constexpr int KP = 1;                           // rank steps per batch of B fragments
-  const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
-  const int dn = P.d[n];
-  const uint16_t* __restrict__ bk = static_cast<const uint16_t*>(P.Bk) + ((size_t)slot * P.D + P.o[n]) * P.Rk;
-  uint4 yv[YCHUNKS];
-  TY* yp[YCHUNKS];
-  bool yok[YCHUNKS];
-#pragma unroll
-  for (int q = 0; q < YCHUNKS; ++q) {
-    const int idx = q * 64 + lane;
-    const int t = idx / (kMfmaCols / YC), cc = (idx % (kMfmaCols / YC)) * YC;
-    yok[q] = t < len && c0 + cc < dn;
-    yp[q] = y + (size_t)R.sorted[p0 + min(t, len - 1)] * ldy + P.o[n] + min(c0 + cc, dn - YC);
-    yv[q] = ld16(yp[q]);
+// Column groups of the matrix-core expand: each slice's 128-column blocks in groups
+// of kMfmaColBlocksPerUnit; a group never spans two slices.  Returns the slice (or -1
+// past the last group) and the group's first block within the slice.
+__device__ __forceinline__ int mfma_group_slice(const PoolView& P, int grp, int& blk0) {
+  int g0 = 0;
+  for (int n = 0; n < P.N; ++n) {
+    const int nbn = P.mblk0[n + 1] - P.mblk0[n];
+    const int gn = (nbn + kMfmaColBlocksPerUnit - 1) / kMfmaColBlocksPerUnit;
+    if (grp < g0 + gn) {
+      blk0 = (grp - g0) * kMfmaColBlocksPerUnit;
+      return n;
+    }
+    g0 += gn;
   }
-  f32x4_t acc[8];
+  return -1;
+}
+
+// Per-lane y rows of a matrix-core expand tile: chunk q of a lane belongs to token
+// (64 q + lane) / RC of the tile (clamped to the tile), whose row of y starts at
+// row[q] (slice offset included).  Loaded once per unit.
+template <typename TY>
+struct ExpandRows16 {
+  static constexpr int YC = 16 / (int)sizeof(TY);                // y elements per 16-byte chunk
+  static constexpr int RC = kMfmaCols / YC;                      // chunks per token row of a block
+  static constexpr int YCH = kMfmaTileM * RC / 64;               // y chunks per lane
+  TY* row[YCH];
+  __device__ __forceinline__ void load(const RouteView& R, TY* __restrict__ y, int ldy, int on, int p0, int len) {
+    const int lane = lane_id();
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < YCH; ++q) {
+      const int t = (q * 64 + lane) / RC;
+      row[q] = y + (size_t)R.sorted[p0 + min(t, len - 1)] * ldy + on;
+    }
+  }
+};
+
+// Loads of one 128-column block of one tile, all unconditional: the tile's y chunks
+// (a lane past the tile re-reads its clamped token's chunk, never stored; columns
+// past the slice re-read its last chunk, never stored) and the B fragments of the
+// NKS rank steps (a lane whose ranks lie past the slot's Bk stride reads the rank-0
+// fragment of its column and zeroes it; columns past the slice read column 0, never
+// stored).
+template <typename TY, int NKS>
+struct ExpandMfmaBlock {
+  using Rows = ExpandRows16<TY>;
+  static constexpr int YC = Rows::YC, RC = Rows::RC, YCH = Rows::YCH;
+  uint4 yv[YCH];
+  uint4 bv[NKS][8];
+  int c0;
+
+  __device__ __forceinline__ void issue(const Rows& Y, const uint16_t* __restrict__ bk, int rs, int dn, int c0_,
+                                        int nks) {
+    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    c0 = c0_;
 #pragma unroll
-  for (int ks0 = 0; ks0 < KSM; ks0 += KP) {
-    if (ks0 < nks) {
-      uint4 bv[KP][8];
+    for (int q = 0; q < YCH; ++q) {
+      const int cc = ((q * 64 + lane) % RC) * YC;
+      yv[q] = ld16(Y.row[q] + min(c0 + cc, dn - YC));
+    }
 #pragma unroll
-      for (int kk = 0; kk < KP; ++kk) {
-        const int ks = ks0 + kk;
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks < nks) {   // compile-time true unless NKS covers a range of rank-step counts
+        const int j0 = ks * kMfmaK + 8 * lk, jc = j0 < rs ? j0 : 0;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
           const int col = c0 + 16 * cb + lr;
-          // (ks < nks) 32 ks + 8 lk + 8 <= 32 nks <= Rk: the load stays in the row
-          bv[kk][cb] = ld16(bk + (size_t)(col < dn ? col : 0) * P.Rk + (ks < nks ? ks : 0) * kMfmaK + 8 * lk);
-        }
-      }
-      sched_fence();
-#pragma unroll
-      for (int kk = 0; kk < KP; ++kk) {
-        const int ks = ks0 + kk;
-        if (ks < nks) {
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
-            const uint4 b = keep_if(bv[kk][cb], c0 + 16 * cb + lr < dn);
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uh[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ul[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
-          }
+          bv[ks][cb] = ld16(bk + (size_t)(col < dn ? col : 0) * rs + jc);
         }
       }
     }
   }
-  // result through LDS: lane holds D[token 4 lk + i][column 16 cb + lr]
+
+  // D[token][col] = sum_j u[token][j] B[col][j] for the block, then y += scale * D
+  // for the tile's tokens, through the wave's LDS slice ds (16 rows of kDsPitch).
+  __device__ __forceinline__ void finish(const Rows& Y, int rs, int dn, int len, int nks, float scale,
+                                         const uint4 (&uh)[NKS], const uint4 (&ul)[NKS], float* __restrict__ ds) const {
+    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    f32x4_t acc[8];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb)
+    for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ds[(4 * lk + i) * kDsPitch + 16 * cb + lr] = acc[cb][i];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks < nks) {
+        const bool kin = ks * kMfmaK + 8 * lk < rs;
 #pragma unroll
-  for (int q = 0; q < YCHUNKS; ++q) {
-    if (yok[q]) {
+        for (int cb = 0; cb < 8; ++cb) {
+          const uint4 b = keep_if(bv[ks][cb], kin);
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uh[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ul[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
+        }
+      }
+    }
+    // lane holds D[token 4 lk + i][column 16 cb + lr]
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds[(4 * lk + i) * kDsPitch + 16 * cb + lr] = acc[cb][i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < YCH; ++q) {
       const int idx = q * 64 + lane;
-      const int t = idx / (kMfmaCols / YC), cc = (idx % (kMfmaCols / YC)) * YC;
-      const float* dp = ds + t * kDsPitch + cc;
-      if constexpr (sizeof(TY) == 2) {
-        float v[8];
-        unpack8(yv[q], v);
+      const int t = idx / RC, cc = (idx % RC) * YC;
+      if (t < len && c0 + cc < dn) {
+        TY* const yp = Y.row[q] + c0 + cc;
+        const float* dp = ds + t * kDsPitch + cc;
+        if constexpr (sizeof(TY) == 2) {
+          float v[8];
+          unpack8(yv[q], v);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = v[c] + scale * dp[c];
-        store8f(yp[q], v);
-      } else {
-        uint4 o;
-        o.x = __float_as_uint(__uint_as_float(yv[q].x) + scale * dp[0]);
-        o.y = __float_as_uint(__uint_as_float(yv[q].y) + scale * dp[1]);
-        o.z = __float_as_uint(__uint_as_float(yv[q].z) + scale * dp[2]);
-        o.w = __float_as_uint(__uint_as_float(yv[q].w) + scale * dp[3]);
-        st16(yp[q], o);
+          for (int c = 0; c < 8; ++c) v[c] = v[c] + scale * dp[c];
+          store8f(yp, v);
+        } else {
+          uint4 o;
+          o.x = __float_as_uint(__uint_as_float(yv[q].x) + scale * dp[0]);
+          o.y = __float_as_uint(__uint_as_float(yv[q].y) + scale * dp[1]);
+          o.z = __float_as_uint(__uint_as_float(yv[q].z) + scale * dp[2]);
+          o.w = __float_as_uint(__uint_as_float(yv[q].w) + scale * dp[3]);
+          st16(yp, o);
+        }
       }
     }
+    // the LDS slice is rewritten by the next block
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // the LDS slice is rewritten by the next block
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+};
+
+// Body of one expand unit with NKS rank steps of 32 (nks <= NKS of them real), NSB
+// split batches of the workspace partials (0: the caller's finished u by token).
+// Order of the memory traffic: the u loads, then the first block's y chunks and B
+// fragments, all in flight together; then, while a block's products run, the next
+// block's loads are in flight (two blocks' loads held when they fit in 12 chunks per
+// lane, else one block at a time).  Every group has kMfmaColBlocksPerUnit blocks: a
+// block past the slice's end loads clamped addresses and stores nothing.  There are
+// no branches between a load and its use, so the compiler keeps the batches as
+// written.
+template <typename TY, int NKS, int NSB>
+__device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, const ExpandRows16<TY>& Y,
+                                                 const uint16_t* __restrict__ bk, int rs, int n, int dn,
+                                                 int c00, int p0, int len, int r, int nks, float scale,
+                                                 float* __restrict__ ds) {
+  using Blk = ExpandMfmaBlock<TY, NKS>;
+  constexpr bool kPipe = Blk::YCH + 8 * NKS <= 12;
+  uint4 uh[NKS], ul[NKS];
+  Blk b0, b1;
+  if constexpr (NSB > 0) {
+    UPartials<NSB> up;
+    up.load(U, n, p0, len, r, 0);
+    b0.issue(Y, bk, rs, dn, c00, nks);
+    sched_fence();
+    up.finish(U, len, r, 0, uh[0], ul[0]);
+#pragma unroll
+    for (int ks = 1; ks < NKS; ++ks) {
+      UPartials<NSB> uq;
+      uq.load(U, n, p0, len, r, ks);
+      uq.finish(U, len, r, ks, uh[ks], ul[ks]);
+    }
+  } else {
+    b0.issue(Y, bk, rs, dn, c00, nks);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) u_frag_by_token(R, U, n, p0, len, r, ks, uh[ks], ul[ks]);
+  }
+  if constexpr (kPipe) {
+#pragma unroll
+    for (int i = 0; i < kMfmaColBlocksPerUnit; i += 2) {
+      b1.issue(Y, bk, rs, dn, c00 + (i + 1) * kMfmaCols, nks);
+      sched_fence();
+      b0.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
+      if (i + 2 < kMfmaColBlocksPerUnit) b0.issue(Y, bk, rs, dn, c00 + (i + 2) * kMfmaCols, nks);
+      sched_fence();
+      b1.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMfmaColBlocksPerUnit; ++i) {
+      if (i > 0) b0.issue(Y, bk, rs, dn, c00 + i * kMfmaCols, nks);
+      sched_fence();
+      b0.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
+    }
+  }
 }
 
-// One expand unit: tile `tile`, global 128-column blocks mb0 .. mb0 + G - 1.  KSM is
-// the number of rank steps of 32 the pool's padded rank has at most (1, 2, 4 or 8).
-// Wave-uniform; ds is the wave's kExpandMfmaWaveFloats floats of LDS.
+// One expand unit: tile `tile`, column group grp (kMfmaColBlocksPerUnit blocks of
+// one slice).  KSM is the number of rank steps of 32 the pool's padded rank has at
+// most (1, 2, 4 or 8); the body is specialised for the tile's own step count (1 or
+// 2; for KSM >= 4 one body with run-time bounds) and split batches.  Wave-uniform; ds is the wave's
+// kExpandMfmaWaveFloats floats of LDS.
 template <typename TY, int KSM>
 __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
-                                                 TY* __restrict__ y, int ldy, int tile, int mb0,
+                                                 TY* __restrict__ y, int ldy, int tile, int grp,
                                                  float* __restrict__ ds) {
+  int blk0;
+  const int n = mfma_group_slice(P, grp, blk0);
+  if (n < 0) return;
+  const int on = P.o[n], dn = P.d[n], c00 = blk0 * kMfmaCols;
   const int4 td = R.tiles[tile];
   const int slot = td.x, p0 = td.y, len = td.z;
+  // the slot-table entry and the tile's token ids in one round trip
   const SlotEntry e = P.table[slot];
-  if (e.rank == 0 || e.scale == 0.f) return;
-  const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK;
-  const int mb1 = min(P.n_mblocks, mb0 + kMfmaColBlocksPerUnit);
-  int cur_n = -1;
-  uint4 uh[KSM], ul[KSM];
-  for (int mb = mb0; mb < mb1; ++mb) {
-    int n = 0;
-    while (n + 1 < P.N && mb >= P.mblk0[n + 1]) ++n;
-    if (!((e.slice_mask >> n) & 1u)) continue;
-    if (n != cur_n) {
-      expand_u_frags<KSM>(R, U, n, p0, len, r, nks, uh, ul);
-      cur_n = n;
-    }
-    expand_mfma_block<TY, KSM>(P, R, y, ldy, slot, e.scale, n, (mb - P.mblk0[n]) * kMfmaCols, p0, len, nks, uh, ul,
-                               ds);
+  ExpandRows16<TY> Y;
+  Y.load(R, y, ldy, on, p0, len);
+  if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
+  const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
+  const uint16_t* __restrict__ bk = static_cast<const uint16_t*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
+  const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
+#define RAX_EXPAND_BODY(NK, NB) \
+  expand_mfma_body<TY, NK, NB>(R, U, Y, bk, rs, n, dn, c00, p0, len, r, nks, e.scale, ds)
+#define RAX_EXPAND_BODIES(NK) \
+  do { if (nsb == 1) RAX_EXPAND_BODY(NK, 1); else if (nsb == 2) RAX_EXPAND_BODY(NK, 2); else RAX_EXPAND_BODY(NK, 0); } while (0)
+  if constexpr (KSM <= 2) {
+    if (nks == 1) RAX_EXPAND_BODIES(1);
+    else if constexpr (KSM == 2) RAX_EXPAND_BODIES(2);
+  } else {
+    RAX_EXPAND_BODIES(KSM);
   }
+#undef RAX_EXPAND_BODIES
+#undef RAX_EXPAND_BODY
 }
 
 }  // namespace rax

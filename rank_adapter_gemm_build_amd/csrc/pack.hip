@@ -26,22 +26,23 @@ __global__ void pack_a_kernel(const T* __restrict__ src, T* __restrict__ dst, lo
     dst[e] = (src != nullptr && e < n_src) ? src[e] : T(0);
 }
 
-// B slice [d][rank] -> Bt rows [Rmax][D] (columns [0, d) of the slice) and
-// Bk [d][Rk]; entries j >= rank are zero.  Optional fold of the scale: one fp32
-// product rounded once to T.
+// B slice [d][rank] -> Bt rows [Rmax][D] (columns [0, d) of the slice) and Bk
+// [d][rs] (rs = rank rounded up to 8); entries j >= rank are zero.  Optional fold of
+// the scale: one fp32 product rounded once to T.
 template <typename T>
 __global__ void pack_b_kernel(const T* __restrict__ src, T* __restrict__ bt, T* __restrict__ bk,
-                              int rank, int Rmax, int Rk, int d, int D, float scale, int premultiply) {
+                              int rank, int Rmax, int rs, int d, int D, float scale, int premultiply) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d) return;
-  for (int j = 0; j < Rk; ++j) {
+  const int jn = Rmax > rs ? Rmax : rs;
+  for (int j = 0; j < jn; ++j) {
     T v = T(0);
     if (src != nullptr && j < rank) {
       v = src[(long long)i * rank + j];
       if (premultiply) from_f(scale * to_f(v), v);
     }
     if (j < Rmax) bt[(long long)j * D + i] = v;
-    bk[(long long)i * Rk + j] = v;
+    if (j < rs) bk[(long long)i * rs + j] = v;
   }
 }
 
@@ -59,7 +60,7 @@ static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* 
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_b_kernel<T>, dim3((d + 255) / 256), dim3(256), 0, stream,
                      static_cast<const T*>(B_src), static_cast<T*>(Bt_dst), static_cast<T*>(Bk_dst),
-                     rank, Rmax, Rk, d, D, scale, premultiply);
+                     rank, Rmax, bk_stride(rank), d, D, scale, premultiply);
   return hipGetLastError();
 }
 

@@ -433,6 +433,32 @@ def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
         _log(f"  {mode}: normwise rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("mode", ["default", "all-mfma", "mfma16", "vector"])
+def test_short_segments_every_path(rx, mode):
+    """Segments of 1..17 tokens through each split between the vector and matrix-core
+    units: the default threshold, every segment on the matrix cores (1-token tiles),
+    a threshold of 16, and the vector units only."""
+    import os
+    segments = [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17]
+    slices = [1024, 256, 256]
+    W = small_case(520, T=0, S=14, k=1536, slices=slices, Rmax=48, segments=segments)
+    mod = W.modules[0]
+    _log(f"mode {mode} segments {segments} T={W.T}")
+    ads = oracle_adapters(W, mod)
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
+                       max_rank=W.Rmax)
+    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}, "mfma16": {"RAXLORA_MFMA_MIN_SEG": "16"},
+           "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
+    os.environ.update(env)
+    try:
+        y = _run_linear(rx, W, mod, np.zeros((W.T, sum(slices)), dtype=np.float32), "f32")
+    finally:
+        for key in env:
+            os.environ.pop(key, None)
+    err = check_close(from_device(y), ref, "bf16", f"delta ({mode})")
+    _log(f"  normwise rel err {err:.2e}")
+
+
 def test_shrink_matrix_cores_match_oracle(rx):
     """u from the matrix-core shrink of long segments (standalone lora_shrink)."""
     import torch
