@@ -150,9 +150,6 @@ rax::PoolView pool_view(const lora_pool* p) {
   v.D = p->D;
   v.n_ctiles = p->tile0[p->N];
   v.n_mblocks = p->mblk0[p->N];
-  v.n_mgroups = 0;
-  for (int n = 0; n < p->N; ++n)
-    v.n_mgroups += (p->mblk0[n + 1] - p->mblk0[n] + rax::kMfmaColBlocksPerUnit - 1) / rax::kMfmaColBlocksPerUnit;
   for (int n = 0; n < rax::kMaxSlices; ++n) {
     v.d[n] = n < p->N ? p->d[n] : 0;
     v.o[n] = n < p->N ? p->o[n] : 0;
@@ -265,6 +262,17 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   pl.n_dec_blocks = expand ? pool->tile0[pool->N] * pool->S * pl.ntg : pool->S * pl.nrb * pl.nsplit * pl.ntg;
   // tiles <= T / tile_m + (segments of at least mfma_min tokens), rounded up
   pl.tile_slots = std::max(1, std::min(r->max_tiles, ceil_div(r->T, r->tile_m) + std::min(r->S, ceil_div(r->T, r->mfma_min))));
+  // matrix-core expand units: kMfmaColBlocksPerUnit column blocks each (the u values
+  // are finished once per unit), or one block each when that still leaves few units
+  // (a short chain per unit matters more then)
+  auto groups = [&](int cb) {
+    int g = 0;
+    for (int n = 0; n < pool->N; ++n) g += ceil_div(pool->mblk0[n + 1] - pool->mblk0[n], cb);
+    return g;
+  };
+  const int g4 = groups(rax::kMfmaColBlocksPerUnit);
+  pl.cb = (long long)g4 * pl.tile_slots <= env_int("RAXLORA_CB1_MAX", 512) ? 1 : rax::kMfmaColBlocksPerUnit;
+  pl.n_mgroups = pl.cb == 1 ? groups(1) : g4;
   return pl;
 }
 

@@ -32,7 +32,7 @@ constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
 constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block
 // elements per column of a slot's Bk region: its rank rounded up to 8
 __host__ __device__ constexpr int bk_stride(int rank) { return (rank + 7) / 8 * 8; }
-constexpr int kMfmaColBlocksPerUnit = 4;   // 128-column blocks of one matrix-core expand unit
+constexpr int kMfmaColBlocksPerUnit = 4;   // most 128-column blocks of one matrix-core expand unit   // 128-column blocks of one matrix-core expand unit
 constexpr int kDefaultMfmaMinSeg = 4;   // segments at least this long use matrix cores (bf16 pools)
 constexpr int kRecInts = 32;       // ints of one slot record: tokens, first position, 2 spare, token ids
 constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
@@ -54,7 +54,7 @@ struct PoolView {
   const void* Bt;
   const void* Bk;
   const SlotEntry* table;
-  int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks, n_mgroups;
+  int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks;
   int d[kMaxSlices];
   int o[kMaxSlices];
   int tile0[kMaxSlices + 1];  // first expand column tile of each slice; tile0[N] = n_ctiles
@@ -99,6 +99,8 @@ struct Plan {
   int nrb, ntg;            // decode: 16-row blocks, token-tile groups
   int n_dec_blocks;        // workgroups of the decode part
   int tile_slots;          // matrix-core part: tiles handled in parallel
+  int cb;                  // matrix-core expand: 128-column blocks per unit (1 or kMfmaColBlocksPerUnit)
+  int n_mgroups;           // matrix-core expand: column groups of cb blocks (per slice, summed)
   int use_mfma;            // long segments go to the matrix-core part
   int xcd_group;           // consecutive units dealt to one XCD (1 = plain round-robin)
 };

@@ -54,8 +54,6 @@ template <typename T>
 __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const RouteView& R,
                                                    const T* __restrict__ x, int ldx, const UView& U,
                                                    const Plan& plan, int unit) {
-  constexpr int E = Elem<T>::kPerChunk;
-  constexpr int CW = 64 * E;         // k elements of one wave-wide chunk step
   const int tg = unit % plan.ntg;
   int rest = unit / plan.ntg;
   const int sp = rest % plan.nsplit;
@@ -90,36 +88,57 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
   }
 }
 
-// One wave per workgroup: matrix-core (tile slot, row group, k part) units, then decode units.
+// Matrix-core work items of one launch, split over the XCDs: workgroup b runs on XCD
+// b % 8, and XCD x takes the x-th contiguous eighth of the items (tiles in slot
+// order within).  Consecutive tiles of a segment share their slot's weights, and the
+// items of one tile share its tokens' data, so each XCD's L2 serves its own stretch
+// of the batch and weights and partial sums are fetched from HBM about once.
+// Worker i of an XCD takes items start + i, start + i + upx, ... (upx workers per
+// XCD; the launch provides at least one worker per item).
+struct MfmaItems {
+  int j, end, step;
+  __device__ __forceinline__ MfmaItems(int b, int n_blocks, int n_items) {
+    const int x = b % kXcds, upx = n_blocks / kXcds;
+    const int per = (n_items + kXcds - 1) / kXcds;
+    j = min(n_items, x * per) + b / kXcds;
+    end = min(n_items, (x + 1) * per);
+    step = upx;
+  }
+};
+
+// Workgroups of a launch: first the matrix-core workers (a multiple of 8, so the XCD
+// of a worker is its index mod 8), then the decode units.
+__host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + kXcds - 1) / kXcds * kXcds; }
+
+// One wave per workgroup: matrix-core (k part, tile, row group) items, then decode units.
 template <typename T>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
-                                                    int ldx, UView U, Plan plan, int n_units) {
-  int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
-  if (b >= n_units) return;
-  // matrix-core units first: they carry the long segments, the longest chains
-  b = b < n_units - plan.n_dec_blocks ? b + plan.n_dec_blocks : b - (n_units - plan.n_dec_blocks);
-  if (b < plan.n_dec_blocks) {
-    shrink_decode_unit<T>(P, R, x, ldx, U, plan, b);
+                                                    int ldx, UView U, Plan plan, int n_mfma_blocks) {
+  const int b = blockIdx.x;
+  if (b >= n_mfma_blocks) {
+    const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
+    if (d < plan.n_dec_blocks) shrink_decode_unit<T>(P, R, x, ldx, U, plan, d);
     return;
   }
   if constexpr (sizeof(T) == 2) {
-    int m = b - plan.n_dec_blocks;
-    const int part = m % plan.nsplit;
-    m /= plan.nsplit;
-    const int rg = m % plan.nrg, ts = m / plan.nrg;
-    const int ntiles = R.meta[kMetaTiles];
-    for (int tile = ts; tile < ntiles; tile += plan.tile_slots)
+    // items part-major: an XCD's stretch covers whole k parts (with 8 parts, one
+    // each), so the rows of A and the k-slices of x it reads are its own
+    const int ntiles = R.meta[kMetaTiles], per_part = ntiles * plan.nrg;
+    for (MfmaItems it(b, n_mfma_blocks, per_part * plan.nsplit); it.j < it.end; it.j += it.step) {
+      const int part = it.j / per_part, rem = it.j - part * per_part;
+      const int tile = rem / plan.nrg, rg = rem - tile * plan.nrg;
       shrink_mfma_unit(P, R, x, ldx, U, tile, rg, part, plan.nsplit);
+    }
   }
 }
 
 template <typename T>
 static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, int ldx, const UView& U,
                             const Plan& plan, hipStream_t stream, const KTimer& tm) {
-  const int units = plan.n_dec_blocks + (plan.use_mfma ? plan.tile_slots * plan.nrg * plan.nsplit : 0);
+  const int nm = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
   const int q = kXcds * plan.xcd_group;
-  const int blocks = (units + q - 1) / q * q;
-  RAX_LAUNCH(tm, shrink_kernel<T>, dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, units);
+  const int blocks = nm + (plan.n_dec_blocks + q - 1) / q * q;
+  RAX_LAUNCH(tm, shrink_kernel<T>, dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm);
 }
 
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
@@ -228,37 +247,34 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   expand_decode_tiles<TW, TY>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
 }
 
-// One wave per workgroup: matrix-core (tile slot, column group) units, then decode items.
+// One wave per workgroup: matrix-core (tile, column group) items, then decode items.
 template <typename TW, typename TY, int KSM>
 __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UView U,
-                                                    TY* __restrict__ y, int ldy, Plan plan, int n_units) {
+                                                    TY* __restrict__ y, int ldy, Plan plan, int n_mfma_blocks) {
   extern __shared__ float smem[];
-  int b = xcd_logical_block(blockIdx.x, plan.xcd_group);
-  if (b >= n_units) return;
-  // matrix-core units first: they carry the long segments, the longest chains
-  b = b < n_units - plan.n_dec_blocks ? b + plan.n_dec_blocks : b - (n_units - plan.n_dec_blocks);
-  if (b < plan.n_dec_blocks) {
-    expand_decode_item<TW, TY>(P, R, U, y, ldy, plan, b, smem);
+  const int b = blockIdx.x;
+  if (b >= n_mfma_blocks) {
+    const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
+    if (d < plan.n_dec_blocks) expand_decode_item<TW, TY>(P, R, U, y, ldy, plan, d, smem);
     return;
   }
   if constexpr (sizeof(TW) == 2) {
-    const int m = b - plan.n_dec_blocks;
-    const int g = m % P.n_mgroups, ts = m / P.n_mgroups;
-    const int ntiles = R.meta[kMetaTiles];
-    for (int tile = ts; tile < ntiles; tile += plan.tile_slots)
-      expand_mfma_unit<TY, KSM>(P, R, U, y, ldy, tile, g, smem);
+    for (MfmaItems it(b, n_mfma_blocks, R.meta[kMetaTiles] * plan.n_mgroups); it.j < it.end; it.j += it.step) {
+      const int tile = it.j / plan.n_mgroups, g = it.j - tile * plan.n_mgroups;
+      expand_mfma_unit<TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, smem);
+    }
   }
 }
 
 template <typename TY>
 static void launch_expand_bf16(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
-                               const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int units,
+                               const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int nm,
                                const KTimer& tm) {
   switch (ksm) {
-    case 1: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
-    case 2: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
-    case 4: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
-    default: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, units); break;
+    case 1: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    case 2: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    case 4: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    default: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
   }
 }
 
@@ -274,22 +290,23 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
   if (plan.xcd_group < 1 || plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
       (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
       plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
-      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1)))
+      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.n_mgroups < 1 ||
+                         (plan.cb != 1 && plan.cb != kMfmaColBlocksPerUnit))))
     return hipErrorInvalidValue;
-  const int units = plan.n_dec_blocks + (plan.use_mfma ? P.n_mgroups * plan.tile_slots : 0);
+  const int nm = plan.use_mfma ? mfma_blocks(plan.n_mgroups * plan.tile_slots) : 0;
   const int q = kXcds * plan.xcd_group;
-  const dim3 grid((units + q - 1) / q * q);
+  const dim3 grid(nm + (plan.n_dec_blocks + q - 1) / q * q);
   const uint32_t lds = (uint32_t)expand_smem_bytes(wdtype, P.Rmax, plan.use_mfma);
   if (wdtype == LORA_BF16) {
     // rank steps of 32 the matrix-core part keeps in registers: Rk / 32 rounded up to a power of 2
     const int ksm = P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8;
     if (ydtype == LORA_BF16)
-      launch_expand_bf16<uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, units, tm);
+      launch_expand_bf16<uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
     else
-      launch_expand_bf16<float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, units, tm);
+      launch_expand_bf16<float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
   } else {
     RAX_LAUNCH(tm, (expand_kernel<float, float, 1>), grid, dim3(64), lds, stream, P, R, U,
-               static_cast<float*>(y), ldy, plan, units);
+               static_cast<float*>(y), ldy, plan, nm);
   }
   return hipGetLastError();
 }

@@ -272,15 +272,15 @@ __device__ __forceinline__ void u_frag_by_token(const RouteView& R, const UView&
 }
 
 // Column groups of the matrix-core expand: each slice's 128-column blocks in groups
-// of kMfmaColBlocksPerUnit; a group never spans two slices.  Returns the slice (or -1
-// past the last group) and the group's first block within the slice.
-__device__ __forceinline__ int mfma_group_slice(const PoolView& P, int grp, int& blk0) {
+// of cb; a group never spans two slices.  Returns the slice (or -1 past the last
+// group) and the group's first block within the slice.
+__device__ __forceinline__ int mfma_group_slice(const PoolView& P, int grp, int cb, int& blk0) {
   int g0 = 0;
   for (int n = 0; n < P.N; ++n) {
     const int nbn = P.mblk0[n + 1] - P.mblk0[n];
-    const int gn = (nbn + kMfmaColBlocksPerUnit - 1) / kMfmaColBlocksPerUnit;
+    const int gn = (nbn + cb - 1) / cb;
     if (grp < g0 + gn) {
-      blk0 = (grp - g0) * kMfmaColBlocksPerUnit;
+      blk0 = (grp - g0) * cb;
       return n;
     }
     g0 += gn;
@@ -288,37 +288,40 @@ __device__ __forceinline__ int mfma_group_slice(const PoolView& P, int grp, int&
   return -1;
 }
 
-// Per-lane y rows of a matrix-core expand tile: chunk q of a lane belongs to token
-// (64 q + lane) / RC of the tile (clamped to the tile), whose row of y starts at
-// row[q] (slice offset included).  Loaded once per unit.
-template <typename TY>
+// Per-lane y rows of a matrix-core expand tile for blocks of BC columns: chunk q of a
+// lane belongs to token (64 q + lane) / RC of the tile (clamped to the tile), whose
+// row of y starts at row[q] (slice offset included).  Set once per unit.
+template <typename TY, int BC>
 struct ExpandRows16 {
   static constexpr int YC = 16 / (int)sizeof(TY);                // y elements per 16-byte chunk
-  static constexpr int RC = kMfmaCols / YC;                      // chunks per token row of a block
+  static constexpr int RC = BC / YC;                             // chunks per token row of a block
   static constexpr int YCH = kMfmaTileM * RC / 64;               // y chunks per lane
   TY* row[YCH];
-  __device__ __forceinline__ void load(const RouteView& R, TY* __restrict__ y, int ldy, int on, int p0, int len) {
+  // tok: this lane's token id of the tile (token lane % 16, clamped to the tile)
+  __device__ __forceinline__ void load(int tok, TY* __restrict__ y, int ldy, int on) {
     const int lane = lane_id();
 #pragma unroll
     for (int q = 0; q < YCH; ++q) {
       const int t = (q * 64 + lane) / RC;
-      row[q] = y + (size_t)R.sorted[p0 + min(t, len - 1)] * ldy + on;
+      row[q] = y + (size_t)__shfl(tok, t) * ldy + on;
     }
   }
 };
 
-// Loads of one 128-column block of one tile, all unconditional: the tile's y chunks
-// (a lane past the tile re-reads its clamped token's chunk, never stored; columns
-// past the slice re-read its last chunk, never stored) and the B fragments of the
-// NKS rank steps (a lane whose ranks lie past the slot's Bk stride reads the rank-0
-// fragment of its column and zeroes it; columns past the slice read column 0, never
-// stored).
-template <typename TY, int NKS>
+// Loads of one block of BC columns (BC / 16 column strips of 16) of one tile, all
+// unconditional: the tile's y chunks (a lane past the tile re-reads its clamped
+// token's chunk, never stored; columns past the slice re-read its last chunk, never
+// stored) and the B fragments of the NKS rank steps (a lane whose ranks lie past the
+// slot's Bk stride reads the rank-0 fragment of its column and zeroes it; columns
+// past the slice read column 0, never stored).
+template <typename TY, int NKS, int BC>
 struct ExpandMfmaBlock {
-  using Rows = ExpandRows16<TY>;
+  using Rows = ExpandRows16<TY, BC>;
   static constexpr int YC = Rows::YC, RC = Rows::RC, YCH = Rows::YCH;
+  static constexpr int NCB = BC / 16;                            // 16-column strips
+  static constexpr int kRegs = YCH + NCB * NKS;                  // 16-byte chunks per lane
   uint4 yv[YCH];
-  uint4 bv[NKS][8];
+  uint4 bv[NKS][NCB];
   int c0;
 
   __device__ __forceinline__ void issue(const Rows& Y, const uint16_t* __restrict__ bk, int rs, int dn, int c0_,
@@ -335,7 +338,7 @@ struct ExpandMfmaBlock {
       if (ks < nks) {   // compile-time true unless NKS covers a range of rank-step counts
         const int j0 = ks * kMfmaK + 8 * lk, jc = j0 < rs ? j0 : 0;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
+        for (int cb = 0; cb < NCB; ++cb) {
           const int col = c0 + 16 * cb + lr;
           bv[ks][cb] = ld16(bk + (size_t)(col < dn ? col : 0) * rs + jc);
         }
@@ -348,15 +351,15 @@ struct ExpandMfmaBlock {
   __device__ __forceinline__ void finish(const Rows& Y, int rs, int dn, int len, int nks, float scale,
                                          const uint4 (&uh)[NKS], const uint4 (&ul)[NKS], float* __restrict__ ds) const {
     const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
-    f32x4_t acc[8];
+    f32x4_t acc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks < nks) {
         const bool kin = ks * kMfmaK + 8 * lk < rs;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
+        for (int cb = 0; cb < NCB; ++cb) {
           const uint4 b = keep_if(bv[ks][cb], kin);
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uh[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ul[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
@@ -365,7 +368,7 @@ struct ExpandMfmaBlock {
     }
     // lane holds D[token 4 lk + i][column 16 cb + lr]
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ds[(4 * lk + i) * kDsPitch + 16 * cb + lr] = acc[cb][i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -401,22 +404,35 @@ struct ExpandMfmaBlock {
   }
 };
 
+// Block width of the expand body: 128 columns when two blocks' loads fit in 12
+// chunks per lane, else 64 when they do, else 128 without overlap.
+template <typename TY, int NKS>
+struct ExpandBlockWidth {
+  static constexpr int value = ExpandMfmaBlock<TY, NKS, 128>::kRegs <= 12  ? 128
+                               : ExpandMfmaBlock<TY, NKS, 64>::kRegs <= 12 ? 64
+                                                                           : 128;
+};
+
 // Body of one expand unit with NKS rank steps of 32 (nks <= NKS of them real), NSB
-// split batches of the workspace partials (0: the caller's finished u by token).
-// Order of the memory traffic: the u loads, then the first block's y chunks and B
-// fragments, all in flight together; then, while a block's products run, the next
-// block's loads are in flight (two blocks' loads held when they fit in 12 chunks per
-// lane, else one block at a time).  Every group has kMfmaColBlocksPerUnit blocks: a
-// block past the slice's end loads clamped addresses and stores nothing.  There are
-// no branches between a load and its use, so the compiler keeps the batches as
-// written.
-template <typename TY, int NKS, int NSB>
-__device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, const ExpandRows16<TY>& Y,
-                                                 const uint16_t* __restrict__ bk, int rs, int n, int dn,
-                                                 int c00, int p0, int len, int r, int nks, float scale,
+// split batches of the workspace partials (0: the caller's finished u by token), CB
+// 128-column blocks.  Order of the memory traffic: the u loads, then the first
+// block's y chunks and B fragments, all in flight together; then, while a block's
+// products run, the next block's loads are in flight (blocks narrowed to 64 columns
+// when that is what lets two blocks' loads fit in 12 chunks per lane; one block at a
+// time when even that does not fit).  A block past the slice's end loads clamped
+// addresses and stores nothing.  There are no branches between a load and its use,
+// so the compiler keeps the batches as written.
+template <typename TY, int NKS, int NSB, int CB>
+__device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, TY* __restrict__ y, int ldy,
+                                                 const uint16_t* __restrict__ bk, int rs, int n, int on, int dn,
+                                                 int c00, int p0, int len, int tok, int r, int nks, float scale,
                                                  float* __restrict__ ds) {
-  using Blk = ExpandMfmaBlock<TY, NKS>;
-  constexpr bool kPipe = Blk::YCH + 8 * NKS <= 12;
+  constexpr int BC = ExpandBlockWidth<TY, NKS>::value;
+  constexpr int NB = CB * (kMfmaCols / BC);                     // blocks of the unit
+  using Blk = ExpandMfmaBlock<TY, NKS, BC>;
+  constexpr bool kPipe = Blk::kRegs <= 12;
+  typename Blk::Rows Y;
+  Y.load(tok, y, ldy, on);
   uint4 uh[NKS], ul[NKS];
   Blk b0, b1;
   if constexpr (NSB > 0) {
@@ -438,51 +454,61 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
   }
   if constexpr (kPipe) {
 #pragma unroll
-    for (int i = 0; i < kMfmaColBlocksPerUnit; i += 2) {
-      b1.issue(Y, bk, rs, dn, c00 + (i + 1) * kMfmaCols, nks);
+    for (int i = 0; i < NB; i += 2) {
+      if (i + 1 < NB) b1.issue(Y, bk, rs, dn, c00 + (i + 1) * BC, nks);
       sched_fence();
       b0.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
-      if (i + 2 < kMfmaColBlocksPerUnit) b0.issue(Y, bk, rs, dn, c00 + (i + 2) * kMfmaCols, nks);
+      if (i + 2 < NB) b0.issue(Y, bk, rs, dn, c00 + (i + 2) * BC, nks);
       sched_fence();
-      b1.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
+      if (i + 1 < NB) b1.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kMfmaColBlocksPerUnit; ++i) {
-      if (i > 0) b0.issue(Y, bk, rs, dn, c00 + i * kMfmaCols, nks);
+    for (int i = 0; i < NB; ++i) {
+      if (i > 0) b0.issue(Y, bk, rs, dn, c00 + i * BC, nks);
       sched_fence();
       b0.finish(Y, rs, dn, len, nks, scale, uh, ul, ds);
     }
   }
 }
 
-// One expand unit: tile `tile`, column group grp (kMfmaColBlocksPerUnit blocks of
-// one slice).  KSM is the number of rank steps of 32 the pool's padded rank has at
+// One expand unit: tile `tile`, column group grp (cb blocks of one slice, cb = 1 or
+// kMfmaColBlocksPerUnit).  KSM is the number of rank steps of 32 the pool's padded rank has at
 // most (1, 2, 4 or 8); the body is specialised for the tile's own step count (1 or
 // 2; for KSM >= 4 one body with run-time bounds) and split batches.  Wave-uniform; ds is the wave's
 // kExpandMfmaWaveFloats floats of LDS.
 template <typename TY, int KSM>
 __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
-                                                 TY* __restrict__ y, int ldy, int tile, int grp,
+                                                 TY* __restrict__ y, int ldy, int tile, int grp, int cb,
                                                  float* __restrict__ ds) {
   int blk0;
-  const int n = mfma_group_slice(P, grp, blk0);
+  const int n = mfma_group_slice(P, grp, cb, blk0);
   if (n < 0) return;
   const int on = P.o[n], dn = P.d[n], c00 = blk0 * kMfmaCols;
   const int4 td = R.tiles[tile];
   const int slot = td.x, p0 = td.y, len = td.z;
   // the slot-table entry and the tile's token ids in one round trip
+  // the slot-table entry and this lane's token id (token lane % 16) in one round trip
   const SlotEntry e = P.table[slot];
-  ExpandRows16<TY> Y;
-  Y.load(R, y, ldy, on, p0, len);
+  const int tok = R.sorted[p0 + min(lane_id() & 15, len - 1)];
   if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
   const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
   const uint16_t* __restrict__ bk = static_cast<const uint16_t*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
   const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
-#define RAX_EXPAND_BODY(NK, NB) \
-  expand_mfma_body<TY, NK, NB>(R, U, Y, bk, rs, n, dn, c00, p0, len, r, nks, e.scale, ds)
-#define RAX_EXPAND_BODIES(NK) \
-  do { if (nsb == 1) RAX_EXPAND_BODY(NK, 1); else if (nsb == 2) RAX_EXPAND_BODY(NK, 2); else RAX_EXPAND_BODY(NK, 0); } while (0)
+#define RAX_EXPAND_BODY(NK, NB, CB) \
+  expand_mfma_body<TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tok, r, nks, e.scale, ds)
+#define RAX_EXPAND_BODIES(NK)                                                          \
+  do {                                                                                 \
+    if (cb == 1) {                                                                     \
+      if (nsb == 1) RAX_EXPAND_BODY(NK, 1, 1);                                         \
+      else if (nsb == 2) RAX_EXPAND_BODY(NK, 2, 1);                                    \
+      else RAX_EXPAND_BODY(NK, 0, 1);                                                  \
+    } else {                                                                           \
+      if (nsb == 1) RAX_EXPAND_BODY(NK, 1, kMfmaColBlocksPerUnit);                     \
+      else if (nsb == 2) RAX_EXPAND_BODY(NK, 2, kMfmaColBlocksPerUnit);                \
+      else RAX_EXPAND_BODY(NK, 0, kMfmaColBlocksPerUnit);                              \
+    }                                                                                  \
+  } while (0)
   if constexpr (KSM <= 2) {
     if (nks == 1) RAX_EXPAND_BODIES(1);
     else if constexpr (KSM == 2) RAX_EXPAND_BODIES(2);

@@ -433,11 +433,12 @@ def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
         _log(f"  {mode}: normwise rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("mode", ["default", "all-mfma", "mfma16", "vector"])
+@pytest.mark.parametrize("mode", ["default", "all-mfma", "all-mfma-wide", "mfma16", "vector"])
 def test_short_segments_every_path(rx, mode):
     """Segments of 1..17 tokens through each split between the vector and matrix-core
-    units: the default threshold, every segment on the matrix cores (1-token tiles),
-    a threshold of 16, and the vector units only."""
+    units: the default threshold, every segment on the matrix cores (1-token tiles;
+    matrix-core expand units of one column block, then of four), a threshold of 16,
+    and the vector units only."""
     import os
     segments = [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17]
     slices = [1024, 256, 256]
@@ -447,7 +448,9 @@ def test_short_segments_every_path(rx, mode):
     ads = oracle_adapters(W, mod)
     ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
                        max_rank=W.Rmax)
-    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}, "mfma16": {"RAXLORA_MFMA_MIN_SEG": "16"},
+    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "1000000000"},
+           "all-mfma-wide": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "0"},
+           "mfma16": {"RAXLORA_MFMA_MIN_SEG": "16"},
            "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
     os.environ.update(env)
     try:
