@@ -38,6 +38,17 @@
  *     work that reads it may still run on another stream.  lora_linear and
  *     lora_shrink use a workspace owned by the pool, so two of them on one pool
  *     must not overlap in time (same stream is always safe).
+ *   - Environment (read by the library; none is needed, all select among
+ *     equivalent paths or launch shapes, and results stay within the tolerances
+ *     the tests check):
+ *       RAXLORA_MFMA_MIN_SEG  segments of at least this many tokens go to the
+ *                             matrix cores (bf16 pools; default 4; read when a
+ *                             routing object is created)
+ *       RAXLORA_DISABLE_MFMA  1: every segment on the vector units
+ *       RAXLORA_CB1_MAX       matrix-core expand units take one 128-column block
+ *                             instead of four when (column groups of four x tile
+ *                             slots) is at most this (default 512)
+ *       RAXLORA_XCD_GROUP     consecutive decode units kept on one XCD (default 4)
  */
 #ifndef RAXLORA_H
 #define RAXLORA_H
