@@ -188,11 +188,57 @@ hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W
 // LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
 __host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }
 
+// Split partials of a decode expand tile's rank-space values, QV per lane: value
+// idx = lane + 64 q is rank idx / 4 of token idx % 4 (token-fastest, as the tile reads
+// them from LDS).  load() issues the first kUSplitBatch splits of every value
+// unconditionally (clamped addresses; splits past nsplit re-read the last), so it
+// can go out in the same batch as the tile's B^T and y rows; stage() adds them in
+// split order (-0.0f, the exact identity, for splits past nsplit; any further batch
+// loaded there) and writes usm, zero past the rank or the tile's tokens.
+template <int QV>
+struct DecodeUPartials {
+  float pv[QV][kUSplitBatch];
+  const float* base[QV];
+  bool ok[QV];
+  __device__ __forceinline__ void load(const UView& U, int n, int row0, int nt, int r) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int qv = 0; qv < QV; ++qv) {
+      const int idx = lane + 64 * qv, j = idx >> 2, i = idx & 3;
+      ok[qv] = i < nt && j < r;
+      base[qv] = U.p + n * U.n_stride + (long long)(row0 + (ok[qv] ? i : 0)) * U.row_stride + (ok[qv] ? j : 0);
+#pragma unroll
+      for (int q = 0; q < kUSplitBatch; ++q) pv[qv][q] = base[qv][(long long)min(q, U.nsplit - 1) * U.split_stride];
+    }
+  }
+  __device__ __forceinline__ void stage(const UView& U, int rp, float* __restrict__ usm) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int qv = 0; qv < QV; ++qv) {
+      float v = pv[qv][0];
+#pragma unroll
+      for (int q = 1; q < kUSplitBatch; ++q) v += q < U.nsplit ? pv[qv][q] : -0.f;
+      for (int q0 = kUSplitBatch; q0 < U.nsplit; q0 += 4) {
+        float w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = base[qv][(long long)min(q0 + q, U.nsplit - 1) * U.split_stride];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v += q0 + q < U.nsplit ? w[q] : -0.f;
+      }
+      const int idx = lane + 64 * qv;
+      if (idx < kExpandTok * rp) usm[idx] = ok[qv] ? v : 0.f;
+    }
+  }
+};
+
 // One decode expand item: column tile [c0, c0 + 512) of slice n, token tiles
 // tt0, tt0 + 4 * ntg, ... of slot s.  Per tile: the tile's rank-space values (split
 // partials added in split order, from L2) are staged in the wave's LDS token-fastest,
-// then the B^T rows and y rows are issued, then the contraction.
-template <typename TW, typename TY>
+// and the B^T rows and y rows are loaded, then the contraction.  For the first tile,
+// when the padded rank gives at most QV values per lane (QV > 0), the partials go
+// out in the same batch as the B^T and y rows, so the tile waits for one round trip
+// after its record; other tiles stage first, then load B^T and y.
+template <typename TW, typename TY, int QV>
 __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const RouteView& R, const UView& U,
                                                     TY* __restrict__ y, int ldy, int s, const SlotEntry& e,
                                                     int n, int c0, int L, int p0, int tt0, int4 tq0, int ntg,
@@ -202,7 +248,23 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   const int r = e.rank;
   const int rp = (r + Tile::RB - 1) / Tile::RB * Tile::RB;   // rank padded to the row batch
   const TW* __restrict__ bt_slot = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n];
-  for (int tt = tt0; tt < L; tt += ntg * kExpandTok) {
+  int tt = tt0;
+  if constexpr (QV > 0) {
+    if (!U.by_token && kExpandTok * rp <= 64 * QV) {
+      const int nt = min(kExpandTok, L - tt);
+      DecodeUPartials<QV> up;
+      up.load(U, n, p0 + tt, nt, r);
+      Tile tile;
+      tile.issue(P, bt_slot, y, ldy, n, c0, r, tq0);
+      sched_fence();
+      up.stage(U, rp, usm);
+      wave_lds_sync();
+      tile.finish(P, r, nt, e.scale, reinterpret_cast<const float4*>(usm));
+      wave_lds_sync();
+      tt += ntg * kExpandTok;
+    }
+  }
+  for (; tt < L; tt += ntg * kExpandTok) {
     const int nt = min(kExpandTok, L - tt);
     const int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
     for (int idx = lane; idx < kExpandTok * rp; idx += 64) {
@@ -221,7 +283,7 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   }
 }
 
-template <typename TW, typename TY>
+template <typename TW, typename TY, int QV>
 __device__ __forceinline__ void expand_decode_item(const PoolView& P, const RouteView& R, const UView& U,
                                                    TY* __restrict__ y, int ldy, const Plan& plan,
                                                    int item, float* __restrict__ usm) {
@@ -244,7 +306,7 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
   if (!((e.slice_mask >> n) & 1u)) return;
   const int c0 = (ct - P.tile0[n]) * kTileCols;
-  expand_decode_tiles<TW, TY>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
+  expand_decode_tiles<TW, TY, QV>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
 }
 
 // One wave per workgroup: matrix-core (tile, column group) items, then decode items.
@@ -255,7 +317,8 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UVi
   const int b = blockIdx.x;
   if (b >= n_mfma_blocks) {
     const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
-    if (d < plan.n_dec_blocks) expand_decode_item<TW, TY>(P, R, U, y, ldy, plan, d, smem);
+    // values per lane of the first tile's early partial loads: the padded rank over 16
+    if (d < plan.n_dec_blocks) expand_decode_item<TW, TY, (KSM <= 2 ? 2 * KSM : 0)>(P, R, U, y, ldy, plan, d, smem);
     return;
   }
   if constexpr (sizeof(TW) == 2) {
