@@ -33,7 +33,20 @@ struct lora_pool {
   float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rk] by sorted position
   int nsplit = 1, ns = 1;     // decode shrink: k splits, chunk steps per split (fixed by k)
   std::vector<SlotEntry> mirror;
+  std::vector<uint8_t> order;  // slots by descending rank, stable (S <= kMaxOrderedSlots)
 };
+
+namespace {
+// Decode expand units of a high-rank slot run longest (one B^T batch per 16 ranks),
+// so they are dispatched first: slots sorted by descending rank, ties by index.
+void update_order(lora_pool* p) {
+  if (p->S > rax::kMaxOrderedSlots) return;
+  std::vector<int> idx(p->S);
+  for (int s = 0; s < p->S; ++s) idx[s] = s;
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return p->mirror[a].rank > p->mirror[b].rank; });
+  p->order.assign(idx.begin(), idx.end());
+}
+}  // namespace
 
 struct lora_routing {
   int device = 0;
@@ -158,6 +171,8 @@ rax::PoolView pool_view(const lora_pool* p) {
     v.tile0[n] = n <= p->N ? p->tile0[n] : p->tile0[p->N];
     v.mblk0[n] = n <= p->N ? p->mblk0[n] : p->mblk0[p->N];
   }
+  v.ordered = (int)p->order.size() == p->S ? 1 : 0;
+  for (size_t i = 0; i < p->order.size(); ++i) v.slot_order[i] = p->order[i];
   return v;
 }
 
@@ -391,6 +406,7 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   p->tile0[num_slices] = tiles;
   p->mblk0[num_slices] = mblocks;
   p->mirror.assign(max_slots, SlotEntry{0, 0.f, 0u, 0});
+  update_order(p);
 
   const size_t a_bytes = (size_t)max_slots * num_slices * max_lora_rank * in_features * p->esize;
   const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
@@ -493,6 +509,7 @@ lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* 
     cleanup();
   }
   pool->mirror[slot] = entry;
+  update_order(pool);
   return ok();
 }
 
@@ -505,6 +522,7 @@ lora_status lora_unregister_adapter(lora_pool* pool, int slot, hipStream_t strea
   hipError_t e = rax::launch_set_slot(pool->table, slot, entry, stream);
   if (e != hipSuccess) return hip_fail(e, "slot table update");
   pool->mirror[slot] = entry;
+  update_order(pool);
   return ok();
 }
 

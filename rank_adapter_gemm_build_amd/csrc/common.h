@@ -22,6 +22,7 @@
 namespace rax {
 
 constexpr int kMaxSlices = LORA_MAX_SLICES;
+constexpr int kMaxOrderedSlots = 256;   // pools up to this size dispatch decode expand units by rank
 constexpr int kMaxSplit = 16;         // k splits of a decode shrink (partial sums per split)
 constexpr int kColsPerLane = 8;    // expand: output columns owned by one lane
 constexpr int kTileCols = 64 * kColsPerLane;  // expand: columns of one wave tile
@@ -58,6 +59,8 @@ struct PoolView {
   int d[kMaxSlices];
   int o[kMaxSlices];
   int tile0[kMaxSlices + 1];  // first expand column tile of each slice; tile0[N] = n_ctiles
+  int ordered;                // 1: slot_order below is valid (S <= kMaxOrderedSlots)
+  uint8_t slot_order[256];    // slots by descending rank (decode expand dispatch order)
   int mblk0[kMaxSlices + 1];  // first matrix-core column block of each slice; mblk0[N] = n_mblocks
 };
 

@@ -290,7 +290,8 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   // token-tile siblings (same slot and columns, same rows of B^T) are neighbours
   const int tg = item % plan.ntg;
   const int rest = item / plan.ntg;
-  const int ct = rest % P.n_ctiles, s = rest / P.n_ctiles;
+  const int ct = rest % P.n_ctiles, si = rest / P.n_ctiles;
+  const int s = P.ordered ? (int)P.slot_order[si] : si;   // high-rank slots first
   // first round trip: record header, token ids of the first tile, slot-table entry
   const int tt0 = tg * kExpandTok;
   const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
