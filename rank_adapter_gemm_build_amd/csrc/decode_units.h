@@ -26,12 +26,6 @@ constexpr int kShrinkRows = 16;   // rank rows per decode shrink block
 constexpr int kShrinkTok = 4;     // tokens per decode tile
 constexpr int kExpandTok = 4;
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Token ids at positions tt .. tt + 3 of slot s's segment: from the slot's routing
 // record when they are among its first kRecTokens (the record repeats the segment's
 // first token past its end), else from sorted_ids (position clamped into the

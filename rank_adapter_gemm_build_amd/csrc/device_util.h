@@ -175,6 +175,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// LDS writes of this wave visible to all of its lanes (wave-scope fences around a
+// wave barrier; no workgroup barrier needed for one-wave workgroups)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
