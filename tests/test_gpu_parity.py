@@ -464,6 +464,31 @@ def test_short_segments_every_path(rx, mode):
     _log(f"  normwise rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("Rmax", [96, 128, 256])
+@pytest.mark.parametrize("mode", ["mfma", "vector"])
+def test_high_rank_pools(rx, Rmax, mode):
+    """Pools whose padded rank needs 3-8 matrix-core rank steps (the expand's general
+    body) and several B^T row batches on the vector units; ranks mixed up to Rmax,
+    short and long segments."""
+    import os
+    segments = [1, 3, 5, 17, 40, 2]
+    slices = [520, 264]
+    W = small_case(600 + Rmax, T=0, S=7, k=1032, slices=slices, Rmax=Rmax, segments=segments)
+    mod = W.modules[0]
+    _log(f"Rmax={Rmax} mode={mode} ranks={sorted(W.ranks.values())} T={W.T}")
+    ads = oracle_adapters(W, mod)
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
+                       max_rank=Rmax)
+    if mode == "vector":
+        os.environ["RAXLORA_DISABLE_MFMA"] = "1"
+    try:
+        y = _run_linear(rx, W, mod, np.zeros((W.T, sum(slices)), dtype=np.float32), "f32")
+    finally:
+        os.environ.pop("RAXLORA_DISABLE_MFMA", None)
+    err = check_close(from_device(y), ref, "bf16", f"delta (Rmax={Rmax}, {mode})")
+    _log(f"  normwise rel err {err:.2e}")
+
+
 def test_shrink_matrix_cores_match_oracle(rx):
     """u from the matrix-core shrink of long segments (standalone lora_shrink)."""
     import torch
