@@ -54,8 +54,8 @@ def test_routing_golden(rx):
 
 @pytest.mark.parametrize("T,S,seed", [(1, 1, 0), (7, 3, 1), (64, 8, 2), (1000, 64, 3), (4096, 128, 4),
                                       (3333, 1024, 5), (20000, 17, 6), (513, 2, 7),
-                                      # around the one-wave kernel's limits (T <= 256, S < 128)
-                                      (256, 127, 8), (255, 64, 9), (129, 100, 10), (257, 8, 11), (200, 128, 12)])
+                                      # around the one-wave kernel's limits (launched for T <= 128, S < 128)
+                                      (128, 127, 8), (127, 64, 9), (129, 100, 10), (257, 8, 11), (100, 128, 12)])
 def test_routing_random(rx, T, S, seed):
     rng = np.random.default_rng(seed)
     ids = rng.integers(-1, S, size=T)
