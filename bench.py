@@ -2,8 +2,11 @@
 """Benchmark of the batched multi-adapter LoRA hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch: build the routing
-metadata from the batch's token -> slot ids, then one fused shrink+expand
-(lora_linear) per target module, adding onto a base output already in HBM.
+metadata from the batch's token -> slot ids, then one fused shrink+expand per
+target module, adding onto a base output already in HBM.  The first module's call
+is lora_route_linear (routing + shrink + expand; for batches of up to 256 tokens the
+routing is built inside the shrink launch), the others lora_linear on that routing.
+--separate-routing times lora_build_routing + lora_linear instead.
 Adapters are registered before timing (registration is once per adapter, off the
 per-step path).  Inputs are seeded synthetic tensors shaped like the workload.
 
@@ -184,7 +187,7 @@ def run(args):
     torch.cuda.set_device(0)
     W = workload(args.workload)
     use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0"
-    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "16"))
+    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "4"))   # the library default
     acc, flops, by_path = step_accounting(W, mfma_min, use_mfma)
     step_bytes = sum(acc.values())
     log(f"workload {W.name}: T={W.T} S={W.S} modules={[m.name for m in W.modules]} "
@@ -202,10 +205,19 @@ def run(args):
 
     def step(i):
         inst = insts[i % M]
-        st = lib.lora_build_routing(inst.routing.handle, inst.ids.data_ptr(), T, stream)
-        if st:
-            raise rx.LoraError(st, "lora_build_routing")
-        for pool, xp, ldx, yp, ldy in inst.calls:
+        calls = inst.calls
+        if args.separate_routing:
+            st = lib.lora_build_routing(inst.routing.handle, inst.ids.data_ptr(), T, stream)
+            if st:
+                raise rx.LoraError(st, "lora_build_routing")
+        else:
+            pool, xp, ldx, yp, ldy = calls[0]
+            st = lib.lora_route_linear(pool, inst.routing.handle, inst.ids.data_ptr(), T, xp, ldx, yp, ldy, ydt,
+                                       stream)
+            if st:
+                raise rx.LoraError(st, "lora_route_linear")
+            calls = calls[1:]
+        for pool, xp, ldx, yp, ldy in calls:
             st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, stream)
             if st:
                 raise rx.LoraError(st, "lora_linear")
@@ -290,7 +302,9 @@ def run(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": W.dtype, "data": "synthetic",
         "config": {"workload": W.name, "tokens": T, "slots": W.S, "k": [m.k for m in W.modules],
                    "slices": [m.slices for m in W.modules], "ranks": sorted(set(W.ranks.values())),
-                   "max_lora_rank": W.Rmax, "parallelism": "none (1 GPU)"},
+                   "max_lora_rank": W.Rmax, "parallelism": "none (1 GPU)",
+                   "calls": "lora_build_routing + lora_linear" if args.separate_routing else
+                            "lora_route_linear + lora_linear"},
         "roofline": roofline,
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
@@ -317,6 +331,8 @@ def main():
     ap.add_argument("--max-instances", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-routing", action="store_true",
+                    help="lora_build_routing + lora_linear per step instead of lora_route_linear for the first module")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     args = ap.parse_args()
     if args.gpus != 1:

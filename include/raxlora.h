@@ -247,6 +247,23 @@ lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, cons
                         void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
+ * Routing and fused shrink + expand of one batch: lora_build_routing(routing,
+ * token_slot_ids, T) followed by lora_linear(pool, routing, x, y), with the same
+ * results (routing outputs and y bitwise identical).  For 1 <= T <= 256 tokens and
+ * pools of at most 255 slots the routing is built inside the shrink launch, whose
+ * units find their segments from token_slot_ids directly ([vLLM-book] §16.4.2: the
+ * per-batch metadata that groups tokens by slot; [TRT-LLM] "一次 decode 批次的路由"), so
+ * the call costs two launches instead of three; larger batches take the two calls.
+ * The routing object then holds this batch's routing for further lora_linear calls
+ * (other target modules of the same tokens).  token_slot_ids must stay unchanged
+ * until the call's work has run.  Arguments and errors as lora_build_routing and
+ * lora_linear (routing and pool must have the same slot count).
+ */
+lora_status lora_route_linear(const lora_pool* pool, lora_routing* routing, const int32_t* token_slot_ids,
+                              int T, const void* x, int ldx, void* y, int ldy, lora_dtype ydtype,
+                              hipStream_t stream);
+
+/*
  * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
  * lora_build_routing, lora_shrink, lora_expand and lora_linear launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start

@@ -46,6 +46,7 @@ SIGNATURES = {
     "lora_shrink": (_I, [_P, _P, _VP, _I, _VP, _VP]),
     "lora_expand": (_I, [_P, _P, _VP, _VP, _I, _I, _VP]),
     "lora_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
+    "lora_route_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP]),
     "lora_timing_enable": (_I, [_I]),
     "lora_timing_report": (_I, [C.POINTER(C.c_double), C.POINTER(C.c_int), _I]),
     "lora_timing_kernel_name": (C.c_char_p, [_I]),
@@ -172,6 +173,12 @@ def lora_expand(pool: int, routing: int, u: int, y: int, ldy: int, ydtype: int, 
 
 def lora_linear(pool: int, routing: int, x: int, ldx: int, y: int, ldy: int, ydtype: int, stream: int = 0) -> None:
     _check(lib.lora_linear(pool, routing, x or None, ldx, y or None, ldy, ydtype, stream or None), "lora_linear")
+
+
+def lora_route_linear(pool: int, routing: int, ids: int, T: int, x: int, ldx: int, y: int, ldy: int, ydtype: int,
+                      stream: int = 0) -> None:
+    _check(lib.lora_route_linear(pool, routing, ids or None, T, x or None, ldx, y or None, ldy, ydtype,
+                                 stream or None), "lora_route_linear")
 
 
 def lora_timing_enable(on: bool) -> None:
@@ -324,3 +331,14 @@ def linear(pool: Pool, routing: Routing, x, y, stream=None) -> None:
     if _dt(x) != pool.wdtype:
         raise TypeError("x dtype must match the pool dtype")
     lora_linear(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y), _stream(stream))
+
+
+def route_linear(pool: Pool, routing: Routing, ids, x, y, stream=None) -> None:
+    """routing.build(ids) then linear(pool, routing, x, y), in one fewer launch for small
+    batches (see lora_route_linear)."""
+    if _dt(x) != pool.wdtype:
+        raise TypeError("x dtype must match the pool dtype")
+    T = int(ids.numel())
+    lora_route_linear(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
+                      y.stride(0), _dt(y), _stream(stream))
+    routing.T = T

@@ -176,6 +176,10 @@ rax::PoolView pool_view(const lora_pool* p) {
   return v;
 }
 
+rax::RouteOut route_out(const lora_routing* r) {
+  return rax::RouteOut{r->counts, r->offs, r->sorted, r->active, r->desc, r->tiles, r->rec, r->meta};
+}
+
 rax::RouteView route_view(const lora_routing* r) {
   rax::RouteView v{};
   v.counts = r->counts;
@@ -222,16 +226,15 @@ lora_status check_pair(const lora_pool* pool, const lora_routing* routing) {
   return LORA_OK;
 }
 
-lora_status check_x(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx) {
-  if (routing->T > 0 && !x) return fail(LORA_ERR_INVALID_ARG, "x is NULL");
+lora_status check_x(const lora_pool* pool, int T, const void* x, int ldx) {
+  if (T > 0 && !x) return fail(LORA_ERR_INVALID_ARG, "x is NULL");
   if (ldx < pool->k) return fail(LORA_ERR_SHAPE, "ldx = %d < in_features = %d", ldx, pool->k);
   if (ldx % 8 != 0 || !aligned16(x)) return fail(LORA_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
   return LORA_OK;
 }
 
-lora_status check_y(const lora_pool* pool, const lora_routing* routing, const void* y, int ldy,
-                    lora_dtype ydtype) {
-  if (routing->T > 0 && !y) return fail(LORA_ERR_INVALID_ARG, "y is NULL");
+lora_status check_y(const lora_pool* pool, int T, const void* y, int ldy, lora_dtype ydtype) {
+  if (T > 0 && !y) return fail(LORA_ERR_INVALID_ARG, "y is NULL");
   if (ydtype != LORA_F32 && ydtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown ydtype %d", (int)ydtype);
   if (ydtype != pool->wdtype && ydtype != LORA_F32)
     return fail(LORA_ERR_DTYPE, "y must be the pool dtype or float32");
@@ -311,11 +314,13 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
   return pl;
 }
 
+// self_ids: build the routing inside the launch from these ids (small batches)
 lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
-                       const rax::UView& U, hipStream_t stream) {
+                       const rax::UView& U, hipStream_t stream, const int32_t* self_ids = nullptr) {
   const rax::Plan pl = make_plan(pool, routing, false);
+  rax::SelfRoute sr{self_ids, route_out(routing)};
   hipError_t e = rax::launch_shrink(pool->wdtype, pool_view(pool), route_view(routing), x, ldx, U, pl,
-                                    stream, timer_for(rax::kKShrink));
+                                    self_ids ? &sr : nullptr, stream, timer_for(rax::kKShrink));
   if (e != hipSuccess) return hip_fail(e, "shrink launch");
   return LORA_OK;
 }
@@ -682,7 +687,7 @@ lora_status lora_shrink(const lora_pool* pool, const lora_routing* routing, cons
                         float* u, hipStream_t stream) {
   lora_status st = check_pair(pool, routing);
   if (st != LORA_OK) return st;
-  if ((st = check_x(pool, routing, x, ldx)) != LORA_OK) return st;
+  if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
   if (routing->T > 0 && !u) return fail(LORA_ERR_INVALID_ARG, "u is NULL");
   if (!aligned16(u)) return fail(LORA_ERR_ALIGN, "u must be 16-byte aligned");
   if (routing->T == 0) return ok();
@@ -702,7 +707,7 @@ lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, cons
                         int ldy, lora_dtype ydtype, hipStream_t stream) {
   lora_status st = check_pair(pool, routing);
   if (st != LORA_OK) return st;
-  if ((st = check_y(pool, routing, y, ldy, ydtype)) != LORA_OK) return st;
+  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
   if (routing->T > 0 && !u) return fail(LORA_ERR_INVALID_ARG, "u is NULL");
   if (!aligned16(u)) return fail(LORA_ERR_ALIGN, "u must be 16-byte aligned");
   if (routing->T == 0) return ok();
@@ -717,13 +722,40 @@ lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, cons
                         void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
   lora_status st = check_pair(pool, routing);
   if (st != LORA_OK) return st;
-  if ((st = check_x(pool, routing, x, ldx)) != LORA_OK) return st;
-  if ((st = check_y(pool, routing, y, ldy, ydtype)) != LORA_OK) return st;
+  if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
+  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
   if (routing->T == 0) return ok();
   DeviceGuard g(pool->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
   if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
+}
+
+lora_status lora_route_linear(const lora_pool* pool, lora_routing* routing, const int32_t* ids, int T,
+                              const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
+  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
+  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
+  if (T > routing->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, routing->max_tokens);
+  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
+  if (routing->S != pool->S) return fail(LORA_ERR_SHAPE, "routing has %d slots, pool has %d", routing->S, pool->S);
+  if (routing->device != pool->device)
+    return fail(LORA_ERR_INVALID_ARG, "routing on device %d, pool on device %d", routing->device, pool->device);
+  if (T > pool->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds the pool's max_tokens = %d", T, pool->max_tokens);
+  lora_status st = check_x(pool, T, x, ldx);
+  if (st != LORA_OK) return st;
+  if ((st = check_y(pool, T, y, ldy, ydtype)) != LORA_OK) return st;
+  // batches the shrink launch can route itself; others: the routing launch, then lora_linear
+  if (T < 1 || T > rax::kSelfRouteTokens || pool->S + 1 > rax::kSelfRouteKeys) {
+    if ((st = lora_build_routing(routing, ids, T, stream)) != LORA_OK) return st;
+    return lora_linear(pool, routing, x, ldx, y, ldy, ydtype, stream);
+  }
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  routing->T = T;
+  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream, ids)) != LORA_OK) return st;
   if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
   return ok();
 }

@@ -38,6 +38,8 @@ constexpr int kDefaultMfmaMinSeg = 4;   // segments at least this long use matri
 constexpr int kRecInts = 32;       // ints of one slot record: tokens, first position, 2 spare, token ids
 constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
 constexpr bool kHaveMfmaPath = true;    // matrix-core kernels compiled in
+constexpr int kSelfRouteTokens = 256;   // most tokens of a batch whose shrink launch builds its routing
+constexpr int kSelfRouteKeys = 256;     // most keys (slots + 1) of such a batch
 
 struct SlotEntry {
   int32_t rank;         // 0 = empty slot
@@ -126,8 +128,27 @@ hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, v
                              void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
                              int D, float scale, int premultiply, hipStream_t stream);
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream);
+// Output buffers of a routing (device memory; sizes as in RouteView).
+struct RouteOut {
+  int* counts;
+  int* offs;
+  int* sorted;
+  int* active;
+  int4* desc;
+  int4* tiles;
+  int* rec;
+  int* meta;
+};
+
+// A shrink launch that also builds the routing of its batch (T <= 256 tokens, S < 256
+// slots): the batch's slot ids (device) and the routing's output buffers.
+struct SelfRoute {
+  const int32_t* ids;
+  RouteOut out;
+};
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
-                         const UView& U, const Plan& plan, hipStream_t stream, const KTimer& tm);
+                         const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
+                         const KTimer& tm);
 
 hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
                          const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,

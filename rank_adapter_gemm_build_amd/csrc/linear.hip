@@ -46,30 +46,20 @@
 #include "device_util.h"
 #include "decode_units.h"
 #include "mfma_tiles.h"
+#include "route_wave.h"
 
 namespace rax {
 
 // ------------------------------------------------------------ decode shrink
-template <typename T>
-__device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const RouteView& R,
-                                                   const T* __restrict__ x, int ldx, const UView& U,
-                                                   const Plan& plan, int unit) {
-  const int tg = unit % plan.ntg;
-  int rest = unit / plan.ntg;
-  const int sp = rest % plan.nsplit;
-  rest /= plan.nsplit;
-  const int rb = rest % plan.nrb, s = rest / plan.nrb;
-  const int tt0 = tg * kShrinkTok;
-  // first round trip: record header, first token ids, slot-table entry
-  const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
-  const int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
-                                         : make_int4(0, 0, 0, 0);
-  const SlotEntry e = P.table[s];
-  const int L = hdr.x, p0 = hdr.y;
-  if (tt0 >= L) return;
-  if (plan.use_mfma && L >= R.mfma_min) return;   // long segment: matrix-core units
+// Token tiles tt0, tt0 + 4 ntg, ... of slot s's segment (L tokens from sorted
+// position p0) against 16 rank rows (block rb) over k split sp; toks(tt) gives the
+// token ids at positions tt .. tt + 3 of the segment (valid rows past its end).
+template <typename T, typename Toks>
+__device__ __forceinline__ void shrink_decode_tiles(const PoolView& P, const T* __restrict__ x, int ldx,
+                                                    const UView& U, const Plan& plan, int s, int sp, int rb,
+                                                    int tt0, int L, int p0, const SlotEntry& e, const Toks& toks) {
   const int r = e.rank, F = P.N * r, fb = rb * kShrinkRows;
-  if (r == 0 || fb >= F) return;                   // all of the above is uniform per wave
+  if (r == 0 || fb >= F) return;                   // uniform per wave
   const int lane = lane_id();
   const ShrinkRows<T> A(P, s, r, fb);
   // this lane's output after the reduce-scatter: row fb + lane / 4, token lane % 4
@@ -79,13 +69,68 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
 
   for (int tt = tt0; tt < L; tt += plan.ntg * kShrinkTok) {
     const int nt = min(kShrinkTok, L - tt);
-    const int4 tq = tt == tt0 && tt0 + 4 <= kRecTokens ? tq0 : segment_tokens(R, s, tt, p0, L);
+    const int4 tq = toks(tt);
     const T* xrow[kShrinkTok];
 #pragma unroll
     for (int i = 0; i < kShrinkTok; ++i) xrow[i] = x + (size_t)tok_at(tq, i) * ldx;
     const float v = shrink_block_partial<T>(P, A, xrow, nt, sp, plan.nsplit, plan.ns);
     if (of < F && oi < nt) uo[(long long)(p0 + tt + oi) * U.row_stride] = v;   // rows by sorted position
   }
+}
+
+struct DecodeShrinkIndex {
+  int tg, sp, rb, s;
+  __device__ __forceinline__ DecodeShrinkIndex(const Plan& plan, int unit) {
+    tg = unit % plan.ntg;
+    int rest = unit / plan.ntg;
+    sp = rest % plan.nsplit;
+    rest /= plan.nsplit;
+    rb = rest % plan.nrb;
+    s = rest / plan.nrb;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const RouteView& R,
+                                                   const T* __restrict__ x, int ldx, const UView& U,
+                                                   const Plan& plan, int unit) {
+  const DecodeShrinkIndex u(plan, unit);
+  const int s = u.s, tt0 = u.tg * kShrinkTok;
+  // first round trip: record header, first token ids, slot-table entry
+  const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
+  const int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
+                                         : make_int4(0, 0, 0, 0);
+  const SlotEntry e = P.table[s];
+  const int L = hdr.x, p0 = hdr.y;
+  if (tt0 >= L) return;
+  if (plan.use_mfma && L >= R.mfma_min) return;   // long segment: matrix-core units
+  shrink_decode_tiles<T>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
+    return tt == tt0 && tt0 + 4 <= kRecTokens ? tq0 : segment_tokens(R, s, tt, p0, L);
+  });
+}
+
+// The same unit in a launch that builds the routing itself: the segment comes from
+// the batch's slot ids (BatchKeys), its token ids through the wave's LDS.
+template <typename T>
+__device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const RouteView& R,
+                                                        const int32_t* __restrict__ ids, const T* __restrict__ x,
+                                                        int ldx, const UView& U, const Plan& plan, int unit,
+                                                        int* __restrict__ tok) {
+  const DecodeShrinkIndex u(plan, unit);
+  const int s = u.s, tt0 = u.tg * kShrinkTok;
+  // first round trip: the batch's ids, slot-table entry
+  BatchKeys K;
+  K.load(ids, R.T, R.S);
+  const SlotEntry e = P.table[s];
+  int L, p0;
+  K.segment(s, L, p0, tok);
+  if (tt0 >= L) return;
+  if (plan.use_mfma && L >= R.mfma_min) return;
+  wave_lds_sync();
+  shrink_decode_tiles<T>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
+    const int last = L - 1;
+    return make_int4(tok[min(tt, last)], tok[min(tt + 1, last)], tok[min(tt + 2, last)], tok[min(tt + 3, last)]);
+  });
 }
 
 // Matrix-core work items of one launch, split over the XCDs: workgroup b runs on XCD
@@ -110,11 +155,59 @@ struct MfmaItems {
 // of a worker is its index mod 8), then the decode units.
 __host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + kXcds - 1) / kXcds * kXcds; }
 
-// One wave per workgroup: matrix-core (k part, tile, row group) items, then decode units.
-template <typename T>
+// One wave per workgroup: matrix-core (k part, tile, row group) items, then decode
+// units.  SELF: the launch also builds the routing (route_wave in workgroup 0;
+// workgroups 1-7 are idle, so the others keep their XCD numbering), and the units
+// take their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead
+// of the routing outputs being written meanwhile.
+template <typename T, bool SELF>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
-                                                    int ldx, UView U, Plan plan, int n_mfma_blocks) {
-  const int b = blockIdx.x;
+                                                    int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
+  int b = blockIdx.x;
+  if constexpr (SELF) {
+    __shared__ __align__(16) int sh[route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64)];
+    static_assert(route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64) >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
+    if (b < kXcds) {
+      if (b == 0)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
+      return;
+    }
+    b -= kXcds;
+    int* tok = sh + kSelfRouteK;
+    if (b >= n_mfma_blocks) {
+      const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
+      if (d < plan.n_dec_blocks) shrink_decode_unit_self<T>(P, R, sr.ids, x, ldx, U, plan, d, tok);
+      return;
+    }
+    if constexpr (sizeof(T) == 2) {
+      // LDS: slot counts [kSelfRouteK], then the tile's tokens, then the batch's keys
+      int* keys = sh + kSelfRouteK + kSelfRouteT;
+      int ntiles;
+      {
+        BatchKeys K;
+        K.load(sr.ids, R.T, R.S);
+        K.store(keys);
+        ntiles = BatchTiles::build(K, R.S, R.mfma_min, R.tile_m, R.max_tiles, sh);
+      }
+      const int per_part = ntiles * plan.nrg;
+      for (MfmaItems it(b, n_mfma_blocks, per_part * plan.nsplit); it.j < it.end; it.j += it.step) {
+        const int part = it.j / per_part, rem = it.j - part * per_part;
+        const int tile = rem / plan.nrg, rg = rem - tile * plan.nrg;
+        int slot, ti, L, p0;
+        BatchTiles::find(sh, R.S, R.mfma_min, R.tile_m, tile, slot, ti);
+        BatchKeys K;
+        K.reload(keys);
+        wave_lds_sync();
+        K.segment(slot, L, p0, tok);
+        wave_lds_sync();
+        const int first = ti * R.tile_m, len = min(R.tile_m, L - first);
+        const SlotEntry e = P.table[slot];
+        const uint16_t* __restrict__ xrow = x + (size_t)tok[first + min(lane_id() & 15, len - 1)] * ldx;
+        shrink_mfma_tile(P, e, xrow, U, slot, p0 + first, len, rg, part, plan.nsplit);
+      }
+    }
+    return;
+  }
   if (b >= n_mfma_blocks) {
     const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
     if (d < plan.n_dec_blocks) shrink_decode_unit<T>(P, R, x, ldx, U, plan, d);
@@ -134,26 +227,32 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
 
 template <typename T>
 static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, int ldx, const UView& U,
-                            const Plan& plan, hipStream_t stream, const KTimer& tm) {
+                            const Plan& plan, const SelfRoute* sr, hipStream_t stream, const KTimer& tm) {
   const int nm = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
   const int q = kXcds * plan.xcd_group;
   const int blocks = nm + (plan.n_dec_blocks + q - 1) / q * q;
-  RAX_LAUNCH(tm, shrink_kernel<T>, dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm);
+  if (sr)
+    RAX_LAUNCH(tm, (shrink_kernel<T, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm, *sr);
+  else
+    RAX_LAUNCH(tm, (shrink_kernel<T, false>), dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
+               SelfRoute{});
 }
 
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
-                         const UView& U, const Plan& plan, hipStream_t stream, const KTimer& tm) {
+                         const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
+                         const KTimer& tm) {
   const int cw = 64 * (wdtype == LORA_BF16 ? 8 : 4);
   const int chunks = (P.k + cw - 1) / cw;
   if (plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
       plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
       plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
-      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)))
+      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)) ||
+      (sr && (!sr->ids || R.T < 1 || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)))
     return hipErrorInvalidValue;
   if (wdtype == LORA_BF16)
-    launch_shrink_t(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, stream, tm);
+    launch_shrink_t(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
   else
-    launch_shrink_t(P, R, static_cast<const float*>(x), ldx, U, plan, stream, tm);
+    launch_shrink_t(P, R, static_cast<const float*>(x), ldx, U, plan, sr, stream, tm);
   return hipGetLastError();
 }
 

@@ -158,15 +158,13 @@ __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const uint16
   }
 }
 
-// One shrink unit: tile `tile`, row group rg (rows 64 rg .. 64 rg + 63), k part
-// `part` of nsplit.  Wave-uniform.  Parts with no k steps write zeros.
-__device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
-                                                 int ldx, const UView& U, int tile, int rg, int part, int nsplit) {
-  const int4 td = R.tiles[tile];
-  const int slot = td.x, p0 = td.y, len = td.z;
-  // the slot-table entry and this lane's token id (token lane % 16) in one round trip
-  const SlotEntry e = P.table[slot];
-  const uint16_t* __restrict__ xrow = x + (size_t)R.sorted[p0 + min(lane_id() & 15, len - 1)] * ldx;
+// One shrink unit of the tile of `len` tokens of slot `slot` at sorted position p0
+// (xrow: this lane's x row, token lane % 16, clamped into the tile), row group rg
+// (rows 64 rg .. 64 rg + 63), k part `part` of nsplit.  Wave-uniform.  Parts with no
+// k steps write zeros.
+__device__ __forceinline__ void shrink_mfma_tile(const PoolView& P, const SlotEntry& e,
+                                                 const uint16_t* __restrict__ xrow, const UView& U, int slot, int p0,
+                                                 int len, int rg, int part, int nsplit) {
   const int r = e.rank, F = P.N * r, fr0 = 64 * rg;
   if (r == 0 || fr0 >= F) return;
   int s0, s1;
@@ -180,6 +178,17 @@ __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteV
     shrink_mfma_rows<2>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else
     shrink_mfma_rows<1>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
+}
+
+// One shrink unit: tile `tile` of the routing's list.
+__device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
+                                                 int ldx, const UView& U, int tile, int rg, int part, int nsplit) {
+  const int4 td = R.tiles[tile];
+  const int slot = td.x, p0 = td.y, len = td.z;
+  // the slot-table entry and this lane's token id (token lane % 16) in one round trip
+  const SlotEntry e = P.table[slot];
+  const uint16_t* __restrict__ xrow = x + (size_t)R.sorted[p0 + min(lane_id() & 15, len - 1)] * ldx;
+  shrink_mfma_tile(P, e, xrow, U, slot, p0, len, rg, part, nsplit);
 }
 
 // ------------------------------------------------------------------ expand

@@ -27,20 +27,9 @@
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
+#include "route_wave.h"
 
 namespace rax {
-
-// Lanes of this wave whose key equals this lane's (keys below 2^nbits; lanes with
-// key < 0 match nothing), as a 64-bit mask.
-__device__ __forceinline__ unsigned long long match_key(int key, int nbits) {
-  unsigned long long m = __ballot(key >= 0);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (key >> b) & 1;
-    const unsigned long long bal = __ballot(bit);
-    m &= bit ? bal : ~bal;
-  }
-  return key >= 0 ? m : 0ull;
-}
 
 __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
     const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles, int stage,
@@ -200,128 +189,14 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
 }
 
 // Small batches (T <= kSmallRoutingT tokens, S + 1 <= kSmallRoutingK keys): the
-// same outputs from one wave, with no workgroup barriers.  Each lane holds up to 2
-// tokens (t = lane + 64 q), loaded in one batch.  Per 64-token group, bit-sliced key
-// matching gives every token its rank among the group's equal keys and the group's
-// count per key; a per-key running count in LDS makes the ranks stable across
-// groups.  One wave scan over the counts gives the segment starts, then the tokens
-// are scattered (to sorted_ids and an LDS copy from which the 128-byte slot records
-// are written whole, 16 bytes per lane), and the active-slot and tile lists are
-// compacted with ballots in slot order.
+// same outputs from one wave (route_wave).
 constexpr int kSmallRoutingT = 128;    // most tokens of the one-wave kernel
 constexpr int kSmallRoutingK = 128;    // most keys (S + 1) it can take
 
-__global__ __launch_bounds__(64) void routing_small_kernel(
-    const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
-    int* __restrict__ counts, int* __restrict__ offs, int* __restrict__ sorted,
-    int* __restrict__ active, int4* __restrict__ desc, int4* __restrict__ tiles,
-    int* __restrict__ rec, int* __restrict__ meta) {
-  __shared__ int cnt[kSmallRoutingK];        // running count per key, then the count
-  __shared__ int off[kSmallRoutingK];        // segment starts
-  __shared__ int first[kSmallRoutingK];      // first token of each segment
-  __shared__ int tok[kSmallRoutingT];        // sorted token ids
-  constexpr int Q = kSmallRoutingT / 64;
-  const int lane = lane_id(), K = S + 1;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  int nbits = 0;
-  while ((1 << nbits) <= S) ++nbits;
-
-  int v[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int t = 64 * q + lane;
-    v[q] = t < T ? ids[t] : -1;
-  }
-  for (int k = lane; k < kSmallRoutingK; k += 64) cnt[k] = 0;
-  int key[Q], rank[Q], invalid = 0;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int t = 64 * q + lane;
-    const bool ok = v[q] >= 0 && v[q] < S;
-    invalid += (t < T && !ok && v[q] != -1) ? 1 : 0;
-    key[q] = t < T ? (ok ? v[q] : S) : -1;
-  }
-  wave_lds_sync();
-  // ranks, stable in token order; the last lane of each key advances its count
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    if (64 * q < T) {
-      const unsigned long long m = match_key(key[q], nbits);
-      const int base = key[q] >= 0 ? cnt[key[q]] : 0;
-      rank[q] = base + __popcll(m & lt);
-      wave_lds_sync();
-      if (key[q] >= 0 && (m >> lane) == 1ull) cnt[key[q]] = base + __popcll(m);
-      wave_lds_sync();
-    } else {
-      rank[q] = 0;
-    }
-  }
-  // segment starts: lane holds keys 2 lane and 2 lane + 1
-  {
-    const int k0 = 2 * lane, k1 = k0 + 1;
-    const int c0 = k0 < K ? cnt[k0] : 0, c1 = k1 < K ? cnt[k1] : 0;
-    const int incl = wave_inclusive_scan(c0 + c1);
-    const int e0 = incl - c0 - c1;
-    if (k0 < K) { off[k0] = e0; counts[k0] = c0; offs[k0] = e0; }
-    if (k1 < K) { off[k1] = e0 + c0; counts[k1] = c1; offs[k1] = e0 + c0; }
-    if (lane == 63) offs[K] = incl;   // == T
-  }
-  wave_lds_sync();
-  // scatter
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    if (key[q] >= 0) {
-      const int t = 64 * q + lane, pos = off[key[q]] + rank[q];
-      sorted[pos] = t;
-      tok[pos] = t;
-      if (rank[q] == 0) first[key[q]] = t;
-    }
-  }
-  wave_lds_sync();
-  // slot records, whole: (tokens, first position, 0, 0) then the first kRecTokens token
-  // ids, entries past the segment repeating its first token (token 0 if empty)
-  for (int idx = lane; idx < S * (kRecInts / 4); idx += 64) {
-    const int key_ = idx / (kRecInts / 4), part = idx - key_ * (kRecInts / 4);
-    const int c = cnt[key_], st = off[key_];
-    int4 w;
-    if (part == 0) {
-      w = make_int4(c, st, 0, 0);
-    } else {
-      const int pad = c > 0 ? first[key_] : 0, e = 4 * (part - 1);
-      w = make_int4(e < c ? tok[st + e] : pad, e + 1 < c ? tok[st + e + 1] : pad, e + 2 < c ? tok[st + e + 2] : pad,
-                    e + 3 < c ? tok[st + e + 3] : pad);
-    }
-    *reinterpret_cast<int4*>(rec + (size_t)key_ * kRecInts + 4 * part) = w;
-  }
-  // active slots, descriptors and matrix-core tiles, in slot order
-  int nact = 0, ntiles = 0;
-#pragma unroll
-  for (int h = 0; h < kSmallRoutingK / 64; ++h) {
-    const int k = lane + 64 * h;
-    const int c = k < S ? cnt[k] : 0;
-    const unsigned long long ma = __ballot(c > 0);
-    if (c > 0) {
-      const int e = nact + __popcll(ma & lt);
-      active[e] = k;
-      desc[e] = make_int4(k, c, off[k], 0);
-    }
-    nact += __popcll(ma);
-    const int nt = (c > 0 && c >= mfma_min) ? (c + tile_m - 1) / tile_m : 0;
-    const int incl = wave_inclusive_scan(nt);
-    for (int i = 0; i < nt; ++i) {
-      const int e = ntiles + incl - nt + i;
-      if (e < max_tiles) tiles[e] = make_int4(k, off[k] + i * tile_m, min(tile_m, c - i * tile_m), 0);
-    }
-    ntiles += __shfl(incl, 63);
-  }
-  invalid = wave_sum(invalid);
-  if (lane == 0) {
-    meta[kMetaT] = T;
-    meta[kMetaActive] = nact;
-    meta[kMetaInvalid] = invalid;
-    meta[kMetaLora] = off[S];
-    meta[kMetaTiles] = min(ntiles, max_tiles);
-  }
+__global__ __launch_bounds__(64) void routing_small_kernel(const int32_t* __restrict__ ids, int T, int S, int mfma_min,
+                                                           int tile_m, int max_tiles, RouteOut o) {
+  __shared__ __align__(16) int lds[route_wave_lds_ints(kSmallRoutingT / 64, kSmallRoutingK / 64)];
+  route_wave<kSmallRoutingT / 64, kSmallRoutingK / 64>(ids, T, S, mfma_min, tile_m, max_tiles, o, lds);
 }
 
 hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
@@ -330,8 +205,8 @@ hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int ti
   // one wave up to 128 tokens (measured: 64 tokens 5.7 -> 4.8 us; at 256 tokens and
   // 64 slots the workgroup kernel is faster, 6.0 against 7.2 us)
   if (T <= kSmallRoutingT && S + 1 <= kSmallRoutingK) {
-    RAX_LAUNCH(tm, routing_small_kernel, dim3(1), dim3(64), 0u, stream, ids, T, S, mfma_min, tile_m, max_tiles,
-               counts, offs, sorted, active, desc, tiles, rec, meta);
+    const RouteOut o{counts, offs, sorted, active, desc, tiles, rec, meta};
+    RAX_LAUNCH(tm, routing_small_kernel, dim3(1), dim3(64), 0u, stream, ids, T, S, mfma_min, tile_m, max_tiles, o);
     return hipGetLastError();
   }
   // 16 waves for large batches when their histograms leave room (the per-token passes
