@@ -33,7 +33,7 @@ constexpr int kMfmaK = 32;         // k of one bf16 matrix-core step (16x16x32)
 constexpr int kMfmaCols = 128;     // output columns of one matrix-core expand block
 // elements per column of a slot's Bk region: its rank rounded up to 8
 __host__ __device__ constexpr int bk_stride(int rank) { return (rank + 7) / 8 * 8; }
-constexpr int kMfmaColBlocksPerUnit = 4;   // most 128-column blocks of one matrix-core expand unit   // 128-column blocks of one matrix-core expand unit
+constexpr int kMfmaColBlocksPerUnit = 4;   // most 128-column blocks of one matrix-core expand unit
 constexpr int kDefaultMfmaMinSeg = 4;   // segments at least this long use matrix cores (bf16 pools)
 constexpr int kRecInts = 32;       // ints of one slot record: tokens, first position, 2 spare, token ids
 constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
@@ -82,8 +82,9 @@ struct RouteView {
 // at p[s * split_stride + n * n_stride + row * row_stride + j], s < nsplit; the value
 // is the sum of its nsplit partials in split order.  Rows are token indices when
 // by_token is set (the caller's finished [N][T][Rmax] buffer, nsplit = 1), sorted
-// positions otherwise (the pool's workspace [nsplit][N][max_tokens][Rmax]).  Tokens
-// of matrix-core segments always hold their finished value in split 0.
+// positions otherwise (the pool's workspace [nsplit][N][max_tokens][Rk]); every
+// token of a call has all nsplit partials, whether a vector or a matrix-core unit
+// wrote them (the matrix-core units split k into the same nsplit parts).
 struct UView {
   float* p;
   long long split_stride, n_stride, row_stride;

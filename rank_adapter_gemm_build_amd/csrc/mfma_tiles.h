@@ -496,7 +496,6 @@ __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteV
   const int on = P.o[n], dn = P.d[n], c00 = blk0 * kMfmaCols;
   const int4 td = R.tiles[tile];
   const int slot = td.x, p0 = td.y, len = td.z;
-  // the slot-table entry and the tile's token ids in one round trip
   // the slot-table entry and this lane's token id (token lane % 16) in one round trip
   const SlotEntry e = P.table[slot];
   const int tok = R.sorted[p0 + min(lane_id() & 15, len - 1)];
