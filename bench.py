@@ -118,6 +118,7 @@ def upload_sources(torch, W):
         else:  # base output of the caller's own base GEMM (not part of the library)
             W0 = dev(m.W0)
             src["y"] = (src["x"].float() @ W0.float().T).to(src["x"].dtype)
+            src["W0T"] = W0.t().contiguous()   # [k, d], for the base-GEMM overlap measurement
         out.append(src)
     return out
 
@@ -174,6 +175,144 @@ def cpu_baseline(W, seconds: float):
     return {"value": reps * W.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the whole {W.name} batch ({W.T} tokens, {len(W.modules)} module(s)) through "
                       f"oracle.lora_apply (float64 per-token definition), repeated {reps} times in {el:.1f} s"}
+
+
+# ------------------------------------------------------- graph replay, overlap
+def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
+    """Two deployment forms of the same step, timed like the main loop (rotating
+    instances, events around the whole run):
+    - graph: the step of G consecutive instances captured once in a HIP graph
+      (torch.cuda.CUDAGraph) and replayed; the launches then cost no host work;
+    - overlap (workloads with a base weight W0): the caller's base GEMM y = x W0^T
+      (torch.mm into y, one shared W0) followed by the LoRA step, serially on one
+      stream, against the GEMM on stream A and the LoRA step on stream B joined to it
+      (lora_route_linear_join: routing and shrink run beside the GEMM, the expand
+      waits for its event)."""
+    T = W.T
+    M = len(insts)
+    G = min(32, M)
+
+    def step_on(inst, stream):
+        calls = inst.calls
+        pool, xp, ldx, yp, ldy = calls[0]
+        st = lib.lora_route_linear(pool, inst.routing.handle, inst.ids.data_ptr(), T, xp, ldx, yp, ldy, ydt, stream)
+        if st:
+            raise rx.LoraError(st, "lora_route_linear")
+        for pool, xp, ldx, yp, ldy in calls[1:]:
+            st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, stream)
+            if st:
+                raise rx.LoraError(st, "lora_linear")
+
+    res = {}
+    # graphs of G steps each, covering every instance
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(G):
+            step_on(insts[i], side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for g0 in range(0, M - G + 1, G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(g0, g0 + G):
+                step_on(insts[i], cs)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // G)
+    for g in graphs[:2]:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        graphs[r % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    res["graph_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / (reps * G), 3)
+    res["graph_steps_per_replay"] = G
+    del graphs
+    log(f"graph replay: {res['graph_us_per_step']:.2f} us/step ({G} steps per graph)")
+
+    if len(W.modules) == 1 and "W0T" in src[0]:
+        W0T = src[0]["W0T"]
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+        n = args.steps
+        evs = [torch.cuda.Event() for _ in range(M)]
+        done = [torch.cuda.Event() for _ in range(M)]
+        for d in done:
+            d.record(sb)
+
+        def gemm(inst):
+            _, x, y = inst.mods[0]
+            torch.mm(x, W0T, out=y)
+
+        def timed(body):
+            for i in range(min(n, 10)):
+                body(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            sa.wait_stream(torch.cuda.current_stream())
+            sb.wait_stream(torch.cuda.current_stream())
+            for i in range(n):
+                body(i)
+            torch.cuda.current_stream().wait_stream(sa)
+            torch.cuda.current_stream().wait_stream(sb)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        def only_gemm(i):
+            with torch.cuda.stream(sa):
+                gemm(insts[i % M])
+
+        def serial(i):
+            inst = insts[i % M]
+            with torch.cuda.stream(sa):
+                gemm(inst)
+                step_on(inst, sa.cuda_stream)
+
+        def overlap(i):
+            # step i's GEMM waits for step i-1's LoRA result (a next layer's input
+            # depends on it); step i's routing and shrink then run beside the GEMM
+            inst = insts[i % M]
+            ev = evs[i % M]
+            with torch.cuda.stream(sa):
+                sa.wait_event(done[(i - 1) % M])
+                gemm(inst)
+                ev.record(sa)
+            pool, xp, ldx, yp, ldy = inst.calls[0]
+            st = lib.lora_route_linear_join(pool, inst.routing.handle, inst.ids.data_ptr(), T, xp, ldx, yp, ldy, ydt,
+                                            sb.cuda_stream, ev.cuda_event)
+            if st:
+                raise rx.LoraError(st, "lora_route_linear_join")
+            done[i % M].record(sb)
+
+        def overlap_free(i):
+            # throughput form: no dependency between consecutive steps
+            inst = insts[i % M]
+            ev = evs[i % M]
+            with torch.cuda.stream(sa):
+                gemm(inst)
+                ev.record(sa)
+            pool, xp, ldx, yp, ldy = inst.calls[0]
+            st = lib.lora_route_linear_join(pool, inst.routing.handle, inst.ids.data_ptr(), T, xp, ldx, yp, ldy, ydt,
+                                            sb.cuda_stream, ev.cuda_event)
+            if st:
+                raise rx.LoraError(st, "lora_route_linear_join")
+
+        res["base_gemm_us"] = round(timed(only_gemm), 3)
+        res["gemm_then_lora_us_per_step"] = round(timed(serial), 3)
+        res["gemm_beside_lora_us_per_step"] = round(timed(overlap), 3)
+        res["gemm_beside_lora_independent_steps_us_per_step"] = round(timed(overlap_free), 3)
+        res["base_gemm"] = f"torch.mm [{T},{W0T.shape[0]}] x [{W0T.shape[0]},{W0T.shape[1]}] bf16, one W0 for all instances"
+        log(f"base GEMM {res['base_gemm_us']:.2f} us; GEMM then LoRA {res['gemm_then_lora_us_per_step']:.2f} us/step; "
+            f"GEMM beside LoRA (joined) {res['gemm_beside_lora_us_per_step']:.2f} us/step; independent steps "
+            f"{res['gemm_beside_lora_independent_steps_us_per_step']:.2f} us/step")
+    return res
 
 
 # ------------------------------------------------------------------------ main
@@ -295,6 +434,8 @@ def run(args):
     roofline["copy_ceiling_gbps"] = round(copy_gbps, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
 
+    graph_overlap = None if args.no_extras else measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
+
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -309,7 +450,8 @@ def run(args):
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
                   "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
-                  "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest()},
+                  "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest(),
+                  "graph_and_overlap": graph_overlap},
     }
     for inst in insts:
         inst.close()
@@ -331,6 +473,7 @@ def main():
     ap.add_argument("--max-instances", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the graph-replay and base-GEMM overlap timings")
     ap.add_argument("--separate-routing", action="store_true",
                     help="lora_build_routing + lora_linear per step instead of lora_route_linear for the first module")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")

@@ -264,6 +264,23 @@ lora_status lora_route_linear(const lora_pool* pool, lora_routing* routing, cons
                               hipStream_t stream);
 
 /*
+ * lora_linear / lora_route_linear joined to a base projection that another stream
+ * is still computing ([llama.cpp] "为什么低秩增量可以「后加」" and [TRT-LLM] "前向替换": the
+ * LoRA branch and the base output are independent until the final add).  The
+ * routing and the shrink (which read only ids and x) are enqueued on `stream`
+ * at once; then `stream` waits for y_ready (hipStreamWaitEvent), recorded by the
+ * caller after the work that writes the base output into y; then the expand adds
+ * onto y.  y_ready NULL: exactly lora_linear / lora_route_linear.  Results are
+ * bitwise those of the base work followed by the plain call.  Arguments and errors
+ * as lora_linear / lora_route_linear, plus HIP if the wait cannot be enqueued.
+ */
+lora_status lora_linear_join(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                             void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready);
+lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing, const int32_t* token_slot_ids,
+                                   int T, const void* x, int ldx, void* y, int ldy, lora_dtype ydtype,
+                                   hipStream_t stream, hipEvent_t y_ready);
+
+/*
  * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
  * lora_build_routing, lora_shrink, lora_expand and lora_linear launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start

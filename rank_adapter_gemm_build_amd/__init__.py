@@ -47,6 +47,8 @@ SIGNATURES = {
     "lora_expand": (_I, [_P, _P, _VP, _VP, _I, _I, _VP]),
     "lora_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
     "lora_route_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP]),
+    "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
+    "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_timing_enable": (_I, [_I]),
     "lora_timing_report": (_I, [C.POINTER(C.c_double), C.POINTER(C.c_int), _I]),
     "lora_timing_kernel_name": (C.c_char_p, [_I]),
@@ -179,6 +181,18 @@ def lora_route_linear(pool: int, routing: int, ids: int, T: int, x: int, ldx: in
                       stream: int = 0) -> None:
     _check(lib.lora_route_linear(pool, routing, ids or None, T, x or None, ldx, y or None, ldy, ydtype,
                                  stream or None), "lora_route_linear")
+
+
+def lora_linear_join(pool: int, routing: int, x: int, ldx: int, y: int, ldy: int, ydtype: int, stream: int,
+                     y_ready: int) -> None:
+    _check(lib.lora_linear_join(pool, routing, x or None, ldx, y or None, ldy, ydtype, stream or None,
+                                y_ready or None), "lora_linear_join")
+
+
+def lora_route_linear_join(pool: int, routing: int, ids: int, T: int, x: int, ldx: int, y: int, ldy: int,
+                           ydtype: int, stream: int, y_ready: int) -> None:
+    _check(lib.lora_route_linear_join(pool, routing, ids or None, T, x or None, ldx, y or None, ldy, ydtype,
+                                      stream or None, y_ready or None), "lora_route_linear_join")
 
 
 def lora_timing_enable(on: bool) -> None:
@@ -342,3 +356,20 @@ def route_linear(pool: Pool, routing: Routing, ids, x, y, stream=None) -> None:
     lora_route_linear(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
                       y.stride(0), _dt(y), _stream(stream))
     routing.T = T
+
+
+def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=None) -> None:
+    """linear (or route_linear when ids is given) whose expand waits for the torch
+    event y_ready, recorded after the base output was written into y on another
+    stream (see lora_linear_join / lora_route_linear_join)."""
+    if _dt(x) != pool.wdtype:
+        raise TypeError("x dtype must match the pool dtype")
+    ev = y_ready.cuda_event if y_ready is not None else 0
+    if ids is None:
+        lora_linear_join(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y),
+                         _stream(stream), ev)
+    else:
+        T = int(ids.numel())
+        lora_route_linear_join(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
+                               y.stride(0), _dt(y), _stream(stream), ev)
+        routing.T = T

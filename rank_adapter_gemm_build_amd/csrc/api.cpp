@@ -334,6 +334,69 @@ lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const
   return LORA_OK;
 }
 
+// Shrink, then (after the stream waits for y_ready, when given) the expand: the
+// shrink reads only x, so it can run while another stream still writes the base
+// output into y.
+lora_status shrink_join_expand(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                               void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready,
+                               const int32_t* self_ids) {
+  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
+  lora_status st = run_shrink(pool, routing, x, ldx, W, stream, self_ids);
+  if (st != LORA_OK) return st;
+  if (y_ready) {
+    hipError_t e = hipStreamWaitEvent(stream, y_ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "waiting for y_ready");
+  }
+  return run_expand(pool, routing, W, y, ldy, ydtype, stream);
+}
+
+lora_status linear_impl(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx, void* y,
+                        int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready) {
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
+  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  if (routing->T == 0) {
+    // nothing to compute; the join is still honoured, so later work on the stream
+    // stays ordered after y_ready as it would with a non-empty batch
+    if (y_ready) {
+      hipError_t e = hipStreamWaitEvent(stream, y_ready, 0);
+      if (e != hipSuccess) return hip_fail(e, "waiting for y_ready");
+    }
+    return ok();
+  }
+  st = shrink_join_expand(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready, nullptr);
+  return st == LORA_OK ? ok() : st;
+}
+
+lora_status route_linear_impl(const lora_pool* pool, lora_routing* routing, const int32_t* ids, int T,
+                              const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream,
+                              hipEvent_t y_ready) {
+  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
+  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
+  if (T > routing->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, routing->max_tokens);
+  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
+  if (routing->S != pool->S) return fail(LORA_ERR_SHAPE, "routing has %d slots, pool has %d", routing->S, pool->S);
+  if (routing->device != pool->device)
+    return fail(LORA_ERR_INVALID_ARG, "routing on device %d, pool on device %d", routing->device, pool->device);
+  if (T > pool->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds the pool's max_tokens = %d", T, pool->max_tokens);
+  lora_status st = check_x(pool, T, x, ldx);
+  if (st != LORA_OK) return st;
+  if ((st = check_y(pool, T, y, ldy, ydtype)) != LORA_OK) return st;
+  // batches the shrink launch can route itself; others: the routing launch first
+  if (T < 1 || T > rax::kSelfRouteTokens || pool->S + 1 > rax::kSelfRouteKeys) {
+    if ((st = lora_build_routing(routing, ids, T, stream)) != LORA_OK) return st;
+    return linear_impl(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready);
+  }
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  routing->T = T;
+  st = shrink_join_expand(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready, ids);
+  return st == LORA_OK ? ok() : st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -720,44 +783,23 @@ lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, cons
 
 lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
                         void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
-  lora_status st = check_pair(pool, routing);
-  if (st != LORA_OK) return st;
-  if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
-  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
-  if (routing->T == 0) return ok();
-  DeviceGuard g(pool->device);
-  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
-  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
-  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
-  return ok();
+  return linear_impl(pool, routing, x, ldx, y, ldy, ydtype, stream, nullptr);
+}
+
+lora_status lora_linear_join(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
+                             void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready) {
+  return linear_impl(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready);
 }
 
 lora_status lora_route_linear(const lora_pool* pool, lora_routing* routing, const int32_t* ids, int T,
                               const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
-  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
-  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
-  if (T > routing->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, routing->max_tokens);
-  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
-  if (routing->S != pool->S) return fail(LORA_ERR_SHAPE, "routing has %d slots, pool has %d", routing->S, pool->S);
-  if (routing->device != pool->device)
-    return fail(LORA_ERR_INVALID_ARG, "routing on device %d, pool on device %d", routing->device, pool->device);
-  if (T > pool->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds the pool's max_tokens = %d", T, pool->max_tokens);
-  lora_status st = check_x(pool, T, x, ldx);
-  if (st != LORA_OK) return st;
-  if ((st = check_y(pool, T, y, ldy, ydtype)) != LORA_OK) return st;
-  // batches the shrink launch can route itself; others: the routing launch, then lora_linear
-  if (T < 1 || T > rax::kSelfRouteTokens || pool->S + 1 > rax::kSelfRouteKeys) {
-    if ((st = lora_build_routing(routing, ids, T, stream)) != LORA_OK) return st;
-    return lora_linear(pool, routing, x, ldx, y, ldy, ydtype, stream);
-  }
-  DeviceGuard g(pool->device);
-  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-  routing->T = T;
-  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
-  if ((st = run_shrink(pool, routing, x, ldx, W, stream, ids)) != LORA_OK) return st;
-  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
-  return ok();
+  return route_linear_impl(pool, routing, ids, T, x, ldx, y, ldy, ydtype, stream, nullptr);
+}
+
+lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing, const int32_t* ids, int T,
+                                   const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream,
+                                   hipEvent_t y_ready) {
+  return route_linear_impl(pool, routing, ids, T, x, ldx, y, ldy, ydtype, stream, y_ready);
 }
 
 lora_status lora_timing_enable(int on) {
