@@ -253,6 +253,42 @@ def route_by_counting(ids: Sequence[int], S: int) -> Routing:
     return _finish(keys, sorted_ids, counts, S, n_invalid)
 
 
+def route_tokens_per_seq(seq_ids: Sequence[int], S: int, tokens_per_seq: int) -> Routing:
+    """Routing of a batch whose sequences contribute tokens_per_seq tokens each.
+
+    [TRT-LLM] "一次 decode 批次的路由:从请求到 slot_ids" (the speculative-decoding branch of
+    the sorted-indices step, and the counts step): sequence q owns tokens
+    q*p .. q*p + p - 1 (p = tokens_per_seq); the sequences are sorted by slot (the
+    same stable counting sort as at token level), then each sorted sequence index
+    is expanded to its p token indices in order; the per-slot counts are the
+    sequence counts times p and the offsets their cumulative sum.  Reading: an
+    invalid sequence id makes its p tokens no-LoRA and counts them all as invalid
+    (the count is per token, as for per-token ids).
+    """
+    p = int(tokens_per_seq)
+    assert p >= 1
+    seq_keys, seq_invalid = _keys(seq_ids, S)
+    Q = len(seq_keys)
+    # sequence level: counting sort
+    seq_counts = [0] * (S + 1)
+    for q in range(Q):
+        seq_counts[int(seq_keys[q])] += 1
+    cursor, run = [0] * (S + 1), 0
+    for k in range(S + 1):
+        cursor[k] = run
+        run += seq_counts[k]
+    sorted_seqs = [0] * Q
+    for q in range(Q):
+        k = int(seq_keys[q])
+        sorted_seqs[cursor[k]] = q
+        cursor[k] += 1
+    # expansion to tokens
+    token_sorted = [q * p + j for q in sorted_seqs for j in range(p)]
+    counts = [c * p for c in seq_counts]
+    keys = np.repeat(np.asarray(seq_keys, dtype=np.int64), p)
+    return _finish(keys, token_sorted, counts, S, seq_invalid * p)
+
+
 # ------------------------------------------------------------- shrink / expand
 def _slice_offsets(slices: Sequence[int]) -> List[int]:
     """Column offset of each output slice in the packed output ([TRT-LLM] "前向替换":

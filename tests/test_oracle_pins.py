@@ -377,3 +377,41 @@ def test_planted_unstable_sort_is_caught(monkeypatch):
         return R
     monkeypatch.setattr(O, "route_by_counting", unstable)
     assert check_routing_golden() is not None
+
+
+# ---------------------------------------------------- several tokens per sequence
+def test_routing_seq_golden():
+    """Hand-worked cases of the sequence-to-token expansion (tests/golden/routing_seq_cases.json)."""
+    for c in _load("routing_seq_cases.json")["cases"]:
+        R = O.route_tokens_per_seq(c["seq_ids"], c["S"], c["tokens_per_seq"])
+        assert _check_routing(R, c) is None, (c["seq_ids"], _check_routing(R, c))
+
+
+def test_routing_seq_planted_interleave_fails_golden():
+    """A plausible slip, expanding sequence-major as j*Q + q instead of q*p + j, does
+    not match the hand-worked case."""
+    c = _load("routing_seq_cases.json")["cases"][0]
+    p, Q = c["tokens_per_seq"], len(c["seq_ids"])
+    good = O.route_tokens_per_seq(c["seq_ids"], c["S"], p)
+    q_order = [t // p for t in good.sorted_ids[::p]]
+    wrong = [j * Q + q for q in q_order for j in range(p)]
+    assert wrong != c["sorted_ids"]
+
+
+@pytest.mark.parametrize("p", [1, 2, 3])
+@pytest.mark.parametrize("S", [1, 2])
+def test_routing_seq_brute_force(S, p):
+    """Every sequence-id vector of up to 4 sequences: the page's sequence sort plus
+    expansion equals a stable token-level sort of the ids repeated p times, and each
+    sequence's tokens stay contiguous and in order."""
+    vals = list(range(-2, S + 1))
+    for Q in range(0, 5):
+        for seq in itertools.product(vals, repeat=Q):
+            a = O.route_tokens_per_seq(list(seq), S, p)
+            b = O.route_by_sort([i for i in seq for _ in range(p)], S)
+            for f in ("counts", "seg_offsets", "sorted_ids", "active_slots"):
+                assert np.array_equal(getattr(a, f), getattr(b, f)), (seq, p, f)
+            assert a.n_invalid == b.n_invalid
+            srt = list(a.sorted_ids)
+            for i in range(0, len(srt), p):
+                assert srt[i] % p == 0 and srt[i:i + p] == list(range(srt[i], srt[i] + p))
