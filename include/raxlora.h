@@ -200,6 +200,22 @@ lora_status lora_routing_destroy(lora_routing* routing);
 lora_status lora_build_routing(lora_routing* routing, const int32_t* token_slot_ids, int T,
                                hipStream_t stream);
 
+/*
+ * The same routing for num_seqs sequences of tokens_per_seq consecutive tokens each
+ * ([TRT-LLM] "一次 decode 批次的路由": the linear-tree verification batch of speculative
+ * decoding, where each sequence contributes its draft tokens plus one): seq_slot_ids
+ * [num_seqs] (device, int32) holds one slot (or -1) per sequence; token t belongs to
+ * sequence t / tokens_per_seq, so T = num_seqs * tokens_per_seq.  The outputs are
+ * those of lora_build_routing on the per-token ids (each sequence's id repeated
+ * tokens_per_seq times): the page's sequence-level sort expanded to tokens, sequence
+ * q's tokens q p .. q p + p - 1 in order, counts p times the sequence counts; an
+ * invalid sequence id counts its p tokens as invalid.  tokens_per_seq = 1 is
+ * lora_build_routing.  Errors: NULL routing, or ids NULL with T > 0 -> INVALID_ARG;
+ * num_seqs < 0 or tokens_per_seq < 1 -> SHAPE; T > max_tokens -> CAPACITY.
+ */
+lora_status lora_build_routing_seq(lora_routing* routing, const int32_t* seq_slot_ids, int num_seqs,
+                                   int tokens_per_seq, hipStream_t stream);
+
 /* Copy the last routing back to host memory (synchronous; for tests and
  * diagnostics).  counts[S+1], seg_offsets[S+2], sorted_ids[T], active_slots[S]
  * (entries past num_active unspecified); any pointer may be NULL.

@@ -47,6 +47,7 @@ SIGNATURES = {
     "lora_expand": (_I, [_P, _P, _VP, _VP, _I, _I, _VP]),
     "lora_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
     "lora_route_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP]),
+    "lora_build_routing_seq": (_I, [_P, _VP, _I, _I, _VP]),
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_timing_enable": (_I, [_I]),
@@ -295,6 +296,14 @@ class Routing:
         T = int(ids.numel())
         lora_build_routing(self.handle, _ptr(ids) if T else 0, T, _stream(stream))
         self.T = T
+
+    def build_seq(self, seq_ids, tokens_per_seq: int, stream=None) -> None:
+        """seq_ids: device int32 tensor [num_seqs], one slot per sequence of
+        tokens_per_seq consecutive tokens (see lora_build_routing_seq)."""
+        n = int(seq_ids.numel())
+        _check(lib.lora_build_routing_seq(self.handle, _ptr(seq_ids) if n else None, n, int(tokens_per_seq),
+                                          _stream(stream) or None), "lora_build_routing_seq")
+        self.T = n * int(tokens_per_seq)
 
     def query(self):
         import numpy as np

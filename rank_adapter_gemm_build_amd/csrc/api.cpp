@@ -707,17 +707,24 @@ lora_status lora_routing_destroy(lora_routing* r) {
 }
 
 lora_status lora_build_routing(lora_routing* r, const int32_t* ids, int T, hipStream_t stream) {
+  return lora_build_routing_seq(r, ids, T, 1, stream);
+}
+
+lora_status lora_build_routing_seq(lora_routing* r, const int32_t* seq_slot_ids, int num_seqs, int tokens_per_seq,
+                                   hipStream_t stream) {
   if (!r) return fail(LORA_ERR_INVALID_ARG, "routing is NULL");
-  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
-  if (T > r->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, r->max_tokens);
-  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
+  if (num_seqs < 0) return fail(LORA_ERR_SHAPE, "num_seqs = %d < 0", num_seqs);
+  if (tokens_per_seq < 1) return fail(LORA_ERR_SHAPE, "tokens_per_seq = %d < 1", tokens_per_seq);
+  const long long T = (long long)num_seqs * tokens_per_seq;
+  if (T > r->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %lld exceeds max_tokens = %d", T, r->max_tokens);
+  if (T > 0 && !seq_slot_ids) return fail(LORA_ERR_INVALID_ARG, "slot ids are NULL");
   DeviceGuard g(r->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-  hipError_t e = rax::launch_routing(ids, T, r->S, r->mfma_min, r->tile_m, r->max_tiles, r->counts,
-                                     r->offs, r->sorted, r->active, r->desc, r->tiles, r->rec, r->meta, stream,
-                                     timer_for(rax::kKRouting));
+  hipError_t e = rax::launch_routing(seq_slot_ids, (int)T, tokens_per_seq, r->S, r->mfma_min, r->tile_m, r->max_tiles,
+                                     r->counts, r->offs, r->sorted, r->active, r->desc, r->tiles, r->rec, r->meta,
+                                     stream, timer_for(rax::kKRouting));
   if (e != hipSuccess) return hip_fail(e, "routing launch");
-  r->T = T;
+  r->T = (int)T;
   return ok();
 }
 

@@ -122,7 +122,8 @@ struct KTimer {
 enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKFinish, kKernelCount };
 
 // launchers (device code in the .hip files); all return the launch status
-hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
+// ids: one per token (tps = 1) or one per sequence of tps consecutive tokens
+hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm);
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
     static_assert(route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64) >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
     if (b < kXcds) {
       if (b == 0)
-        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
       return;
     }
     b -= kXcds;

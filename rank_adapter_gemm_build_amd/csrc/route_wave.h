@@ -45,8 +45,8 @@ __host__ __device__ constexpr int route_wave_lds_ints(int Q, int KQ) { return 3 
 // an LDS copy from which the 128-byte slot records are written whole, 16 bytes per
 // lane), and the active-slot and tile lists are compacted with ballots in slot order.
 template <int Q, int KQ>
-__device__ __forceinline__ void route_wave(const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m,
-                                           int max_tiles, const RouteOut& o, int* __restrict__ lds) {
+__device__ __forceinline__ void route_wave(const int32_t* __restrict__ ids, int T, int tps, int S, int mfma_min,
+                                           int tile_m, int max_tiles, const RouteOut& o, int* __restrict__ lds) {
   constexpr int KMAX = 64 * KQ;
   int* cnt = lds;                 // [KMAX] running count per key, then the count
   int* off = lds + KMAX;          // [KMAX] segment starts
@@ -61,7 +61,7 @@ __device__ __forceinline__ void route_wave(const int32_t* __restrict__ ids, int 
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int t = 64 * q + lane;
-    v[q] = t < T ? ids[t] : -1;
+    v[q] = t < T ? ids[t / tps] : -1;   // tps tokens per id (sequence)
   }
 #pragma unroll
   for (int i = 0; i < KQ; ++i) cnt[lane + 64 * i] = 0;

@@ -8,6 +8,12 @@
 // the counts, and requests without an adapter go to a sentinel slot after the real ones
 // (section "adapter 池:AdapterSlotManager").
 //
+// Sequences of several tokens (tokens_per_seq = p > 1, the linear-tree verification
+// batch of speculative decoding): the ids are per sequence and token t takes the id of
+// sequence t / p; a stable sort of the tokens is then the page's expansion of the
+// sorted sequences, sequence q's tokens q p .. q p + p - 1 in order (section
+// "一次 decode 批次的路由": token_sorted_ids and counts times tokens_per_seq).
+//
 // One workgroup of 8 waves (16 for large batches).  All ids are read once, in
 // one batch of independent loads, and kept in LDS as 16-bit keys (when the batch
 // fits; else each pass reads them again).  The token range is cut into contiguous
@@ -32,7 +38,7 @@
 namespace rax {
 
 __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
-    const int32_t* __restrict__ ids, int T, int S, int mfma_min, int tile_m, int max_tiles, int stage,
+    const int32_t* __restrict__ ids, int T, int tps, int S, int mfma_min, int tile_m, int max_tiles, int stage,
     int* __restrict__ counts, int* __restrict__ offs, int* __restrict__ sorted,
     int* __restrict__ active, int4* __restrict__ desc, int4* __restrict__ tiles,
     int* __restrict__ rec, int* __restrict__ meta) {
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
 #pragma unroll
       for (int q = 0; q < kRoutingStageBatch; ++q) {
         const int t = b0 + q * NT + tid;
-        v[q] = t < T ? ids[t] : -1;
+        v[q] = t < T ? ids[t / tps] : -1;
       }
 #pragma unroll
       for (int q = 0; q < kRoutingStageBatch; ++q) {
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
   const int t0 = min(T, w * chunk), t1 = min(T, t0 + chunk);
   auto key_of = [&](int t) -> int {
     if (stage) return key16[t];
-    const int id = ids[t];
+    const int id = ids[t / tps];
     return (id >= 0 && id < S) ? id : S;
   };
 
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
     if (t < t1) {
       key = key_of(t);
       if (!stage) {
-        const int id = ids[t];
+        const int id = ids[t / tps];
         invalid += (id < -1 || id >= S) ? 1 : 0;
       }
     }
@@ -193,20 +199,20 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
 constexpr int kSmallRoutingT = 128;    // most tokens of the one-wave kernel
 constexpr int kSmallRoutingK = 128;    // most keys (S + 1) it can take
 
-__global__ __launch_bounds__(64) void routing_small_kernel(const int32_t* __restrict__ ids, int T, int S, int mfma_min,
-                                                           int tile_m, int max_tiles, RouteOut o) {
+__global__ __launch_bounds__(64) void routing_small_kernel(const int32_t* __restrict__ ids, int T, int tps, int S,
+                                                           int mfma_min, int tile_m, int max_tiles, RouteOut o) {
   __shared__ __align__(16) int lds[route_wave_lds_ints(kSmallRoutingT / 64, kSmallRoutingK / 64)];
-  route_wave<kSmallRoutingT / 64, kSmallRoutingK / 64>(ids, T, S, mfma_min, tile_m, max_tiles, o, lds);
+  route_wave<kSmallRoutingT / 64, kSmallRoutingK / 64>(ids, T, tps, S, mfma_min, tile_m, max_tiles, o, lds);
 }
 
-hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int tile_m, int max_tiles,
+hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm) {
   // one wave up to 128 tokens (measured: 64 tokens 5.7 -> 4.8 us; at 256 tokens and
   // 64 slots the workgroup kernel is faster, 6.0 against 7.2 us)
   if (T <= kSmallRoutingT && S + 1 <= kSmallRoutingK) {
     const RouteOut o{counts, offs, sorted, active, desc, tiles, rec, meta};
-    RAX_LAUNCH(tm, routing_small_kernel, dim3(1), dim3(64), 0u, stream, ids, T, S, mfma_min, tile_m, max_tiles, o);
+    RAX_LAUNCH(tm, routing_small_kernel, dim3(1), dim3(64), 0u, stream, ids, T, tps, S, mfma_min, tile_m, max_tiles, o);
     return hipGetLastError();
   }
   // 16 waves for large batches when their histograms leave room (the per-token passes
@@ -218,7 +224,7 @@ hipError_t launch_routing(const int32_t* ids, int T, int S, int mfma_min, int ti
   const size_t keys = ((size_t)T * sizeof(uint16_t) + 15) / 16 * 16;
   const int stage = base + keys <= 65536 ? 1 : 0;
   const size_t lds = base + (stage ? keys : 0);
-  RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(64 * nw), (uint32_t)lds, stream, ids, T, S,
+  RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(64 * nw), (uint32_t)lds, stream, ids, T, tps, S,
              mfma_min, tile_m, max_tiles, stage, counts, offs, sorted, active, desc, tiles, rec, meta);
   return hipGetLastError();
 }
