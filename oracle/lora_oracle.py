@@ -384,6 +384,33 @@ def lora_apply(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int], i
     return y
 
 
+def embedding_apply(vocab_ids: Sequence[int], y_base, adapters: Dict[int, Adapter], vocab: int,
+                    ids: Sequence[int], S: int, wdtype: str) -> np.ndarray:
+    """Embedding LoRA: y_t = y_base_t + s * B A[:, v_t] per token, in float64.
+
+    [llama.cpp] "嵌入层:查表后再加增量": the token embedding is a table lookup, so the
+    branch takes each token's r-vector out of A by its vocabulary id (get_rows), lifts
+    it to the output width with B and adds the scaled result onto the lookup;
+    "适配器文件:形状约定" (token_embd exception): A is [r, V], its columns indexed by
+    vocabulary id, B is [d, r].  Each adapter has one slice: A[0] [r, V], B[0] [d, r].
+    Reading: a vocabulary id outside [0, V) contributes zero (the row still gets
+    y + 0); no-LoRA tokens and empty or zero-scale slots leave their rows unchanged.
+    """
+    y = np.array(y_base, dtype=np.float64, copy=True)
+    keys, _ = _keys(ids, S)
+    for t in range(len(keys)):
+        ad = adapters.get(int(keys[t])) if keys[t] < S else None
+        if not _contributes(ad) or ad.A[0] is None:
+            continue
+        A = np.asarray(ad.A[0], dtype=np.float64)
+        assert A.shape == (ad.rank, vocab)
+        v = int(vocab_ids[t])
+        u = A[:, v] if 0 <= v < vocab else np.zeros(ad.rank)
+        Bn, s_eff = effective_b(ad, 0, wdtype)
+        y[t] = y[t] + s_eff * (Bn @ u)
+    return y
+
+
 def lora_apply_grouped(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int],
                        ids: Sequence[int], S: int, wdtype: str) -> np.ndarray:
     """Second formulation: the naive loop over the adapters present in the batch.

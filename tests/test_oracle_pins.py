@@ -415,3 +415,36 @@ def test_routing_seq_brute_force(S, p):
             srt = list(a.sorted_ids)
             for i in range(0, len(srt), p):
                 assert srt[i] % p == 0 and srt[i:i + p] == list(range(srt[i], srt[i] + p))
+
+
+# ---------------------------------------------------------------- embedding LoRA
+def test_embedding_golden():
+    """Hand-worked embedding case (tests/golden/embedding_case.json)."""
+    g = _load("embedding_case.json")
+    ad = O.Adapter(rank=g["rank"], A=[np.array(g["A"], dtype=np.float64)], B=[np.array(g["B"], dtype=np.float64)],
+                   alpha=g["alpha"])
+    y = O.embedding_apply(g["vocab_ids"], np.array(g["y_base"], dtype=np.float64), {0: ad}, g["vocab"],
+                          g["slot_ids"], g["S"], "f32")
+    assert np.array_equal(y, np.array(g["y"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("premultiply", [False, True])
+def test_embedding_is_linear_lora_on_one_hot_inputs(premultiply):
+    """get_rows of A by vocabulary id is A times a one-hot input: the embedding branch
+    equals the linear branch (the per-token definition) on one-hot rows, exactly; a
+    vocabulary id outside the table is an all-zero row."""
+    rng = np.random.default_rng(7)
+    S, V, d, T = 5, 40, 24, 60
+    ranks = {0: 3, 1: 8, 2: 1, 4: 5}
+    ads = {s: O.Adapter(rank=r, A=[rng.standard_normal((r, V))], B=[rng.standard_normal((d, r))],
+                        alpha=float(2 * r + s), premultiply=premultiply) for s, r in ranks.items()}
+    ids = rng.integers(-1, S + 1, size=T)
+    vocab = rng.integers(-2, V + 2, size=T)
+    yb = rng.standard_normal((T, d))
+    onehot = np.zeros((T, V))
+    for t, v in enumerate(vocab):
+        if 0 <= v < V:
+            onehot[t, v] = 1.0
+    got = O.embedding_apply(vocab, yb, ads, V, ids, S, "f32")
+    ref = O.lora_apply(onehot, yb, ads, [d], ids, S, "f32", max_rank=8)
+    assert np.array_equal(got, ref)
