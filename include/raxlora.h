@@ -129,6 +129,21 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
                              int in_features, const int* slice_out, int num_slices,
                              lora_dtype wdtype, int max_tokens);
 
+/*
+ * A pool for the token embedding ([llama.cpp] "嵌入层:查表后再加增量": the lookup gets
+ * a low-rank delta, get_rows of A by token id lifted by B; "token_embd" shape
+ * contract: A is [r, V], B is [d, r]).  One slice of width d; vocab = V.  Adapters
+ * are registered with lora_register_adapter as for other pools (A_slices[0] is
+ * [rank, vocab], B_slices[0] is [d, rank]); the pool stores A transposed, one
+ * contiguous row of max_lora_rank values per vocabulary id, so
+ * lora_pool_read_slot returns A_host as [vocab, max_lora_rank].  Used only with
+ * lora_embedding (and lora_expand); lora_shrink, lora_linear and lora_route_linear
+ * reject it (INVALID_ARG).  Errors as lora_pool_create, except that vocab needs no
+ * alignment and no upper bound (it is not a contraction length).
+ */
+lora_status lora_embedding_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank, int vocab,
+                                       int d, lora_dtype wdtype, int max_tokens);
+
 /* Free the pool.  All work that uses it must have completed.  NULL is a no-op. */
 lora_status lora_pool_destroy(lora_pool* pool);
 
@@ -168,7 +183,8 @@ lora_status lora_pool_slot_info(const lora_pool* pool, int slot, int* rank, floa
                                 uint32_t* slice_mask, uint64_t* a_offset, uint64_t* bt_offset);
 
 /* Copy a slot's stored slice back to host memory (synchronous; for tests):
- * A_host [max_lora_rank, in_features] and Bt_host [max_lora_rank, slice_out[slice]]
+ * A_host [max_lora_rank, in_features] (embedding pools: [vocab, max_lora_rank])
+ * and Bt_host [max_lora_rank, slice_out[slice]]
  * (B transposed, rank-major), both in the pool dtype, rows >= rank zero.
  * Either pointer may be NULL. */
 lora_status lora_pool_read_slot(const lora_pool* pool, int slot, int slice, void* A_host,
@@ -297,14 +313,28 @@ lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing,
                                    hipStream_t stream, hipEvent_t y_ready);
 
 /*
+ * Embedding LoRA onto the caller's lookup result ([llama.cpp] "嵌入层:查表后再加增量"):
+ *   y[t][i] = round_y( y[t][i] + s * sum_j B_slot(t)[i][j] * A_slot(t)[j][vocab_ids[t]] )
+ * for LoRA tokens of the routing (built from the tokens' slot ids as usual).
+ * vocab_ids: device int32 [T], the tokens' vocabulary ids; an id outside
+ * [0, vocab) contributes zero (its row is rewritten as y + 0).  Two launches: a
+ * gather of each token's row of A into the pool's workspace, then the expand of
+ * lora_linear.  y as for lora_expand; the pool must come from
+ * lora_embedding_pool_create (else INVALID_ARG).  Errors as lora_expand, plus
+ * INVALID_ARG for vocab_ids NULL with T > 0.
+ */
+lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, const int32_t* vocab_ids, void* y,
+                           int ldy, lora_dtype ydtype, hipStream_t stream);
+
+/*
  * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
- * lora_build_routing, lora_shrink, lora_expand and lora_linear launch is started
+ * the routing, shrink, expand, linear and embedding calls launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start
  * and end, on the stream it runs on.  lora_timing_report waits for the recorded
  * events, writes per kernel id (0 routing, 1 shrink, 2 expand, 3 finish_u: the
- * pass of lora_shrink that adds the k-split partial sums into the caller's u;
- * the shrink and expand launches cover both short and long segments) the summed
- * milliseconds and the
+ * pass of lora_shrink that adds the k-split partial sums into the caller's u,
+ * 4 gather: the embedding rows of lora_embedding; the shrink and expand launches
+ * cover both short and long segments) the summed milliseconds and the
  * number of launches into total_ms[0..max_kernels) and launches[0..max_kernels), and
  * clears the record.  lora_timing_kernel_name gives the name of an id ("" if none).
  * Errors: INVALID_ARG for NULL arrays with max_kernels > 0; HIP if an event fails.

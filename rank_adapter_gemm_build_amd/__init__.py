@@ -48,6 +48,8 @@ SIGNATURES = {
     "lora_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
     "lora_route_linear": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP]),
     "lora_build_routing_seq": (_I, [_P, _VP, _I, _I, _VP]),
+    "lora_embedding_pool_create": (_I, [C.POINTER(_P), _I, _I, _I, _I, _I, _I, _I]),
+    "lora_embedding": (_I, [_P, _P, _VP, _VP, _I, _I, _VP]),
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_timing_enable": (_I, [_I]),
@@ -55,7 +57,7 @@ SIGNATURES = {
     "lora_timing_kernel_name": (C.c_char_p, [_I]),
 }
 
-KERNEL_NAMES = ["routing", "shrink", "expand", "finish_u"]
+KERNEL_NAMES = ["routing", "shrink", "expand", "finish_u", "gather"]
 
 
 def _load():
@@ -106,6 +108,19 @@ def lora_compute_scale(alpha: float, rank: int, rslora: bool, adapter_scale: flo
     _check(lib.lora_compute_scale(alpha, rank, int(bool(rslora)), adapter_scale, C.byref(out)),
            "lora_compute_scale")
     return out.value
+
+
+def lora_embedding_pool_create(device: int, max_slots: int, max_lora_rank: int, vocab: int, d: int, wdtype: int,
+                               max_tokens: int) -> int:
+    h = C.c_void_p()
+    _check(lib.lora_embedding_pool_create(C.byref(h), device, max_slots, max_lora_rank, vocab, d, wdtype, max_tokens),
+           "lora_embedding_pool_create")
+    return h.value
+
+
+def lora_embedding(pool: int, routing: int, vocab_ids: int, y: int, ldy: int, ydtype: int, stream: int = 0) -> None:
+    _check(lib.lora_embedding(pool, routing, vocab_ids or None, y or None, ldy, ydtype, stream or None),
+           "lora_embedding")
 
 
 def lora_pool_create(device: int, max_slots: int, max_lora_rank: int, in_features: int,
@@ -230,12 +245,21 @@ class Pool:
     """One target module's adapter slots (owns the device pool)."""
 
     def __init__(self, device: int, max_slots: int, max_lora_rank: int, in_features: int,
-                 slice_out: Sequence[int], wdtype: int, max_tokens: int):
+                 slice_out: Sequence[int], wdtype: int, max_tokens: int, embedding: bool = False):
+        """embedding: a token-embedding pool (in_features = vocabulary size, one slice;
+        see lora_embedding_pool_create)."""
         self.device, self.S, self.Rmax, self.k = device, max_slots, max_lora_rank, in_features
         self.slices = list(slice_out)
         self.D = sum(self.slices)
-        self.wdtype, self.max_tokens = wdtype, max_tokens
-        self.handle = lora_pool_create(device, max_slots, max_lora_rank, in_features, slice_out, wdtype, max_tokens)
+        self.wdtype, self.max_tokens, self.embedding = wdtype, max_tokens, embedding
+        if embedding:
+            if len(self.slices) != 1:
+                raise ValueError("an embedding pool has one slice")
+            self.handle = lora_embedding_pool_create(device, max_slots, max_lora_rank, in_features, self.slices[0],
+                                                     wdtype, max_tokens)
+        else:
+            self.handle = lora_pool_create(device, max_slots, max_lora_rank, in_features, slice_out, wdtype,
+                                           max_tokens)
 
     def register(self, slot: int, A_slices, B_slices, alpha: float, rank: int, rslora: bool = False,
                  adapter_scale: float = 1.0, premultiply: bool = False, device_src: Optional[bool] = None,
@@ -266,7 +290,7 @@ class Pool:
     def read_slot(self, slot: int, slice_: int):
         import numpy as np
         dt = np.uint16 if self.wdtype == LORA_BF16 else np.float32
-        A = np.zeros((self.Rmax, self.k), dtype=dt)
+        A = np.zeros((self.k, self.Rmax) if self.embedding else (self.Rmax, self.k), dtype=dt)
         Bt = np.zeros((self.Rmax, self.slices[slice_]), dtype=dt)
         lora_pool_read_slot(self.handle, slot, slice_, A.ctypes.data, Bt.ctypes.data)
         return A, Bt
@@ -382,3 +406,8 @@ def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=No
         lora_route_linear_join(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
                                y.stride(0), _dt(y), _stream(stream), ev)
         routing.T = T
+
+
+def embedding(pool: Pool, routing: Routing, vocab_ids, y, stream=None) -> None:
+    """y += s B_slot A_slot[:, vocab_id] per LoRA token (see lora_embedding)."""
+    lora_embedding(pool.handle, routing.handle, _ptr(vocab_ids), _ptr(y), y.stride(0), _dt(y), _stream(stream))

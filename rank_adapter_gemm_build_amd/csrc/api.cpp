@@ -26,6 +26,7 @@ struct lora_pool {
   int mblk0[LORA_MAX_SLICES + 1] = {0};
   lora_dtype wdtype = LORA_BF16;
   size_t esize = 2;
+  bool embedding = false;     // A stored [S][V][Rmax] (rows by vocabulary id); k = V
   void* A = nullptr;
   void* Bt = nullptr;
   void* Bk = nullptr;
@@ -139,7 +140,7 @@ rax::KTimer timer_for(int kernel) {
   return t;
 }
 
-const char* const kKernelNames[rax::kKernelCount] = {"routing", "shrink", "expand", "finish_u"};
+const char* const kKernelNames[rax::kKernelCount] = {"routing", "shrink", "expand", "finish_u", "gather"};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -227,6 +228,7 @@ lora_status check_pair(const lora_pool* pool, const lora_routing* routing) {
 }
 
 lora_status check_x(const lora_pool* pool, int T, const void* x, int ldx) {
+  if (pool->embedding) return fail(LORA_ERR_INVALID_ARG, "embedding pool: use lora_embedding");
   if (T > 0 && !x) return fail(LORA_ERR_INVALID_ARG, "x is NULL");
   if (ldx < pool->k) return fail(LORA_ERR_SHAPE, "ldx = %d < in_features = %d", ldx, pool->k);
   if (ldx % 8 != 0 || !aligned16(x)) return fail(LORA_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
@@ -440,9 +442,9 @@ lora_status lora_compute_scale(float alpha, int rank, int rslora, float adapter_
   return ok();
 }
 
-lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank,
-                             int in_features, const int* slice_out, int num_slices,
-                             lora_dtype wdtype, int max_tokens) {
+static lora_status create_pool(lora_pool** out, int device, int max_slots, int max_lora_rank, int in_features,
+                               const int* slice_out, int num_slices, lora_dtype wdtype, int max_tokens,
+                               bool embedding) {
   if (!out || !slice_out) return fail(LORA_ERR_INVALID_ARG, "out and slice_out must not be NULL");
   *out = nullptr;
   if (max_slots < 1 || max_slots > LORA_MAX_SLOTS)
@@ -461,8 +463,9 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
     D += slice_out[n];
   }
   if (D > (1LL << 30)) return fail(LORA_ERR_SHAPE, "total output width too large");
-  if (in_features % 8) return fail(LORA_ERR_ALIGN, "in_features %d not a multiple of 8", in_features);
-  if (in_features > LORA_MAX_IN_FEATURES)
+  // the shrink's 16-byte chunks need k % 8 == 0 and bound k; an embedding pool has no shrink
+  if (!embedding && in_features % 8) return fail(LORA_ERR_ALIGN, "in_features %d not a multiple of 8", in_features);
+  if (!embedding && in_features > LORA_MAX_IN_FEATURES)
     return fail(LORA_ERR_SHAPE, "in_features %d above LORA_MAX_IN_FEATURES = %d", in_features, LORA_MAX_IN_FEATURES);
 
   lora_status st = check_device(device);
@@ -480,6 +483,7 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   p->max_tokens = max_tokens;
   p->wdtype = wdtype;
   p->esize = wdtype == LORA_BF16 ? 2 : 4;
+  p->embedding = embedding;
   int o = 0, tiles = 0, mblocks = 0;
   for (int n = 0; n < num_slices; ++n) {
     p->d[n] = slice_out[n];
@@ -500,6 +504,7 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
   const size_t bk_bytes = (size_t)max_slots * p->Rk * p->D * p->esize;
   choose_split(p);
+  if (embedding) p->nsplit = p->ns = 1;   // the gathered u is final: one part
   const size_t ws_bytes = (size_t)p->nsplit * num_slices * max_tokens * p->Rk * sizeof(float);
   hipError_t e;
   if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
@@ -519,6 +524,19 @@ lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max
   }
   *out = p;
   return ok();
+}
+
+lora_status lora_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank,
+                             int in_features, const int* slice_out, int num_slices,
+                             lora_dtype wdtype, int max_tokens) {
+  return create_pool(out, device, max_slots, max_lora_rank, in_features, slice_out, num_slices, wdtype, max_tokens,
+                     false);
+}
+
+lora_status lora_embedding_pool_create(lora_pool** out, int device, int max_slots, int max_lora_rank, int vocab,
+                                       int d, lora_dtype wdtype, int max_tokens) {
+  const int slice_out[1] = {d};
+  return create_pool(out, device, max_slots, max_lora_rank, vocab, slice_out, 1, wdtype, max_tokens, true);
 }
 
 lora_status lora_pool_destroy(lora_pool* p) {
@@ -586,7 +604,8 @@ lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* 
     char* Bk_dst = static_cast<char*>(pool->Bk) +
                    ((size_t)slot * pool->D * pool->Rk + (size_t)pool->o[n] * rax::bk_stride(rank)) * es;
     e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bt_dst, Bk_dst, rank, pool->Rmax,
-                               pool->Rk, pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, stream);
+                               pool->Rk, pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, pool->embedding ? 1 : 0,
+                               stream);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "pack launch"); }
   }
   const SlotEntry entry{rank, premul ? 1.0f : s, mask, 0};
@@ -807,6 +826,25 @@ lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing,
                                    const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream,
                                    hipEvent_t y_ready) {
   return route_linear_impl(pool, routing, ids, T, x, ldx, y, ldy, ydtype, stream, y_ready);
+}
+
+lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, const int32_t* vocab_ids, void* y,
+                           int ldy, lora_dtype ydtype, hipStream_t stream) {
+  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
+  if (!pool->embedding) return fail(LORA_ERR_INVALID_ARG, "not an embedding pool (lora_embedding_pool_create)");
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
+  if (routing->T > 0 && !vocab_ids) return fail(LORA_ERR_INVALID_ARG, "vocab_ids is NULL");
+  if (routing->T == 0) return ok();
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const rax::UView W = workspace_view(pool, 1);
+  hipError_t e = rax::launch_embed_gather(pool->wdtype, pool_view(pool), route_view(routing), vocab_ids, pool->k, W,
+                                          stream, timer_for(rax::kKGather));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
 }
 
 lora_status lora_timing_enable(int on) {

@@ -119,16 +119,17 @@ struct KTimer {
 };
 
 // kernels the timing facility reports, in this order
-enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKFinish, kKernelCount };
+enum KernelId { kKRouting = 0, kKShrink, kKExpand, kKFinish, kKGather, kKernelCount };
 
 // launchers (device code in the .hip files); all return the launch status
 // ids: one per token (tps = 1) or one per sequence of tps consecutive tokens
 hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm);
+// a_by_row: store A transposed, [k][Rmax] (embedding pools: k = vocabulary size)
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
                              void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
-                             int D, float scale, int premultiply, hipStream_t stream);
+                             int D, float scale, int premultiply, int a_by_row, hipStream_t stream);
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream);
 // Output buffers of a routing (device memory; sizes as in RouteView).
 struct RouteOut {
@@ -155,6 +156,10 @@ hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, cons
 hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
                          const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,
                          const KTimer& tm);
+// embedding pools: u (workspace split 0, rows by sorted position) = the rows of the
+// transposed A [V][Rmax] of each token's slot at its vocabulary id
+hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R, const int32_t* vocab_ids, int V,
+                               const UView& W, hipStream_t stream, const KTimer& tm);
 // finished u of a standalone shrink: workspace partials -> caller's [N][T][Rmax]
 hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W, const UView& U,
                            const Plan& plan, hipStream_t stream, const KTimer& tm);

@@ -43,6 +43,8 @@
 // replaced by zero) and issued as one batch before the math.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device_util.h"
 #include "decode_units.h"
 #include "mfma_tiles.h"
@@ -280,6 +282,54 @@ hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W
   (void)plan;
   if (W.nsplit < 1 || W.nsplit > kMaxSplit || W.by_token || !U.by_token) return hipErrorInvalidValue;
   RAX_LAUNCH(tm, finish_u_kernel, dim3(R.S), dim3(256), 0u, stream, P, R, W, U);
+  return hipGetLastError();
+}
+
+// Embedding LoRA (page "llama.cpp 源码完全拆解(十六)", section "嵌入层:查表后再加增量":
+// get_rows takes each token's r-vector out of A by its vocabulary id, then B lifts it
+// to the output width): the workspace row of sorted position p < offs[S] (split 0,
+// slice 0) gets A^T[slot][v][j] for j < rank and a vocabulary id v in [0, V), else
+// 0, for j < Rk; the expand then runs on it as on a finished shrink.  The slot of a
+// position comes from the segment offsets, staged in LDS (binary search).  One thread
+// per (position, rank) value, so a token's rank values are one contiguous read.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_gather_kernel(PoolView P, RouteView R, const int32_t* __restrict__ vocab_ids,
+                                                           int V, UView W) {
+  extern __shared__ int offs[];   // [S + 2]
+  for (int i = threadIdx.x; i < R.S + 2; i += blockDim.x) offs[i] = R.offs[i];
+  __syncthreads();
+  const long long n = (long long)offs[R.S] * P.Rk;   // LoRA tokens come first
+  const T* __restrict__ At = static_cast<const T*>(P.A);
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int p = (int)(idx / P.Rk), j = (int)(idx - (long long)p * P.Rk);
+    int lo = 0, hi = R.S - 1;   // the last slot whose segment starts at or before p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offs[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const SlotEntry e = P.table[lo];
+    const int v = vocab_ids[R.sorted[p]];
+    float val = 0.f;
+    if (j < e.rank && v >= 0 && v < V) {
+      const T a = At[((size_t)lo * P.k + v) * P.Rmax + j];
+      if constexpr (sizeof(T) == 2) val = __uint_as_float((uint32_t)a << 16); else val = a;
+    }
+    W.p[(long long)p * W.row_stride + j] = val;
+  }
+}
+
+hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R, const int32_t* vocab_ids, int V,
+                               const UView& W, hipStream_t stream, const KTimer& tm) {
+  if (W.by_token || W.nsplit != 1 || W.row_stride < P.Rk || P.N != 1 || P.k != V || R.T < 1 || !vocab_ids)
+    return hipErrorInvalidValue;
+  const long long n = (long long)R.T * P.Rk;   // at least the LoRA tokens' values
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  const uint32_t lds = (uint32_t)((R.S + 2) * sizeof(int));
+  if (wdtype == LORA_BF16)
+    RAX_LAUNCH(tm, embed_gather_kernel<uint16_t>, dim3(blocks), dim3(256), lds, stream, P, R, vocab_ids, V, W);
+  else
+    RAX_LAUNCH(tm, embed_gather_kernel<float>, dim3(blocks), dim3(256), lds, stream, P, R, vocab_ids, V, W);
   return hipGetLastError();
 }
 

@@ -46,16 +46,33 @@ __global__ void pack_b_kernel(const T* __restrict__ src, T* __restrict__ bt, T* 
   }
 }
 
+// Embedding pools: A [rank][V] (columns by vocabulary id) -> [V][Rmax], so a token's
+// r values are one contiguous row (the get_rows layout); entries j >= rank zero.
+template <typename T>
+__global__ void pack_a_t_kernel(const T* __restrict__ src, T* __restrict__ dst, int rank, int Rmax, long long V) {
+  const long long n_all = V * Rmax;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n_all;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long v = e / Rmax;
+    const int j = (int)(e - v * Rmax);
+    dst[e] = (src != nullptr && j < rank) ? src[(long long)j * V + v] : T(0);
+  }
+}
+
 __global__ void set_slot_kernel(SlotEntry* table, int slot, SlotEntry entry) { table[slot] = entry; }
 
 template <typename T>
 static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* Bt_dst, void* Bk_dst,
                        int rank, int Rmax, int Rk, int k, int d, int D, float scale, int premultiply,
-                       hipStream_t stream) {
+                       int a_by_row, hipStream_t stream) {
   const long long n_all = (long long)Rmax * k, n_src = (long long)rank * k;
   const int blocks_a = (int)((n_all + 255) / 256 < 4096 ? (n_all + 255) / 256 : 4096);
-  hipLaunchKernelGGL(pack_a_kernel<T>, dim3(blocks_a), dim3(256), 0, stream,
-                     static_cast<const T*>(A_src), static_cast<T*>(A_dst), n_src, n_all);
+  if (a_by_row)
+    hipLaunchKernelGGL(pack_a_t_kernel<T>, dim3(blocks_a), dim3(256), 0, stream,
+                       static_cast<const T*>(A_src), static_cast<T*>(A_dst), rank, Rmax, (long long)k);
+  else
+    hipLaunchKernelGGL(pack_a_kernel<T>, dim3(blocks_a), dim3(256), 0, stream,
+                       static_cast<const T*>(A_src), static_cast<T*>(A_dst), n_src, n_all);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_b_kernel<T>, dim3((d + 255) / 256), dim3(256), 0, stream,
@@ -66,12 +83,12 @@ static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* 
 
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
                              void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
-                             int D, float scale, int premultiply, hipStream_t stream) {
+                             int D, float scale, int premultiply, int a_by_row, hipStream_t stream) {
   if (wdtype == LORA_BF16)
     return pack<uint16_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
-                          premultiply, stream);
+                          premultiply, a_by_row, stream);
   return pack<float>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
-                     premultiply, stream);
+                     premultiply, a_by_row, stream);
 }
 
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream) {
