@@ -236,6 +236,34 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
     del graphs
     log(f"graph replay: {res['graph_us_per_step']:.2f} us/step ({G} steps per graph)")
 
+    # speculative-decoding batch of the same size: T / 4 sequences of 4 tokens, the
+    # routing built from one slot id per sequence (lora_build_routing_seq)
+    if T % 4 == 0:
+        p = 4
+        seq = torch.from_numpy(W.ids[: T // p].astype("int32")).cuda()
+
+        def seq_step(i):
+            inst = insts[i % M]
+            st = lib.lora_build_routing_seq(inst.routing.handle, seq.data_ptr(), T // p, p, torch.cuda.current_stream().cuda_stream)
+            if st:
+                raise rx.LoraError(st, "lora_build_routing_seq")
+            for pool, xp, ldx, yp, ldy in inst.calls:
+                st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, torch.cuda.current_stream().cuda_stream)
+                if st:
+                    raise rx.LoraError(st, "lora_linear")
+
+        for i in range(10):
+            seq_step(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            seq_step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res["seq_routing_step_us"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 3)
+        res["seq_routing_step"] = f"lora_build_routing_seq ({T // p} sequences x {p} tokens) + lora_linear per module"
+        log(f"sequence-routed step: {res['seq_routing_step_us']:.2f} us/step")
+
     if len(W.modules) == 1 and "W0T" in src[0]:
         W0T = src[0]["W0T"]
         sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
@@ -312,6 +340,76 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
         log(f"base GEMM {res['base_gemm_us']:.2f} us; GEMM then LoRA {res['gemm_then_lora_us_per_step']:.2f} us/step; "
             f"GEMM beside LoRA (joined) {res['gemm_beside_lora_us_per_step']:.2f} us/step; independent steps "
             f"{res['gemm_beside_lora_independent_steps_us_per_step']:.2f} us/step")
+    return res
+
+
+# ------------------------------------------------------------- embedding LoRA
+def measure_embedding(torch, rx, lib, W, args, vocab=32000):
+    """Embedding LoRA on the workload's batch (one module): the same slots, ranks,
+    ids and output width, A drawn as [r, vocab] per slot (seeded), vocabulary ids
+    uniform; one step = lora_build_routing + lora_embedding (gather + expand) onto a
+    resident bf16 lookup result.  Rotates over enough instances to exceed the
+    256 MB Infinity Cache.  Algorithmic bytes per step: per LoRA token its rank row
+    (r x 2 B) and the output row read and written (2 x d x 2 B), per active slot its
+    B (r x d x 2 B)."""
+    import numpy as np
+    m = W.modules[0]
+    d, T = m.slices[0], W.T
+    if len(m.slices) != 1 or W.dtype != "bf16":
+        return None
+    rng = np.random.default_rng(4242)
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    counts = np.bincount(keys, minlength=W.S + 1)
+    step_bytes = sum(int(counts[s]) * (r * 2 + 4 * d) + r * d * 2 for s, r in W.ranks.items() if counts[s] > 0)
+    per_inst = W.S * W.Rmax * vocab * 2 + W.S * W.Rmax * d * 4 + T * d * 2
+    M = max(2, min(64, int(np.ceil(1.5 * 2 ** 30 / per_inst))))
+    ids = torch.from_numpy(W.ids.astype(np.int32)).cuda()
+    insts = []
+    for i in range(M):
+        pool = rx.Pool(0, W.S, W.Rmax, vocab, [d], rx.LORA_BF16, T, embedding=True)
+        for s, r in W.ranks.items():
+            A = torch.randn((r, vocab), device="cuda").to(torch.bfloat16)
+            B = (torch.randn((d, r), device="cuda") / float(np.sqrt(r))).to(torch.bfloat16)
+            pool.register(s, [A], [B], W.alpha[s], r, W.rslora, W.adapter_scale, device_src=True)
+        R = rx.Routing(0, T, W.S)
+        v = torch.from_numpy(rng.integers(0, vocab, size=T).astype(np.int32)).cuda()
+        y = torch.randn((T, d), device="cuda").to(torch.bfloat16)
+        insts.append((pool, R, v, y))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        pool, R, v, y = insts[i % M]
+        st = lib.lora_route_embedding(pool.handle, R.handle, ids.data_ptr(), T, v.data_ptr(), y.data_ptr(), y.stride(0),
+                                      rx.LORA_BF16, stream)
+        if st:
+            raise rx.LoraError(st, "lora_route_embedding")
+
+    for i in range(min(args.warmup, 10) + M):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    rx.lora_timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    rep = rx.lora_timing_report()
+    rx.lora_timing_enable(False)
+    kern = {k: round(1e3 * ms / n, 3) for k, (ms, n) in rep.items() if n}
+    for pool, R, _, _ in insts:
+        pool.close()
+        R.close()
+    res = {"us_per_step": round(us, 3), "tokens_per_s": round(T / (us * 1e-6), 1),
+           "step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (us * 1e-6) / 1e9, 2),
+           "kernels_avg_us": kern, "vocab": vocab, "rotation_instances": M,
+           "step": "lora_route_embedding (routing + gather + expand), bf16, same slots/ids as the workload"}
+    log(f"embedding LoRA: {us:.2f} us/step, kernels {kern}")
     return res
 
 
@@ -435,6 +533,10 @@ def run(args):
     roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
 
     graph_overlap = None if args.no_extras else measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
+    for inst in insts:
+        inst.close()
+    insts = []
+    embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
 
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
@@ -451,7 +553,7 @@ def run(args):
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
                   "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
                   "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest(),
-                  "graph_and_overlap": graph_overlap},
+                  "graph_and_overlap": graph_overlap, "embedding_lora": embedding},
     }
     for inst in insts:
         inst.close()

@@ -327,6 +327,18 @@ lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, c
                            int ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
+ * lora_build_routing(routing, slot_ids, T) followed by lora_embedding(pool,
+ * routing, vocab_ids, y), with the same results (routing outputs and y bitwise
+ * identical): the gather reads the tokens' slot ids directly and writes each
+ * token's rank row by token index, and for T <= 256 tokens and pools of at most
+ * 255 slots the routing is built inside the gather launch (two launches instead of
+ * three).  slot_ids, vocab_ids: device int32 [T].  Errors as lora_build_routing and
+ * lora_embedding.
+ */
+lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, const int32_t* slot_ids, int T,
+                                 const int32_t* vocab_ids, void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
+
+/*
  * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
  * the routing, shrink, expand, linear and embedding calls launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start

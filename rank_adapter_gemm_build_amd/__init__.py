@@ -50,6 +50,7 @@ SIGNATURES = {
     "lora_build_routing_seq": (_I, [_P, _VP, _I, _I, _VP]),
     "lora_embedding_pool_create": (_I, [C.POINTER(_P), _I, _I, _I, _I, _I, _I, _I]),
     "lora_embedding": (_I, [_P, _P, _VP, _VP, _I, _I, _VP]),
+    "lora_route_embedding": (_I, [_P, _P, _VP, _I, _VP, _VP, _I, _I, _VP]),
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_timing_enable": (_I, [_I]),
@@ -411,3 +412,13 @@ def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=No
 def embedding(pool: Pool, routing: Routing, vocab_ids, y, stream=None) -> None:
     """y += s B_slot A_slot[:, vocab_id] per LoRA token (see lora_embedding)."""
     lora_embedding(pool.handle, routing.handle, _ptr(vocab_ids), _ptr(y), y.stride(0), _dt(y), _stream(stream))
+
+
+def route_embedding(pool: Pool, routing: Routing, slot_ids, vocab_ids, y, stream=None) -> None:
+    """routing.build(slot_ids) then embedding(pool, routing, vocab_ids, y), in one fewer
+    launch for small batches (see lora_route_embedding)."""
+    T = int(slot_ids.numel())
+    _check(lib.lora_route_embedding(pool.handle, routing.handle, _ptr(slot_ids) if T else None, T,
+                                    _ptr(vocab_ids) if T else None, _ptr(y), y.stride(0), _dt(y),
+                                    _stream(stream) or None), "lora_route_embedding")
+    routing.T = T

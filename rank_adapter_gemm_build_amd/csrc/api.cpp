@@ -847,6 +847,35 @@ lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, c
   return ok();
 }
 
+lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, const int32_t* slot_ids, int T,
+                                 const int32_t* vocab_ids, void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
+  if (!pool || !routing) return fail(LORA_ERR_INVALID_ARG, "pool and routing must not be NULL");
+  if (!pool->embedding) return fail(LORA_ERR_INVALID_ARG, "not an embedding pool (lora_embedding_pool_create)");
+  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
+  if (T > routing->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, routing->max_tokens);
+  if (T > 0 && (!slot_ids || !vocab_ids)) return fail(LORA_ERR_INVALID_ARG, "slot ids or vocab_ids NULL");
+  if (routing->S != pool->S) return fail(LORA_ERR_SHAPE, "routing has %d slots, pool has %d", routing->S, pool->S);
+  if (routing->device != pool->device)
+    return fail(LORA_ERR_INVALID_ARG, "routing on device %d, pool on device %d", routing->device, pool->device);
+  if (T > pool->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds the pool's max_tokens = %d", T, pool->max_tokens);
+  lora_status st = check_y(pool, T, y, ldy, ydtype);
+  if (st != LORA_OK) return st;
+  if (T == 0) return lora_build_routing(routing, slot_ids, 0, stream);
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  // u by token index in the workspace, read by the expand as a caller's finished u
+  const rax::UView U{pool->ws, 0, (long long)pool->max_tokens * pool->Rk, pool->Rk, 1, 1};
+  const bool fused = T <= rax::kSelfRouteTokens && pool->S + 1 <= rax::kSelfRouteKeys;
+  if (!fused && (st = lora_build_routing(routing, slot_ids, T, stream)) != LORA_OK) return st;
+  routing->T = T;
+  rax::SelfRoute sr{slot_ids, route_out(routing)};
+  hipError_t e = rax::launch_embed_gather_tok(pool->wdtype, pool_view(pool), route_view(routing), slot_ids, vocab_ids,
+                                              pool->k, U, fused ? &sr : nullptr, stream, timer_for(rax::kKGather));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
+}
+
 lora_status lora_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   g_timing_on = on != 0;

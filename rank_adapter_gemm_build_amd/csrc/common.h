@@ -160,6 +160,11 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
 // transposed A [V][Rmax] of each token's slot at its vocabulary id
 hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R, const int32_t* vocab_ids, int V,
                                const UView& W, hipStream_t stream, const KTimer& tm);
+// the same by token index, from the tokens' slot ids (W by_token); with sr, the
+// launch also builds the routing (T <= 256, S < 256)
+hipError_t launch_embed_gather_tok(int wdtype, const PoolView& P, const RouteView& R, const int32_t* slot_ids,
+                                   const int32_t* vocab_ids, int V, const UView& W, const SelfRoute* sr,
+                                   hipStream_t stream, const KTimer& tm);
 // finished u of a standalone shrink: workspace partials -> caller's [N][T][Rmax]
 hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W, const UView& U,
                            const Plan& plan, hipStream_t stream, const KTimer& tm);

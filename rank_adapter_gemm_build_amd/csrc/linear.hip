@@ -333,6 +333,67 @@ hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R
   return hipGetLastError();
 }
 
+// The same gather by token index, for a call that also has the tokens' slot ids: row
+// t of W gets A^T[slot_ids[t]][vocab_ids[t]][j] (zero for no-LoRA tokens, ranks past
+// the slot's and out-of-vocabulary ids), read by the expand as a caller's finished u.
+// ROUTE: the launch also builds the routing of the batch (route_wave on the first
+// wave of workgroup 0, T <= 256 and S < 256), which only the expand reads.
+template <typename T, bool ROUTE>
+__global__ __launch_bounds__(256) void embed_gather_tok_kernel(PoolView P, RouteView R, const int32_t* __restrict__ slot_ids,
+                                                               const int32_t* __restrict__ vocab_ids, int V, UView W,
+                                                               SelfRoute sr) {
+  int b = blockIdx.x;
+  if constexpr (ROUTE) {
+    __shared__ __align__(16) int sh[route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64)];
+    if (b == 0) {
+      if (threadIdx.x < 64)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
+      return;
+    }
+    b -= 1;
+  }
+  const long long n = (long long)R.T * P.Rk;
+  const long long step = (long long)(gridDim.x - (ROUTE ? 1 : 0)) * blockDim.x;
+  const T* __restrict__ At = static_cast<const T*>(P.A);
+  for (long long idx = b * (long long)blockDim.x + threadIdx.x; idx < n; idx += step) {
+    const int t = (int)(idx / P.Rk), j = (int)(idx - (long long)t * P.Rk);
+    const int s = slot_ids[t], v = vocab_ids[t];
+    float val = 0.f;
+    if (s >= 0 && s < P.S && v >= 0 && v < V && j < P.table[s].rank) {
+      const T a = At[((size_t)s * P.k + v) * P.Rmax + j];
+      if constexpr (sizeof(T) == 2) val = __uint_as_float((uint32_t)a << 16); else val = a;
+    }
+    W.p[(long long)t * W.row_stride + j] = val;
+  }
+}
+
+hipError_t launch_embed_gather_tok(int wdtype, const PoolView& P, const RouteView& R, const int32_t* slot_ids,
+                                   const int32_t* vocab_ids, int V, const UView& W, const SelfRoute* sr,
+                                   hipStream_t stream, const KTimer& tm) {
+  if (!W.by_token || W.nsplit != 1 || W.row_stride < P.Rk || P.N != 1 || P.k != V || R.T < 1 || !vocab_ids ||
+      !slot_ids || (sr && (sr->ids != slot_ids || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)))
+    return hipErrorInvalidValue;
+  const long long n = (long long)R.T * P.Rk;
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  const SelfRoute none{};
+  if (wdtype == LORA_BF16) {
+    if (sr)
+      RAX_LAUNCH(tm, (embed_gather_tok_kernel<uint16_t, true>), dim3(blocks + 1), dim3(256), 0u, stream, P, R, slot_ids,
+                 vocab_ids, V, W, *sr);
+    else
+      RAX_LAUNCH(tm, (embed_gather_tok_kernel<uint16_t, false>), dim3(blocks), dim3(256), 0u, stream, P, R, slot_ids,
+                 vocab_ids, V, W, none);
+  } else {
+    if (sr)
+      RAX_LAUNCH(tm, (embed_gather_tok_kernel<float, true>), dim3(blocks + 1), dim3(256), 0u, stream, P, R, slot_ids,
+                 vocab_ids, V, W, *sr);
+    else
+      RAX_LAUNCH(tm, (embed_gather_tok_kernel<float, false>), dim3(blocks), dim3(256), 0u, stream, P, R, slot_ids,
+                 vocab_ids, V, W, none);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ decode expand
 // LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
 __host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }

@@ -157,3 +157,27 @@ def test_embedding_pool_errors(rx):
     assert lib.lora_embedding(emb.handle, R.handle, None, y.data_ptr(), 64, rx.LORA_BF16, None) == \
         rx.LORA_ERR_INVALID_ARG
     emb.close(); lin.close(); R.close()
+
+
+@pytest.mark.parametrize("T,S", [(64, 8), (256, 200), (300, 9), (1, 1)])
+def test_route_embedding_matches_two_calls(rx, T, S):
+    """lora_route_embedding (routing inside the gather launch up to 256 tokens; the
+    separate routing launch above) against lora_build_routing + lora_embedding:
+    routing outputs and y bitwise equal."""
+    import torch
+    V, d, Rmax = 5000, 512, 32
+    ranks, A, B, ids, vocab, yb, alpha = _draw(90 + T, S, V, d, Rmax, T, "bf16")
+    pool = _embed_pool(rx, S, Rmax, V, d, "bf16", T, ranks, A, B, alpha)
+    it, vt = torch.from_numpy(ids).cuda(), torch.from_numpy(vocab).cuda()
+    R1, R2 = rx.Routing(0, T, S), rx.Routing(0, T, S)
+    y1, y2 = to_device(yb, "bf16"), to_device(yb, "bf16")
+    R1.build(it)
+    rx.embedding(pool, R1, vt, y1)
+    rx.route_embedding(pool, R2, it, vt, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y1), bits(y2))
+    q1, q2 = R1.query(), R2.query()
+    for key in ("counts", "seg_offsets", "sorted_ids", "active_slots"):
+        assert np.array_equal(q1[key], q2[key])
+    assert q1["n_invalid"] == q2["n_invalid"] and q1["num_active"] == q2["num_active"]
+    pool.close(); R1.close(); R2.close()
