@@ -129,6 +129,65 @@ def round_to_dtype(a, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+# ------------------------------------------------------------------ FP8 (e4m3)
+# [TRT-LLM] "LoraConfig"/FP8 special case (the fifth step of the weight preparation)
+# and "前向替换" (the input conversion and the output restore): with a native-FP8
+# adapter cache the adapter stays FP8; the scale is applied in BF16 and the result
+# clamped back into the FP8 range; the BF16 activations are clamped to the FP8 range
+# and converted; the correction is added to the BF16 base output.  The format is
+# OCP float8 e4m3 ("fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+# exponent field 0 subnormal, S.1111.111 NaN, no infinities, largest finite 448).
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_decode(bits) -> np.ndarray:
+    """Exact float64 value of e4m3 bit patterns (NaN for S.1111.111)."""
+    b = np.asarray(bits, dtype=np.int64) & 0xFF
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = s * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Round values with |x| <= 448 to e4m3 bit patterns, to nearest, ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    assert np.all(np.abs(x) <= FP8_MAX), "clamp to the FP8 range first"
+    out = np.zeros(x.shape, dtype=np.int64)
+    for idx, v in np.ndenumerate(x):
+        sign = 0x80 if np.signbit(v) else 0
+        a = abs(float(v))
+        if a < 2.0 ** -6:                          # subnormal range: steps of 2^-9
+            q = int(np.rint(a * 512.0))            # rint: ties to even
+            e, m = (1, 0) if q == 8 else (0, q)
+        else:
+            f, E = np.frexp(a)                     # a = f 2^E, f in [0.5, 1)
+            eu = E - 1
+            q = int(np.rint((a / 2.0 ** eu - 1.0) * 8.0))
+            if q == 8:
+                eu, q = eu + 1, 0
+            e, m = eu + 7, q
+        out[idx] = sign | (e << 3) | m
+    return out
+
+
+def fp8_quantize(x) -> np.ndarray:
+    """The forward input conversion: clamp to [-448, 448], then round to e4m3
+    ([TRT-LLM] "前向替换": x.clamp(-fp8_max, fp8_max).to(float8_e4m3fn)).  float64 out."""
+    return fp8_e4m3_decode(fp8_e4m3_encode(np.clip(np.asarray(x, dtype=np.float64), -FP8_MAX, FP8_MAX)))
+
+
+def fp8_fold_scale(b_fp8_values, scale) -> np.ndarray:
+    """The FP8 scale fold at weight preparation: the FP8 weights go to BF16, are
+    multiplied by the scale (a float32 product rounded once to BF16), clamped to the
+    FP8 range and rounded back to e4m3.  Returns the new e4m3 values as float64."""
+    prod32 = np.asarray(b_fp8_values, dtype=np.float32) * np.float32(scale)
+    p = bf16_bits_to_f64(f32_to_bf16_bits(prod32))
+    return fp8_e4m3_decode(fp8_e4m3_encode(np.clip(p, -FP8_MAX, FP8_MAX)))
+
+
 # ------------------------------------------------------------------ adapter pool
 @dataclass
 class Adapter:
@@ -169,6 +228,8 @@ def effective_b(adapter: Adapter, n: int, wdtype: str):
         return None, float(s)
     if not adapter.premultiply:
         return np.asarray(B, dtype=np.float64), float(s)
+    if wdtype == "fp8":   # folded in BF16 and clamped back into FP8 (fp8_fold_scale)
+        return fp8_fold_scale(np.asarray(B, dtype=np.float64), s), 1.0
     prod32 = np.float32(s) * np.asarray(B, dtype=np.float32)  # one fp32 rounding
     return round_to_dtype(prod32.astype(np.float64), wdtype), 1.0
 
@@ -382,6 +443,14 @@ def lora_apply(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int], i
                 sl = slice(offs[n], offs[n] + slices[n])
                 y[t, sl] = y[t, sl] + delta[t, sl]
     return y
+
+
+def lora_apply_fp8(x, y_base, adapters: Dict[int, Adapter], slices: Sequence[int], ids: Sequence[int],
+                   S: int, max_rank: Optional[int] = None) -> np.ndarray:
+    """The FP8 adapter path: x (the BF16 activations, exact values) is first
+    converted to FP8 (fp8_quantize), the adapters' A and B hold e4m3 values (and a
+    pre-multiplied B the folded values); then the definition as lora_apply."""
+    return lora_apply(fp8_quantize(x), y_base, adapters, slices, ids, S, "fp8", max_rank=max_rank)
 
 
 def embedding_apply(vocab_ids: Sequence[int], y_base, adapters: Dict[int, Adapter], vocab: int,

@@ -448,3 +448,66 @@ def test_embedding_is_linear_lora_on_one_hot_inputs(premultiply):
     got = O.embedding_apply(vocab, yb, ads, V, ids, S, "f32")
     ref = O.lora_apply(onehot, yb, ads, [d], ids, S, "f32", max_rank=8)
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ FP8 (e4m3)
+def _torch_fp8():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    return torch
+
+
+def test_fp8_decode_matches_torch_all_bytes():
+    """Every e4m3 bit pattern decodes to torch's float8_e4m3fn value (a library
+    implementation of the OCP format), NaN patterns included."""
+    torch = _torch_fp8()
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.fp8_e4m3_decode(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert O.fp8_e4m3_decode([0x7E])[0] == 448.0 and O.fp8_e4m3_decode([0x01])[0] == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch_rounding():
+    """Round-to-nearest-even to e4m3 agrees with torch's conversion on every finite
+    value, on every midpoint between neighbours (the ties) and on random values."""
+    torch = _torch_fp8()
+    vals = O.fp8_e4m3_decode(np.arange(256))
+    fin = np.unique(vals[~np.isnan(vals)])
+    mids = (fin[:-1] + fin[1:]) / 2.0
+    rng = np.random.default_rng(3)
+    rnd = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 0.01,
+                          rng.standard_normal(2000) * 2.0 ** -8])
+    for x in (fin, mids, rnd):
+        ref = torch.from_numpy(x.astype(np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+        got = O.fp8_e4m3_encode(x)
+        assert np.array_equal(got, ref)
+    # two ties by hand: 1.0625 lies between 1.0 (mantissa 000) and 1.125 (001) -> 1.0;
+    # 1.1875 between 1.125 (001) and 1.25 (010) -> 1.25
+    assert list(O.fp8_e4m3_encode([1.0625, 1.1875])) == [0x38, 0x3A]
+
+
+def test_fp8_quantize_clamps_first():
+    """Without the clamp a value past 464 would round to NaN; the input conversion
+    clamps to +-448 first, and values already on the grid are unchanged."""
+    assert list(O.fp8_quantize([500.0, -1e6, 460.0])) == [448.0, -448.0, 448.0]
+    grid = O.fp8_e4m3_decode(np.arange(0, 0x7F))
+    assert np.array_equal(O.fp8_quantize(grid), grid)
+
+
+def test_fp8_fold_scale_matches_the_pages_expression():
+    """The scale fold equals the page's expression evaluated by torch:
+    (t.to(bfloat16) * scale).clamp(-fp8_max, fp8_max).to(float8_e4m3fn)."""
+    torch = _torch_fp8()
+    rng = np.random.default_rng(5)
+    b = rng.integers(0, 256, size=3000).astype(np.uint8)
+    b = b[~np.isnan(O.fp8_e4m3_decode(b))]
+    vals = O.fp8_e4m3_decode(b)
+    for s in (np.float32(2.0), np.float32(1.0 / 3.0), np.float32(4.0), np.float32(0.70710677), np.float32(37.5)):
+        t = torch.from_numpy(b).view(torch.float8_e4m3fn)
+        ref = (t.to(torch.bfloat16) * float(s)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        got = O.fp8_fold_scale(vals, s)
+        assert np.array_equal(got, ref), float(s)
