@@ -63,7 +63,14 @@ extern "C" {
 typedef struct lora_pool lora_pool;
 typedef struct lora_routing lora_routing;
 
-typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+/* LORA_FP8E4M3: adapter weights as OCP float8 e4m3 ("fn": 4 exponent bits, bias 7, 3
+ * mantissa bits, largest finite 448), the native-FP8 adapter cache of [TRT-LLM]
+ * (the FP8 special case of the weight preparation, and "前向替换").  A pool of this
+ * weight type takes bf16 activations x, which the kernels clamp to [-448, 448]
+ * and round to e4m3 before use, as the page converts the input; products are exact
+ * and accumulate in fp32; y is bf16 or fp32.  Such pools use the vector units for
+ * every segment (no matrix-core path). */
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1, LORA_FP8E4M3 = 2 } lora_dtype;
 
 typedef int lora_status;
 #define LORA_OK                0

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libraxlora.so")
 
-LORA_F32, LORA_BF16 = 0, 1
+LORA_F32, LORA_BF16, LORA_FP8E4M3 = 0, 1, 2
 LORA_SRC_DEVICE, LORA_PREMULTIPLY = 1, 2
 LORA_MAX_SLICES, LORA_MAX_SLOTS, LORA_MAX_RANK, LORA_MAX_IN_FEATURES = 8, 1024, 256, 65536
 
@@ -290,7 +290,7 @@ class Pool:
 
     def read_slot(self, slot: int, slice_: int):
         import numpy as np
-        dt = np.uint16 if self.wdtype == LORA_BF16 else np.float32
+        dt = {LORA_BF16: np.uint16, LORA_FP8E4M3: np.uint8}.get(self.wdtype, np.float32)
         A = np.zeros((self.k, self.Rmax) if self.embedding else (self.Rmax, self.k), dtype=dt)
         Bt = np.zeros((self.Rmax, self.slices[slice_]), dtype=dt)
         lora_pool_read_slot(self.handle, slot, slice_, A.ctypes.data, Bt.ctypes.data)
@@ -359,13 +359,20 @@ def _dt(t) -> int:
         return LORA_F32
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return LORA_BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        return LORA_FP8E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _act(pool) -> int:
+    """dtype of the activations x a pool takes: bf16 for FP8 pools, else the pool's."""
+    return LORA_BF16 if pool.wdtype == LORA_FP8E4M3 else pool.wdtype
 
 
 def shrink(pool: Pool, routing: Routing, x, u, stream=None) -> None:
     """u [N, T, Rmax] fp32 = per-token A_slot x (see lora_shrink)."""
-    if _dt(x) != pool.wdtype:
-        raise TypeError("x dtype must match the pool dtype")
+    if _dt(x) != _act(pool):
+        raise TypeError("x dtype must be the pool's activation dtype")
     lora_shrink(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(u), _stream(stream))
 
 
@@ -376,16 +383,16 @@ def expand(pool: Pool, routing: Routing, u, y, stream=None) -> None:
 
 def linear(pool: Pool, routing: Routing, x, y, stream=None) -> None:
     """y += s B_slot (A_slot x) in place onto the caller's base output (see lora_linear)."""
-    if _dt(x) != pool.wdtype:
-        raise TypeError("x dtype must match the pool dtype")
+    if _dt(x) != _act(pool):
+        raise TypeError("x dtype must be the pool's activation dtype")
     lora_linear(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y), _stream(stream))
 
 
 def route_linear(pool: Pool, routing: Routing, ids, x, y, stream=None) -> None:
     """routing.build(ids) then linear(pool, routing, x, y), in one fewer launch for small
     batches (see lora_route_linear)."""
-    if _dt(x) != pool.wdtype:
-        raise TypeError("x dtype must match the pool dtype")
+    if _dt(x) != _act(pool):
+        raise TypeError("x dtype must be the pool's activation dtype")
     T = int(ids.numel())
     lora_route_linear(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
                       y.stride(0), _dt(y), _stream(stream))
@@ -396,8 +403,8 @@ def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=No
     """linear (or route_linear when ids is given) whose expand waits for the torch
     event y_ready, recorded after the base output was written into y on another
     stream (see lora_linear_join / lora_route_linear_join)."""
-    if _dt(x) != pool.wdtype:
-        raise TypeError("x dtype must match the pool dtype")
+    if _dt(x) != _act(pool):
+        raise TypeError("x dtype must be the pool's activation dtype")
     ev = y_ready.cuda_event if y_ready is not None else 0
     if ids is None:
         lora_linear_join(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y),

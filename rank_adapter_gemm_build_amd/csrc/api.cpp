@@ -199,7 +199,8 @@ rax::RouteView route_view(const lora_routing* r) {
   return v;
 }
 
-int chunk_width(lora_dtype t) { return 64 * (t == LORA_BF16 ? 8 : 4); }
+// k elements of one wave-wide chunk step of the decode shrink (x is bf16 for FP8 pools)
+int chunk_width(lora_dtype t) { return 64 * (t == LORA_F32 ? 4 : 8); }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -238,8 +239,9 @@ lora_status check_x(const lora_pool* pool, int T, const void* x, int ldx) {
 lora_status check_y(const lora_pool* pool, int T, const void* y, int ldy, lora_dtype ydtype) {
   if (T > 0 && !y) return fail(LORA_ERR_INVALID_ARG, "y is NULL");
   if (ydtype != LORA_F32 && ydtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown ydtype %d", (int)ydtype);
-  if (ydtype != pool->wdtype && ydtype != LORA_F32)
-    return fail(LORA_ERR_DTYPE, "y must be the pool dtype or float32");
+  const lora_dtype act = pool->wdtype == LORA_FP8E4M3 ? LORA_BF16 : pool->wdtype;   // activation dtype
+  if (ydtype != act && ydtype != LORA_F32)
+    return fail(LORA_ERR_DTYPE, "y must be the pool's activation dtype or float32");
   if (ldy < pool->D) return fail(LORA_ERR_SHAPE, "ldy = %d < output width %d", ldy, pool->D);
   if (ldy % 8 != 0 || !aligned16(y)) return fail(LORA_ERR_ALIGN, "y must be 16-byte aligned with ldy a multiple of 8");
   return LORA_OK;
@@ -455,7 +457,9 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   if (num_slices < 1 || num_slices > LORA_MAX_SLICES)
     return fail(LORA_ERR_SHAPE, "num_slices %d outside [1, %d]", num_slices, LORA_MAX_SLICES);
   if (max_tokens < 1) return fail(LORA_ERR_SHAPE, "max_tokens %d < 1", max_tokens);
-  if (wdtype != LORA_F32 && wdtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown wdtype %d", (int)wdtype);
+  if (wdtype != LORA_F32 && wdtype != LORA_BF16 && wdtype != LORA_FP8E4M3)
+    return fail(LORA_ERR_DTYPE, "unknown wdtype %d", (int)wdtype);
+  if (embedding && wdtype == LORA_FP8E4M3) return fail(LORA_ERR_DTYPE, "embedding pools take bf16 or fp32 weights");
   long long D = 0;
   for (int n = 0; n < num_slices; ++n) {
     if (slice_out[n] < 1) return fail(LORA_ERR_SHAPE, "slice %d width %d < 1", n, slice_out[n]);
@@ -482,7 +486,7 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   p->N = num_slices;
   p->max_tokens = max_tokens;
   p->wdtype = wdtype;
-  p->esize = wdtype == LORA_BF16 ? 2 : 4;
+  p->esize = wdtype == LORA_BF16 ? 2 : wdtype == LORA_FP8E4M3 ? 1 : 4;
   p->embedding = embedding;
   int o = 0, tiles = 0, mblocks = 0;
   for (int n = 0; n < num_slices; ++n) {

@@ -60,15 +60,37 @@ struct ShrinkRows {
   }
 };
 
+// One lane's 16-byte chunk of an A row as the dot products read it: as stored for
+// bf16 and fp32 pools; for FP8 pools 8 bytes, widened to 8 bf16 at use.
+template <typename TW> struct AChunk {
+  using type = uint4;
+  __device__ __forceinline__ static type load(const TW* p) { return ld16(p); }
+  __device__ __forceinline__ static uint4 widen(const type& c) { return c; }
+  __device__ __forceinline__ static type keep(const type& c, bool ok) { return keep_if(c, ok); }
+};
+template <> struct AChunk<uint8_t> {
+  using type = uint2;
+  __device__ __forceinline__ static type load(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ static uint4 widen(const type& c) { return fp8x8_to_bf16x8(c); }
+  __device__ __forceinline__ static type keep(const type& c, bool ok) {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return make_uint2(c.x & m, c.y & m);
+  }
+};
+
 // Partial sums of split sp (chunk steps sp + nsplit * m, m < ns) for the block's 16
 // rows and the tile's 4 token rows; tokens at or past nt contribute zero.  Returns
 // this lane's value after the reduce-scatter: row fb + lane / 4, token lane % 4.
-template <typename T>
-__device__ __forceinline__ float shrink_block_partial(const PoolView& P, const ShrinkRows<T>& A,
-                                                      const T* const (&xrow)[kShrinkTok], int nt, int sp,
+// TX is the x type, TW the weight type (TW = TX, or FP8 weights with bf16 x, whose
+// chunks are first put on the e4m3 grid).
+template <typename TX, typename TW>
+__device__ __forceinline__ float shrink_block_partial(const PoolView& P, const ShrinkRows<TW>& A,
+                                                      const TX* const (&xrow)[kShrinkTok], int nt, int sp,
                                                       int nsplit, int ns) {
-  constexpr int E = Elem<T>::kPerChunk;
+  constexpr int E = Elem<TX>::kPerChunk;
   constexpr int CW = 64 * E;         // k elements of one wave-wide chunk step
+  static_assert(Elem<TW>::kPerChunk == E, "weight and x chunks cover the same k range");
+  using AC = AChunk<TW>;
   const int lane = lane_id();
   float acc[64];
 #pragma unroll
@@ -78,20 +100,24 @@ __device__ __forceinline__ float shrink_block_partial(const PoolView& P, const S
     const bool inb = col < P.k;
     const int colc = min(col, P.k - E);
     // the x chunks and all 16 A rows of this chunk step in flight before the first product
-    uint4 xv[kShrinkTok], av[kShrinkRows];
+    uint4 xv[kShrinkTok];
+    typename AC::type av[kShrinkRows];
 #pragma unroll
     for (int i = 0; i < kShrinkTok; ++i) xv[i] = ld16(xrow[i] + colc);
 #pragma unroll
-    for (int rr = 0; rr < kShrinkRows; ++rr) av[rr] = ld16(A.arow[rr] + colc);
+    for (int rr = 0; rr < kShrinkRows; ++rr) av[rr] = AC::load(A.arow[rr] + colc);
     sched_fence();
 #pragma unroll
-    for (int i = 0; i < kShrinkTok; ++i) xv[i] = keep_if(xv[i], i < nt && inb);
+    for (int i = 0; i < kShrinkTok; ++i) {
+      if constexpr (sizeof(TW) == 1) xv[i] = bf16x8_to_fp8_grid(xv[i]);
+      xv[i] = keep_if(xv[i], i < nt && inb);
+    }
 #pragma unroll
     for (int rr = 0; rr < kShrinkRows; ++rr) {
-      const uint4 a = keep_if(av[rr], A.rval[rr]);
+      const uint4 a = AC::widen(AC::keep(av[rr], A.rval[rr]));
 #pragma unroll
       for (int i = 0; i < kShrinkTok; ++i)
-        acc[rr * kShrinkTok + i] = chunk_dot(a, xv[i], acc[rr * kShrinkTok + i], T());
+        acc[rr * kShrinkTok + i] = chunk_dot(a, xv[i], acc[rr * kShrinkTok + i], TX());
     }
   }
   reduce_scatter64(acc);
@@ -117,8 +143,18 @@ template <> struct Row8<float> {
   }
 };
 
-// rank rows of B^T per load batch: 16 for bf16 pools (64 registers), 8 for fp32
-template <typename TW> struct ExpandRows { static constexpr int kBatch = sizeof(TW) == 2 ? 16 : 8; };
+template <> struct Row8<uint8_t> {   // FP8 pools: 8 bytes, widened at use
+  uint2 w;
+  __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void keep(bool ok) {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    w = make_uint2(w.x & m, w.y & m);
+  }
+  __device__ __forceinline__ void get(float (&v)[8]) const { fp8x8_to_f32(w, v); }
+};
+
+// rank rows of B^T per load batch: 16 for bf16 and FP8 pools (64 or 32 registers), 8 for fp32
+template <typename TW> struct ExpandRows { static constexpr int kBatch = sizeof(TW) <= 2 ? 16 : 8; };
 
 // One expand tile in two halves, so a caller can put other work between issuing the
 // loads and using them: issue() loads the first RB rows of B^T and the 4 token rows

@@ -39,11 +39,55 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// ------------------------------------------------------------ float8 (e4m3)
+// OCP e4m3 ("fn"): every value is exactly a bfloat16 value, so FP8 operands are
+// widened to bf16 in registers and the bf16 arithmetic is reused.  The hardware
+// conversions round to nearest even (checked against the format definition on
+// every e4m3 byte and every bf16 value in [-448, 448]).
+__device__ __forceinline__ uint32_t f32x2_hi_to_bf16x2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);   // exact: the low halves are zero
+}
+// 8 e4m3 bytes -> 8 bf16 (one 16-byte chunk)
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 w) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  return make_uint4(f32x2_hi_to_bf16x2(a[0], a[1]), f32x2_hi_to_bf16x2(b[0], b[1]), f32x2_hi_to_bf16x2(c[0], c[1]),
+                    f32x2_hi_to_bf16x2(d[0], d[1]));
+}
+// 8 e4m3 bytes -> 8 floats
+__device__ __forceinline__ void fp8x8_to_f32(uint2 w, float (&v)[8]) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1]; v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+}
+constexpr float kFp8Max = 448.f;
+// FP8 pools' input conversion of 8 bf16 activations: clamp to [-448, 448], round to
+// e4m3, back to bf16 (page "TensorRT-LLM 源码完全拆解(二十一)", section "前向替换")
+__device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
+  float v[8];
+  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+  v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+  v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -kFp8Max), kFp8Max);
+  int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p0, true);
+  int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], p1, true);
+  return fp8x8_to_bf16x8(make_uint2((uint32_t)p0, (uint32_t)p1));
+}
+
 // -------------------------------------------------------------- lane chunks
 // Every lane moves 16 bytes per load: 8 bf16 or 4 fp32 elements.
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int kPerChunk = 8; };
 template <> struct Elem<float> { static constexpr int kPerChunk = 4; };
+template <> struct Elem<uint8_t> { static constexpr int kPerChunk = 8; };   // 8-byte chunks, widened to bf16
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 // v if ok else zero, component-wise (a ternary on the whole vector makes the compiler

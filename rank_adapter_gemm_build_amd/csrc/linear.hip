@@ -56,14 +56,14 @@ namespace rax {
 // Token tiles tt0, tt0 + 4 ntg, ... of slot s's segment (L tokens from sorted
 // position p0) against 16 rank rows (block rb) over k split sp; toks(tt) gives the
 // token ids at positions tt .. tt + 3 of the segment (valid rows past its end).
-template <typename T, typename Toks>
+template <typename T, typename TW, typename Toks>
 __device__ __forceinline__ void shrink_decode_tiles(const PoolView& P, const T* __restrict__ x, int ldx,
                                                     const UView& U, const Plan& plan, int s, int sp, int rb,
                                                     int tt0, int L, int p0, const SlotEntry& e, const Toks& toks) {
   const int r = e.rank, F = P.N * r, fb = rb * kShrinkRows;
   if (r == 0 || fb >= F) return;                   // uniform per wave
   const int lane = lane_id();
-  const ShrinkRows<T> A(P, s, r, fb);
+  const ShrinkRows<TW> A(P, s, r, fb);
   // this lane's output after the reduce-scatter: row fb + lane / 4, token lane % 4
   const int orr = lane / kShrinkTok, oi = lane - orr * kShrinkTok, of = fb + orr;
   const int on = of < F ? of / r : 0, oj = of < F ? of - on * r : 0;
@@ -75,7 +75,7 @@ __device__ __forceinline__ void shrink_decode_tiles(const PoolView& P, const T* 
     const T* xrow[kShrinkTok];
 #pragma unroll
     for (int i = 0; i < kShrinkTok; ++i) xrow[i] = x + (size_t)tok_at(tq, i) * ldx;
-    const float v = shrink_block_partial<T>(P, A, xrow, nt, sp, plan.nsplit, plan.ns);
+    const float v = shrink_block_partial<T, TW>(P, A, xrow, nt, sp, plan.nsplit, plan.ns);
     if (of < F && oi < nt) uo[(long long)(p0 + tt + oi) * U.row_stride] = v;   // rows by sorted position
   }
 }
@@ -92,7 +92,7 @@ struct DecodeShrinkIndex {
   }
 };
 
-template <typename T>
+template <typename T, typename TW>
 __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const RouteView& R,
                                                    const T* __restrict__ x, int ldx, const UView& U,
                                                    const Plan& plan, int unit) {
@@ -106,14 +106,14 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
   const int L = hdr.x, p0 = hdr.y;
   if (tt0 >= L) return;
   if (plan.use_mfma && L >= R.mfma_min) return;   // long segment: matrix-core units
-  shrink_decode_tiles<T>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
+  shrink_decode_tiles<T, TW>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
     return tt == tt0 && tt0 + 4 <= kRecTokens ? tq0 : segment_tokens(R, s, tt, p0, L);
   });
 }
 
 // The same unit in a launch that builds the routing itself: the segment comes from
 // the batch's slot ids (BatchKeys), its token ids through the wave's LDS.
-template <typename T>
+template <typename T, typename TW>
 __device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const RouteView& R,
                                                         const int32_t* __restrict__ ids, const T* __restrict__ x,
                                                         int ldx, const UView& U, const Plan& plan, int unit,
@@ -129,7 +129,7 @@ __device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const
   if (tt0 >= L) return;
   if (plan.use_mfma && L >= R.mfma_min) return;
   wave_lds_sync();
-  shrink_decode_tiles<T>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
+  shrink_decode_tiles<T, TW>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
     const int last = L - 1;
     return make_int4(tok[min(tt, last)], tok[min(tt + 1, last)], tok[min(tt + 2, last)], tok[min(tt + 3, last)]);
   });
@@ -161,8 +161,9 @@ __host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + 
 // units.  SELF: the launch also builds the routing (route_wave in workgroup 0;
 // workgroups 1-7 are idle, so the others keep their XCD numbering), and the units
 // take their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead
-// of the routing outputs being written meanwhile.
-template <typename T, bool SELF>
+// of the routing outputs being written meanwhile.  T is the type of x, TW of the
+// weights (T, or FP8 with bf16 x: vector units only).
+template <typename T, typename TW, bool SELF>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
                                                     int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
   int b = blockIdx.x;
@@ -178,10 +179,10 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
     int* tok = sh + kSelfRouteK;
     if (b >= n_mfma_blocks) {
       const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
-      if (d < plan.n_dec_blocks) shrink_decode_unit_self<T>(P, R, sr.ids, x, ldx, U, plan, d, tok);
+      if (d < plan.n_dec_blocks) shrink_decode_unit_self<T, TW>(P, R, sr.ids, x, ldx, U, plan, d, tok);
       return;
     }
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && sizeof(TW) == 2) {
       // LDS: slot counts [kSelfRouteK], then the tile's tokens, then the batch's keys
       int* keys = sh + kSelfRouteK + kSelfRouteT;
       int ntiles;
@@ -212,10 +213,10 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
   }
   if (b >= n_mfma_blocks) {
     const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
-    if (d < plan.n_dec_blocks) shrink_decode_unit<T>(P, R, x, ldx, U, plan, d);
+    if (d < plan.n_dec_blocks) shrink_decode_unit<T, TW>(P, R, x, ldx, U, plan, d);
     return;
   }
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && sizeof(TW) == 2) {
     // items part-major: an XCD's stretch covers whole k parts (with 8 parts, one
     // each), so the rows of A and the k-slices of x it reads are its own
     const int ntiles = R.meta[kMetaTiles], per_part = ntiles * plan.nrg;
@@ -227,23 +228,24 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
   }
 }
 
-template <typename T>
+template <typename T, typename TW>
 static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, int ldx, const UView& U,
                             const Plan& plan, const SelfRoute* sr, hipStream_t stream, const KTimer& tm) {
   const int nm = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
   const int q = kXcds * plan.xcd_group;
   const int blocks = nm + (plan.n_dec_blocks + q - 1) / q * q;
   if (sr)
-    RAX_LAUNCH(tm, (shrink_kernel<T, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm, *sr);
+    RAX_LAUNCH(tm, (shrink_kernel<T, TW, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
+               *sr);
   else
-    RAX_LAUNCH(tm, (shrink_kernel<T, false>), dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
+    RAX_LAUNCH(tm, (shrink_kernel<T, TW, false>), dim3(blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
                SelfRoute{});
 }
 
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
                          const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
                          const KTimer& tm) {
-  const int cw = 64 * (wdtype == LORA_BF16 ? 8 : 4);
+  const int cw = 64 * (wdtype == LORA_F32 ? 4 : 8);   // x is bf16 for FP8 pools
   const int chunks = (P.k + cw - 1) / cw;
   if (plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
       plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
@@ -252,9 +254,11 @@ hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, cons
       (sr && (!sr->ids || R.T < 1 || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)))
     return hipErrorInvalidValue;
   if (wdtype == LORA_BF16)
-    launch_shrink_t(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
+    launch_shrink_t<uint16_t, uint16_t>(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
+  else if (wdtype == LORA_FP8E4M3)
+    launch_shrink_t<uint16_t, uint8_t>(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
   else
-    launch_shrink_t(P, R, static_cast<const float*>(x), ldx, U, plan, sr, stream, tm);
+    launch_shrink_t<float, float>(P, R, static_cast<const float*>(x), ldx, U, plan, sr, stream, tm);
   return hipGetLastError();
 }
 
@@ -540,15 +544,15 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UVi
   }
 }
 
-template <typename TY>
-static void launch_expand_bf16(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
-                               const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int nm,
-                               const KTimer& tm) {
+template <typename TW, typename TY>
+static void launch_expand_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
+                            const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int nm,
+                            const KTimer& tm) {
   switch (ksm) {
-    case 1: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    case 2: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    case 4: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    default: RAX_LAUNCH(tm, (expand_kernel<uint16_t, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    case 1: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    case 2: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    case 4: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
+    default: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
   }
 }
 
@@ -571,13 +575,18 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
   const int q = kXcds * plan.xcd_group;
   const dim3 grid(nm + (plan.n_dec_blocks + q - 1) / q * q);
   const uint32_t lds = (uint32_t)expand_smem_bytes(wdtype, P.Rmax, plan.use_mfma);
+  // rank steps of 32 the matrix-core part keeps in registers: Rk / 32 rounded up to a power of 2
+  const int ksm = P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8;
   if (wdtype == LORA_BF16) {
-    // rank steps of 32 the matrix-core part keeps in registers: Rk / 32 rounded up to a power of 2
-    const int ksm = P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8;
     if (ydtype == LORA_BF16)
-      launch_expand_bf16<uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
+      launch_expand_w<uint16_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
     else
-      launch_expand_bf16<float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
+      launch_expand_w<uint16_t, float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
+  } else if (wdtype == LORA_FP8E4M3) {   // vector units only
+    if (ydtype == LORA_BF16)
+      launch_expand_w<uint8_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
+    else
+      launch_expand_w<uint8_t, float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
   } else {
     RAX_LAUNCH(tm, (expand_kernel<float, float, 1>), grid, dim3(64), lds, stream, P, R, U,
                static_cast<float*>(y), ldy, plan, nm);

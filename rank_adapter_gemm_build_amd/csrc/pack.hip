@@ -16,6 +16,15 @@ __device__ __forceinline__ float to_f(uint16_t v) { return __uint_as_float((uint
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ void from_f(float f, uint16_t& v) { v = (uint16_t)f32_to_bf16(f); }
 __device__ __forceinline__ void from_f(float f, float& v) { v = f; }
+// FP8 pools: the scale fold of page "TensorRT-LLM 源码完全拆解(二十一)" (FP8 weights stay
+// FP8; the scale is applied in bf16 and the result clamped back into the FP8 range):
+// the fp32 product is rounded to bf16, clamped to [-448, 448] and rounded to e4m3
+__device__ __forceinline__ float to_f(uint8_t v) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false)[0]; }
+__device__ __forceinline__ void from_f(float f, uint8_t& v) {
+  const float b = __uint_as_float(f32_to_bf16(f) << 16);
+  const float c = fminf(fmaxf(b, -kFp8Max), kFp8Max);
+  v = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.f, 0, false) & 0xff);
+}
 
 // A block [Rmax][k]: rows < rank copied from src [rank][k] (NULL -> zeros), the rest zero.
 template <typename T>
@@ -87,6 +96,9 @@ hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, v
   if (wdtype == LORA_BF16)
     return pack<uint16_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                           premultiply, a_by_row, stream);
+  if (wdtype == LORA_FP8E4M3)
+    return pack<uint8_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
+                         premultiply, a_by_row, stream);
   return pack<float>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                      premultiply, a_by_row, stream);
 }
