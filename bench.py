@@ -413,6 +413,87 @@ def measure_embedding(torch, rx, lib, W, args, vocab=32000):
     return res
 
 
+# ------------------------------------------------------------ FP8 adapter pools
+def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
+    """The same workload with FP8 (e4m3) adapter pools: every A and B converted to
+    e4m3 by torch (float8_e4m3fn), activations and outputs bf16 as before; one step
+    = lora_route_linear + lora_linear per further module, rotating over instances
+    like the main loop.  Algorithmic bytes: the bf16 step's with the weight bytes
+    halved (x and y unchanged)."""
+    import numpy as np
+    if W.dtype != "bf16" or not hasattr(torch, "float8_e4m3fn"):
+        return None
+    T = W.T
+    # weight bytes of the bf16 step (shrink: A, expand: B), halved for e4m3
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    counts = np.bincount(keys, minlength=W.S + 1)
+    wbytes = sum(r * (m.k * len(m.slices) + sum(m.slices)) * 2 for m in W.modules
+                 for s, r in W.ranks.items() if counts[s] > 0)
+    step_bytes = step_bytes_bf16 - wbytes // 2
+    per_inst = sum(W.S * W.Rmax * (m.k * len(m.slices) + 2 * sum(m.slices)) for m in W.modules)
+    M = max(2, min(args.max_instances, int(np.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes, 1)))))
+    M = min(M, max(2, int(40 * 2 ** 30 // max(per_inst, 1))))
+
+    def fp8(t):
+        return None if t is None else t.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+    conv = [{"A": {s: [fp8(a) for a in src_m["A"][s]] for s in W.ranks},
+             "B": {s: [fp8(b) for b in src_m["B"][s]] for s in W.ranks}} for src_m in src]
+    ids = torch.from_numpy(W.ids.astype(np.int32)).cuda()
+    insts = []
+    for i in range(M):
+        mods = []
+        R = rx.Routing(0, T, W.S)
+        for m, src_m, c in zip(W.modules, src, conv):
+            pool = rx.Pool(0, W.S, W.Rmax, m.k, m.slices, rx.LORA_FP8E4M3, T)
+            for s, r in W.ranks.items():
+                pool.register(s, c["A"][s], c["B"][s], W.alpha[s], r, W.rslora, W.adapter_scale, device_src=True)
+            mods.append((pool, src_m["x"].clone(), src_m["y"].clone()))
+        insts.append((R, mods))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        R, mods = insts[i % M]
+        pool, x, y = mods[0]
+        st = lib.lora_route_linear(pool.handle, R.handle, ids.data_ptr(), T, x.data_ptr(), x.stride(0), y.data_ptr(),
+                                   y.stride(0), rx.LORA_BF16, stream)
+        if st:
+            raise rx.LoraError(st, "lora_route_linear")
+        for pool, x, y in mods[1:]:
+            st = lib.lora_linear(pool.handle, R.handle, x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0),
+                                 rx.LORA_BF16, stream)
+            if st:
+                raise rx.LoraError(st, "lora_linear")
+
+    for i in range(min(args.warmup, 10) + M):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    rx.lora_timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    rep = rx.lora_timing_report()
+    rx.lora_timing_enable(False)
+    kern = {k: round(1e3 * ms / n, 3) for k, (ms, n) in rep.items() if n}
+    for R, mods in insts:
+        R.close()
+        for pool, _, _ in mods:
+            pool.close()
+    res = {"us_per_step": round(us, 3), "tokens_per_s": round(T / (us * 1e-6), 1), "step_algorithmic_bytes": step_bytes,
+           "step_hbm_gbps": round(step_bytes / (us * 1e-6) / 1e9, 2), "kernels_avg_us": kern, "rotation_instances": M,
+           "weights": "e4m3 (OCP), activations and outputs bf16; vector units only"}
+    log(f"FP8 pools: {us:.2f} us/step ({step_bytes / 1e6:.1f} MB algorithmic), kernels {kern}")
+    return res
+
+
 # ------------------------------------------------------------------------ main
 def run(args):
     import numpy as np
@@ -537,6 +618,7 @@ def run(args):
         inst.close()
     insts = []
     embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
+    fp8 = None if args.no_extras else measure_fp8(torch, rx, lib, W, src, args, step_bytes, acc)
 
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
@@ -553,7 +635,7 @@ def run(args):
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
                   "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
                   "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest(),
-                  "graph_and_overlap": graph_overlap, "embedding_lora": embedding},
+                  "graph_and_overlap": graph_overlap, "embedding_lora": embedding, "fp8_pools": fp8},
     }
     for inst in insts:
         inst.close()

@@ -42,7 +42,7 @@
  *     equivalent paths or launch shapes, and results stay within the tolerances
  *     the tests check):
  *       RAXLORA_MFMA_MIN_SEG  segments of at least this many tokens go to the
- *                             matrix cores (bf16 pools; default 4; read when a
+ *                             matrix cores (bf16 and FP8 pools; default 4; read when a
  *                             routing object is created)
  *       RAXLORA_DISABLE_MFMA  1: every segment on the vector units
  *       RAXLORA_CB1_MAX       matrix-core expand units take one 128-column block
@@ -68,8 +68,8 @@ typedef struct lora_routing lora_routing;
  * (the FP8 special case of the weight preparation, and "前向替换").  A pool of this
  * weight type takes bf16 activations x, which the kernels clamp to [-448, 448]
  * and round to e4m3 before use, as the page converts the input; products are exact
- * and accumulate in fp32; y is bf16 or fp32.  Such pools use the vector units for
- * every segment (no matrix-core path). */
+ * and accumulate in fp32; y is bf16 or fp32.  The weights are widened to bf16 in
+ * registers (exact), so both the vector and the matrix-core paths serve them. */
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1, LORA_FP8E4M3 = 2 } lora_dtype;
 
 typedef int lora_status;
@@ -278,7 +278,7 @@ lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, cons
  * §16.4.4 add_lora_linear).  Same result as lora_shrink then lora_expand, with the
  * intermediate kept in the pool's workspace as k-split partial sums, added in
  * split order by the expand, so repeated calls are bitwise identical (and equal
- * to lora_shrink then lora_expand).  Long same-slot segments of bf16 pools go to
+ * to lora_shrink then lora_expand).  Long same-slot segments of bf16 and FP8 pools go to
  * the matrix cores (MFMA).  Two kernel launches per call.
  * Errors as lora_expand.
  */

@@ -279,7 +279,7 @@ rax::UView caller_u_view(const lora_pool* p, const lora_routing* r, float* u) {
 }
 
 bool use_mfma(const lora_pool* pool) {
-  return rax::kHaveMfmaPath && pool->wdtype == LORA_BF16 && env_int("RAXLORA_DISABLE_MFMA", 0) == 0;
+  return rax::kHaveMfmaPath && pool->wdtype != LORA_F32 && env_int("RAXLORA_DISABLE_MFMA", 0) == 0;
 }
 
 // Launch shape of a call, from host-known sizes only (T, S, the pool's shape): the

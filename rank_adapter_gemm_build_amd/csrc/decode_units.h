@@ -60,24 +60,6 @@ struct ShrinkRows {
   }
 };
 
-// One lane's 16-byte chunk of an A row as the dot products read it: as stored for
-// bf16 and fp32 pools; for FP8 pools 8 bytes, widened to 8 bf16 at use.
-template <typename TW> struct AChunk {
-  using type = uint4;
-  __device__ __forceinline__ static type load(const TW* p) { return ld16(p); }
-  __device__ __forceinline__ static uint4 widen(const type& c) { return c; }
-  __device__ __forceinline__ static type keep(const type& c, bool ok) { return keep_if(c, ok); }
-};
-template <> struct AChunk<uint8_t> {
-  using type = uint2;
-  __device__ __forceinline__ static type load(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ static uint4 widen(const type& c) { return fp8x8_to_bf16x8(c); }
-  __device__ __forceinline__ static type keep(const type& c, bool ok) {
-    const uint32_t m = ok ? 0xffffffffu : 0u;
-    return make_uint2(c.x & m, c.y & m);
-  }
-};
-
 // Partial sums of split sp (chunk steps sp + nsplit * m, m < ns) for the block's 16
 // rows and the tile's 4 token rows; tokens at or past nt contribute zero.  Returns
 // this lane's value after the reduce-scatter: row fb + lane / 4, token lane % 4.
@@ -90,7 +72,7 @@ __device__ __forceinline__ float shrink_block_partial(const PoolView& P, const S
   constexpr int E = Elem<TX>::kPerChunk;
   constexpr int CW = 64 * E;         // k elements of one wave-wide chunk step
   static_assert(Elem<TW>::kPerChunk == E, "weight and x chunks cover the same k range");
-  using AC = AChunk<TW>;
+  using AC = WChunk<TW>;
   const int lane = lane_id();
   float acc[64];
 #pragma unroll

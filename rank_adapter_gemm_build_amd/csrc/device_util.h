@@ -82,6 +82,32 @@ __device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
   return fp8x8_to_bf16x8(make_uint2((uint32_t)p0, (uint32_t)p1));
 }
 
+// One lane's 8 consecutive weight values as a bf16 operand (dot products, MFMA
+// fragments): one 16-byte chunk for bf16 (and fp32: 4 values) pools; 8 bytes for
+// FP8 pools, widened to 8 bf16 at use.  keep() zeroes a chunk that is not used.
+template <typename TW> struct WChunk {
+  using type = uint4;
+  __device__ __forceinline__ static type load(const TW* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static uint4 widen(const type& c) { return c; }
+  __device__ __forceinline__ static type keep(const type& c, bool ok) {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return make_uint4(c.x & m, c.y & m, c.z & m, c.w & m);
+  }
+};
+template <> struct WChunk<uint8_t> {
+  using type = uint2;
+  __device__ __forceinline__ static type load(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ static uint4 widen(const type& c) { return fp8x8_to_bf16x8(c); }
+  __device__ __forceinline__ static type keep(const type& c, bool ok) {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return make_uint2(c.x & m, c.y & m);
+  }
+};
+// x chunks of a shrink with weights TW: bf16 as given, put on the e4m3 grid for FP8 pools
+template <typename TW> __device__ __forceinline__ uint4 x_for(uint4 x) {
+  if constexpr (sizeof(TW) == 1) return bf16x8_to_fp8_grid(x); else return x;
+}
+
 // -------------------------------------------------------------- lane chunks
 // Every lane moves 16 bytes per load: 8 bf16 or 4 fp32 elements.
 template <typename T> struct Elem;

@@ -162,7 +162,7 @@ __host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + 
 // workgroups 1-7 are idle, so the others keep their XCD numbering), and the units
 // take their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead
 // of the routing outputs being written meanwhile.  T is the type of x, TW of the
-// weights (T, or FP8 with bf16 x: vector units only).
+// weights (T, or FP8 with bf16 x).
 template <typename T, typename TW, bool SELF>
 __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
                                                     int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
       if (d < plan.n_dec_blocks) shrink_decode_unit_self<T, TW>(P, R, sr.ids, x, ldx, U, plan, d, tok);
       return;
     }
-    if constexpr (sizeof(T) == 2 && sizeof(TW) == 2) {
+    if constexpr (sizeof(T) == 2 && sizeof(TW) <= 2) {
       // LDS: slot counts [kSelfRouteK], then the tile's tokens, then the batch's keys
       int* keys = sh + kSelfRouteK + kSelfRouteT;
       int ntiles;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
         const int first = ti * R.tile_m, len = min(R.tile_m, L - first);
         const SlotEntry e = P.table[slot];
         const uint16_t* __restrict__ xrow = x + (size_t)tok[first + min(lane_id() & 15, len - 1)] * ldx;
-        shrink_mfma_tile(P, e, xrow, U, slot, p0 + first, len, rg, part, plan.nsplit);
+        shrink_mfma_tile<TW>(P, e, xrow, U, slot, p0 + first, len, rg, part, plan.nsplit);
       }
     }
     return;
@@ -216,14 +216,14 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
     if (d < plan.n_dec_blocks) shrink_decode_unit<T, TW>(P, R, x, ldx, U, plan, d);
     return;
   }
-  if constexpr (sizeof(T) == 2 && sizeof(TW) == 2) {
+  if constexpr (sizeof(T) == 2 && sizeof(TW) <= 2) {
     // items part-major: an XCD's stretch covers whole k parts (with 8 parts, one
     // each), so the rows of A and the k-slices of x it reads are its own
     const int ntiles = R.meta[kMetaTiles], per_part = ntiles * plan.nrg;
     for (MfmaItems it(b, n_mfma_blocks, per_part * plan.nsplit); it.j < it.end; it.j += it.step) {
       const int part = it.j / per_part, rem = it.j - part * per_part;
       const int tile = rem / plan.nrg, rg = rem - tile * plan.nrg;
-      shrink_mfma_unit(P, R, x, ldx, U, tile, rg, part, plan.nsplit);
+      shrink_mfma_unit<TW>(P, R, x, ldx, U, tile, rg, part, plan.nsplit);
     }
   }
 }
@@ -250,7 +250,7 @@ hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, cons
   if (plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
       plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
       plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
-      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)) ||
+      (plan.use_mfma && (wdtype == LORA_F32 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)) ||
       (sr && (!sr->ids || R.T < 1 || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)))
     return hipErrorInvalidValue;
   if (wdtype == LORA_BF16)
@@ -536,10 +536,10 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UVi
     if (d < plan.n_dec_blocks) expand_decode_item<TW, TY, (KSM <= 2 ? 2 * KSM : 0)>(P, R, U, y, ldy, plan, d, smem);
     return;
   }
-  if constexpr (sizeof(TW) == 2) {
+  if constexpr (sizeof(TW) <= 2) {   // bf16 and FP8 weights
     for (MfmaItems it(b, n_mfma_blocks, R.meta[kMetaTiles] * plan.n_mgroups); it.j < it.end; it.j += it.step) {
       const int tile = it.j / plan.n_mgroups, g = it.j - tile * plan.n_mgroups;
-      expand_mfma_unit<TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, smem);
+      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, smem);
     }
   }
 }
@@ -558,7 +558,7 @@ static void launch_expand_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream
 
 size_t expand_smem_bytes(int wdtype, int Rmax, int use_mfma) {
   size_t f = (size_t)expand_usm_floats(Rmax);
-  if (use_mfma && wdtype == LORA_BF16 && (size_t)kExpandMfmaWaveFloats > f) f = kExpandMfmaWaveFloats;
+  if (use_mfma && wdtype != LORA_F32 && (size_t)kExpandMfmaWaveFloats > f) f = kExpandMfmaWaveFloats;
   return f * sizeof(float);
 }
 
@@ -568,7 +568,7 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
   if (plan.xcd_group < 1 || plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
       (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
       plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
-      (plan.use_mfma && (wdtype != LORA_BF16 || plan.tile_slots < 1 || plan.n_mgroups < 1 ||
+      (plan.use_mfma && (wdtype == LORA_F32 || plan.tile_slots < 1 || plan.n_mgroups < 1 ||
                          (plan.cb != 1 && plan.cb != kMfmaColBlocksPerUnit))))
     return hipErrorInvalidValue;
   const int nm = plan.use_mfma ? mfma_blocks(plan.n_mgroups * plan.tile_slots) : 0;
@@ -582,7 +582,7 @@ hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteV
       launch_expand_w<uint16_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
     else
       launch_expand_w<uint16_t, float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
-  } else if (wdtype == LORA_FP8E4M3) {   // vector units only
+  } else if (wdtype == LORA_FP8E4M3) {
     if (ydtype == LORA_BF16)
       launch_expand_w<uint8_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
     else

@@ -50,56 +50,57 @@ constexpr int kDsPitch = kMfmaCols + 4;          // LDS row pitch (floats) of th
 constexpr int kExpandMfmaWaveFloats = kMfmaTileM * kDsPitch;   // LDS floats per expand wave
 
 // ------------------------------------------------------------------ shrink
-template <int NB>
+// TW: weight type (bf16, or FP8 widened to bf16 at use; x is bf16 for both)
+template <typename TW, int NB>
 struct ShrinkFrags {
   uint4 xa[kMfmaGroup];
-  uint4 wb[kMfmaGroup][NB];
+  typename WChunk<TW>::type wb[kMfmaGroup][NB];
 };
 
 // Loads of one group: raw values only, so that nothing consumes them before the
 // products (a consumer in the load phase would make the wave wait for the group
 // right after issuing it, defeating the double buffering).  Steps past the part's
 // end reload its last step (a cache hit); the products zero them.
-template <int NB>
-__device__ __forceinline__ void shrink_load_group(ShrinkFrags<NB>& f, const uint16_t* __restrict__ xrow,
-                                                  const uint16_t* const (&arow)[NB], int sg, int last, int k,
-                                                  int lk) {
+template <typename TW, int NB>
+__device__ __forceinline__ void shrink_load_group(ShrinkFrags<TW, NB>& f, const uint16_t* __restrict__ xrow,
+                                                  const TW* const (&arow)[NB], int sg, int last, int k, int lk) {
 #pragma unroll
   for (int g = 0; g < kMfmaGroup; ++g) {
     const int st = min(sg + g, last);
     const int colc = min(st * kMfmaK + 8 * lk, k - 8);
     f.xa[g] = ld16(xrow + colc);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) f.wb[g][b] = ld16(arow[b] + colc);
+    for (int b = 0; b < NB; ++b) f.wb[g][b] = WChunk<TW>::load(arow[b] + colc);
   }
 }
 
 // Products of one group; fragments of steps outside [sg, s1), of rows past the last
 // valid one and of tokens past the tile's length are zeroed here.
-template <int NB>
-__device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<NB>& f, bool tval, const bool (&rval)[NB], int sg,
-                                                 int s1, int k, int lk, f32x4_t (&acc)[NB]) {
+template <typename TW, int NB>
+__device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<TW, NB>& f, bool tval, const bool (&rval)[NB],
+                                                 int sg, int s1, int k, int lk, f32x4_t (&acc)[NB]) {
+  using W = WChunk<TW>;
 #pragma unroll
   for (int g = 0; g < kMfmaGroup; ++g) {
     const bool inb = sg + g < s1 && (sg + g) * kMfmaK + 8 * lk < k;  // k % 8 == 0: chunks wholly in or out
-    const uint4 xa = keep_if(f.xa[g], tval && inb);
+    const uint4 xa = keep_if(x_for<TW>(f.xa[g]), tval && inb);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(keep_if(f.wb[g][b], rval[b])), acc[b],
-                                                       0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(W::widen(W::keep(f.wb[g][b], rval[b]))),
+                                                       acc[b], 0, 0, 0);
   }
 }
 
 // Products of rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1): lane
 // holds D[token 4 * lk + i][row fr0 + 16 b + lr] in acc[b][i].
-template <int NB>
+template <typename TW, int NB>
 __device__ __forceinline__ void shrink_mfma_acc(const PoolView& P, const uint16_t* __restrict__ xrow, int slot, int r,
                                                 int len, int fr0, int s0, int s1, f32x4_t (&acc)[NB]) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int F = P.N * r;
   const bool tval = lr < len;
-  const uint16_t* Aslot = static_cast<const uint16_t*>(P.A) + (size_t)slot * P.N * P.Rmax * P.k;
-  const uint16_t* arow[NB];
+  const TW* Aslot = static_cast<const TW*>(P.A) + (size_t)slot * P.N * P.Rmax * P.k;
+  const TW* arow[NB];
   bool rval[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -112,16 +113,16 @@ __device__ __forceinline__ void shrink_mfma_acc(const PoolView& P, const uint16_
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int last = max(s1 - 1, 0);
-  ShrinkFrags<NB> f0, f1;
-  shrink_load_group<NB>(f0, xrow, arow, s0, last, P.k, lk);
+  ShrinkFrags<TW, NB> f0, f1;
+  shrink_load_group<TW, NB>(f0, xrow, arow, s0, last, P.k, lk);
   for (int sg = s0; sg < s1; sg += 2 * kMfmaGroup) {
-    shrink_load_group<NB>(f1, xrow, arow, sg + kMfmaGroup, last, P.k, lk);
+    shrink_load_group<TW, NB>(f1, xrow, arow, sg + kMfmaGroup, last, P.k, lk);
     sched_fence();
-    shrink_mma_group<NB>(f0, tval, rval, sg, s1, P.k, lk, acc);
+    shrink_mma_group<TW, NB>(f0, tval, rval, sg, s1, P.k, lk, acc);
     sched_fence();
-    shrink_load_group<NB>(f0, xrow, arow, sg + 2 * kMfmaGroup, last, P.k, lk);
+    shrink_load_group<TW, NB>(f0, xrow, arow, sg + 2 * kMfmaGroup, last, P.k, lk);
     sched_fence();
-    shrink_mma_group<NB>(f1, tval, rval, sg + kMfmaGroup, s1, P.k, lk, acc);
+    shrink_mma_group<TW, NB>(f1, tval, rval, sg + kMfmaGroup, s1, P.k, lk, acc);
     sched_fence();
   }
 }
@@ -135,13 +136,13 @@ __device__ __forceinline__ void mfma_part_range(int k, int part, int nsplit, int
 }
 
 // Rows fr0 .. fr0 + 16 * NB of one tile over k steps [s0, s1); writes partial `part`.
-template <int NB>
+template <typename TW, int NB>
 __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const uint16_t* __restrict__ xrow, const UView& U,
                                                  int slot, int r, int p0, int len, int fr0, int part, int s0, int s1) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int F = P.N * r;
   f32x4_t acc[NB];
-  shrink_mfma_acc<NB>(P, xrow, slot, r, len, fr0, s0, s1, acc);
+  shrink_mfma_acc<TW, NB>(P, xrow, slot, r, len, fr0, s0, s1, acc);
   // lane holds D[token 4 * lk + i][row fr0 + 16 b + lr]; rows by sorted position
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -162,6 +163,7 @@ __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const uint16
 // (xrow: this lane's x row, token lane % 16, clamped into the tile), row group rg
 // (rows 64 rg .. 64 rg + 63), k part `part` of nsplit.  Wave-uniform.  Parts with no
 // k steps write zeros.
+template <typename TW>
 __device__ __forceinline__ void shrink_mfma_tile(const PoolView& P, const SlotEntry& e,
                                                  const uint16_t* __restrict__ xrow, const UView& U, int slot, int p0,
                                                  int len, int rg, int part, int nsplit) {
@@ -171,16 +173,17 @@ __device__ __forceinline__ void shrink_mfma_tile(const PoolView& P, const SlotEn
   mfma_part_range(P.k, part, nsplit, s0, s1);
   const int nb = min(4, (F - fr0 + 15) / 16);
   if (nb == 4)
-    shrink_mfma_rows<4>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<TW, 4>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else if (nb == 3)
-    shrink_mfma_rows<3>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<TW, 3>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else if (nb == 2)
-    shrink_mfma_rows<2>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<TW, 2>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
   else
-    shrink_mfma_rows<1>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
+    shrink_mfma_rows<TW, 1>(P, xrow, U, slot, r, p0, len, fr0, part, s0, s1);
 }
 
 // One shrink unit: tile `tile` of the routing's list.
+template <typename TW>
 __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
                                                  int ldx, const UView& U, int tile, int rg, int part, int nsplit) {
   const int4 td = R.tiles[tile];
@@ -188,7 +191,7 @@ __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteV
   // the slot-table entry and this lane's token id (token lane % 16) in one round trip
   const SlotEntry e = P.table[slot];
   const uint16_t* __restrict__ xrow = x + (size_t)R.sorted[p0 + min(lane_id() & 15, len - 1)] * ldx;
-  shrink_mfma_tile(P, e, xrow, U, slot, p0, len, rg, part, nsplit);
+  shrink_mfma_tile<TW>(P, e, xrow, U, slot, p0, len, rg, part, nsplit);
 }
 
 // ------------------------------------------------------------------ expand
@@ -323,17 +326,19 @@ struct ExpandRows16 {
 // stored) and the B fragments of the NKS rank steps (a lane whose ranks lie past the
 // slot's Bk stride reads the rank-0 fragment of its column and zeroes it; columns
 // past the slice read column 0, never stored).
-template <typename TY, int NKS, int BC>
+template <typename TW, typename TY, int NKS, int BC>
 struct ExpandMfmaBlock {
   using Rows = ExpandRows16<TY, BC>;
+  using W = WChunk<TW>;
   static constexpr int YC = Rows::YC, RC = Rows::RC, YCH = Rows::YCH;
   static constexpr int NCB = BC / 16;                            // 16-column strips
-  static constexpr int kRegs = YCH + NCB * NKS;                  // 16-byte chunks per lane
+  // 16-byte chunks per lane (FP8 B fragments are 8 bytes)
+  static constexpr int kRegs = YCH + NCB * NKS * (int)sizeof(typename W::type) / 16;
   uint4 yv[YCH];
-  uint4 bv[NKS][NCB];
+  typename W::type bv[NKS][NCB];
   int c0;
 
-  __device__ __forceinline__ void issue(const Rows& Y, const uint16_t* __restrict__ bk, int rs, int dn, int c0_,
+  __device__ __forceinline__ void issue(const Rows& Y, const TW* __restrict__ bk, int rs, int dn, int c0_,
                                         int nks) {
     const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
     c0 = c0_;
@@ -349,7 +354,7 @@ struct ExpandMfmaBlock {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const int col = c0 + 16 * cb + lr;
-          bv[ks][cb] = ld16(bk + (size_t)(col < dn ? col : 0) * rs + jc);
+          bv[ks][cb] = W::load(bk + (size_t)(col < dn ? col : 0) * rs + jc);
         }
       }
     }
@@ -369,7 +374,7 @@ struct ExpandMfmaBlock {
         const bool kin = ks * kMfmaK + 8 * lk < rs;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const uint4 b = keep_if(bv[ks][cb], kin);
+          const uint4 b = W::widen(W::keep(bv[ks][cb], kin));
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uh[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ul[ks]), as_bf16x8(b), acc[cb], 0, 0, 0);
         }
@@ -415,11 +420,11 @@ struct ExpandMfmaBlock {
 
 // Block width of the expand body: 128 columns when two blocks' loads fit in 12
 // chunks per lane, else 64 when they do, else 128 without overlap.
-template <typename TY, int NKS>
+template <typename TW, typename TY, int NKS>
 struct ExpandBlockWidth {
-  static constexpr int value = ExpandMfmaBlock<TY, NKS, 128>::kRegs <= 12  ? 128
-                               : ExpandMfmaBlock<TY, NKS, 64>::kRegs <= 12 ? 64
-                                                                           : 128;
+  static constexpr int value = ExpandMfmaBlock<TW, TY, NKS, 128>::kRegs <= 12  ? 128
+                               : ExpandMfmaBlock<TW, TY, NKS, 64>::kRegs <= 12 ? 64
+                                                                               : 128;
 };
 
 // Body of one expand unit with NKS rank steps of 32 (nks <= NKS of them real), NSB
@@ -431,14 +436,14 @@ struct ExpandBlockWidth {
 // time when even that does not fit).  A block past the slice's end loads clamped
 // addresses and stores nothing.  There are no branches between a load and its use,
 // so the compiler keeps the batches as written.
-template <typename TY, int NKS, int NSB, int CB>
+template <typename TW, typename TY, int NKS, int NSB, int CB>
 __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, TY* __restrict__ y, int ldy,
-                                                 const uint16_t* __restrict__ bk, int rs, int n, int on, int dn,
+                                                 const TW* __restrict__ bk, int rs, int n, int on, int dn,
                                                  int c00, int p0, int len, int tok, int r, int nks, float scale,
                                                  float* __restrict__ ds) {
-  constexpr int BC = ExpandBlockWidth<TY, NKS>::value;
+  constexpr int BC = ExpandBlockWidth<TW, TY, NKS>::value;
   constexpr int NB = CB * (kMfmaCols / BC);                     // blocks of the unit
-  using Blk = ExpandMfmaBlock<TY, NKS, BC>;
+  using Blk = ExpandMfmaBlock<TW, TY, NKS, BC>;
   constexpr bool kPipe = Blk::kRegs <= 12;
   typename Blk::Rows Y;
   Y.load(tok, y, ldy, on);
@@ -486,7 +491,7 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
 // most (1, 2, 4 or 8); the body is specialised for the tile's own step count (1 or
 // 2; for KSM >= 4 one body with run-time bounds) and split batches.  Wave-uniform; ds is the wave's
 // kExpandMfmaWaveFloats floats of LDS.
-template <typename TY, int KSM>
+template <typename TW, typename TY, int KSM>
 __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
                                                  TY* __restrict__ y, int ldy, int tile, int grp, int cb,
                                                  float* __restrict__ ds) {
@@ -501,10 +506,10 @@ __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteV
   const int tok = R.sorted[p0 + min(lane_id() & 15, len - 1)];
   if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
   const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
-  const uint16_t* __restrict__ bk = static_cast<const uint16_t*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
+  const TW* __restrict__ bk = static_cast<const TW*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
   const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
 #define RAX_EXPAND_BODY(NK, NB, CB) \
-  expand_mfma_body<TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tok, r, nks, e.scale, ds)
+  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tok, r, nks, e.scale, ds)
 #define RAX_EXPAND_BODIES(NK)                                                          \
   do {                                                                                 \
     if (cb == 1) {                                                                     \
