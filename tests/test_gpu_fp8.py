@@ -109,14 +109,23 @@ def test_fp8_registration_bit_exact(rx, premultiply, rslora):
     pool.close()
 
 
-def test_fp8_exact_integer_case(rx):
+@pytest.mark.parametrize("mode", ["default", "vector", "all-mfma"])
+def test_fp8_exact_integer_case(rx, mode):
     """Small integers everywhere: every product and partial sum is exact in fp32, so
-    the fp32 output equals the definition exactly."""
-    T, S, k, slices, Rmax = 70, 5, 512, [256, 64], 16
+    the fp32 output equals the definition exactly, on the vector units, the matrix
+    cores and the default split between them."""
+    import os
+    T, S, k, slices, Rmax = 70, 5, 512, [256, 64], 40
     ranks, A, B, ids, x, alpha = _case(11, T, S, k, slices, Rmax, integer=True)
-    pool = _pool(rx, S, Rmax, k, slices, T, ranks, A, B, alpha)
-    D = sum(slices)
-    y = _run(rx, pool, ids, x, np.zeros((T, D), dtype=np.float32), "f32")
+    env = {"vector": {"RAXLORA_DISABLE_MFMA": "1"}, "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}}.get(mode, {})
+    os.environ.update(env)
+    try:
+        pool = _pool(rx, S, Rmax, k, slices, T, ranks, A, B, alpha)
+        D = sum(slices)
+        y = _run(rx, pool, ids, x, np.zeros((T, D), dtype=np.float32), "f32")
+    finally:
+        for key in env:
+            os.environ.pop(key, None)
     ref = _oracle(ranks, A, B, ids, x, alpha, S, slices, Rmax, np.zeros((T, D)))
     assert np.array_equal(from_device(y), ref)
     pool.close()
