@@ -57,6 +57,7 @@ def step_accounting(W, mfma_min: int, use_mfma: bool):
     acc = {"shrink": 0, "expand": 0}
     split = {"shrink_decode": 0, "expand_decode": 0, "shrink_mfma": 0, "expand_mfma": 0}
     flops = 0
+    mfma_flops = 0
     for mod in W.modules:
         D = sum(mod.slices)
         for s, r in W.ranks.items():
@@ -71,6 +72,9 @@ def step_accounting(W, mfma_min: int, use_mfma: bool):
             split[f"shrink_{fam}"] += sb
             split[f"expand_{fam}"] += eb
             flops += 2 * L * r * (mod.k * len(mod.slices) + D)
+            if fam == "mfma":
+                mfma_flops += 2 * L * r * (mod.k * len(mod.slices) + D)
+    split["mfma_flops"] = mfma_flops
     return acc, flops, split
 
 
@@ -620,6 +624,17 @@ def run(args):
     embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
     fp8 = None if args.no_extras else measure_fp8(torch, rx, lib, W, src, args, step_bytes, acc)
 
+    # matrix-core path: its algorithmic FLOPs over the shrink + expand kernel time of a
+    # step (a lower bound of the MFMA utilisation: those launches also run the vector
+    # units' work; the executed MFMA FLOPs from counters are in profiles/mfma_*.md)
+    mfma_flops = by_path.pop("mfma_flops", 0)
+    kt = sum(v["avg_us"] * v["launches_per_step"] for k, v in kern.items() if k in ("shrink", "expand"))
+    mfma_path = None
+    if mfma_flops and kt > 0:
+        tf = mfma_flops / (kt * 1e-6) / 1e12
+        mfma_path = {"algorithmic_flop_per_step": int(mfma_flops), "tflops_over_shrink_expand_time": round(tf, 2),
+                     "peak_tflops_bf16_dense": 2500.0, "frac": round(tf / 2500.0, 5)}
+
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -635,7 +650,8 @@ def run(args):
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
                   "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
                   "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest(),
-                  "graph_and_overlap": graph_overlap, "embedding_lora": embedding, "fp8_pools": fp8},
+                  "graph_and_overlap": graph_overlap, "embedding_lora": embedding, "fp8_pools": fp8,
+                  "mfma_path": mfma_path},
     }
     for inst in insts:
         inst.close()
