@@ -186,6 +186,10 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
       // LDS: slot counts [kSelfRouteK], then the tile's tokens, then the batch's keys
       int* keys = sh + kSelfRouteK + kSelfRouteT;
       int ntiles;
+      // pools of up to 64 slots: lane l holds slot l's table entry, loaded with the ids,
+      // so a tile's entry needs no round trip of its own
+      const bool table_in_lanes = P.S <= 64;
+      const int4 te = *reinterpret_cast<const int4*>(P.table + min(lane_id(), P.S - 1));
       {
         BatchKeys K;
         K.load(sr.ids, R.T, R.S);
@@ -204,7 +208,15 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, con
         K.segment(slot, L, p0, tok);
         wave_lds_sync();
         const int first = ti * R.tile_m, len = min(R.tile_m, L - first);
-        const SlotEntry e = P.table[slot];
+        SlotEntry e;
+        if (table_in_lanes) {
+          e.rank = __builtin_amdgcn_readfirstlane(__shfl(te.x, slot));   // wave-uniform
+          e.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__shfl(te.y, slot)));
+          e.slice_mask = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(te.z, slot));
+          e.pad = 0;
+        } else {
+          e = P.table[slot];
+        }
         const uint16_t* __restrict__ xrow = x + (size_t)tok[first + min(lane_id() & 15, len - 1)] * ldx;
         shrink_mfma_tile<TW>(P, e, xrow, U, slot, p0 + first, len, rg, part, plan.nsplit);
       }
