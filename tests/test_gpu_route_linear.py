@@ -166,3 +166,40 @@ def test_route_linear_no_lora_and_errors(rx):
                                y.data_ptr(), y.stride(0), rx.LORA_BF16, None)
     assert st == rx.LORA_ERR_SHAPE
     pool.close(); R.close(); R2.close()
+
+
+@pytest.mark.parametrize("num", [2, 4])
+def test_route_linear_full_size_matches_two_calls(rx, num):
+    """At the full decode workloads (the launch shapes bench.py times: T = 64 and 8
+    slots; T = 256, 64 slots and the packed QKV / gate_up / down modules), the fused
+    call of the first module and the following lora_linear calls are bitwise equal to
+    lora_build_routing + lora_linear (itself checked against the oracle on sampled
+    rows at these sizes)."""
+    import torch
+    from synthetic import workload
+    W = workload(num)
+    _log(f"workload {num}: T={W.T} S={W.S} modules={[m.name for m in W.modules]}")
+    ids = _ids_tensor(W)
+    outs = []
+    for fused in (False, True):
+        pools = [make_pool(rx, W, m) for m in W.modules]
+        R = rx.Routing(0, W.T, W.S)
+        ys = []
+        for i, (m, p) in enumerate(zip(W.modules, pools)):
+            y = to_device(m.y_base if m.y_base is not None else np.zeros((W.T, sum(m.slices)), np.float32),
+                          "bf16" if m.y_base is not None else "f32")
+            x = to_device(m.x, W.dtype)
+            if i == 0 and fused:
+                rx.route_linear(p, R, ids, x, y)
+            else:
+                if i == 0:
+                    R.build(ids)
+                rx.linear(p, R, x, y)
+            ys.append(y)
+        torch.cuda.synchronize()
+        outs.append([bits(y) for y in ys])
+        for p in pools:
+            p.close()
+        R.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
