@@ -549,9 +549,11 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UVi
     return;
   }
   if constexpr (sizeof(TW) <= 2) {   // bf16 and FP8 weights
+    LaneTable lt;
+    lt.load(P);   // in flight with the tile count
     for (MfmaItems it(b, n_mfma_blocks, R.meta[kMetaTiles] * plan.n_mgroups); it.j < it.end; it.j += it.step) {
       const int tile = it.j / plan.n_mgroups, g = it.j - tile * plan.n_mgroups;
-      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, smem);
+      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, lt, smem);
     }
   }
 }

@@ -340,13 +340,23 @@ struct ExpandMfmaBlock {
 
   __device__ __forceinline__ void issue(const Rows& Y, const TW* __restrict__ bk, int rs, int dn, int c0_,
                                         int nks) {
-    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    issue_y(Y, dn, c0_);
+    issue_b(bk, rs, dn, c0_, nks);
+  }
+  // the two halves, for a first block whose B can go out before the tile's token ids
+  // (and so its y rows) are known
+  __device__ __forceinline__ void issue_y(const Rows& Y, int dn, int c0_) {
+    const int lane = lane_id();
     c0 = c0_;
 #pragma unroll
     for (int q = 0; q < YCH; ++q) {
       const int cc = ((q * 64 + lane) % RC) * YC;
       yv[q] = ld16(Y.row[q] + min(c0 + cc, dn - YC));
     }
+  }
+  __device__ __forceinline__ void issue_b(const TW* __restrict__ bk, int rs, int dn, int c0_, int nks) {
+    const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
+    c0 = c0_;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks < nks) {   // compile-time true unless NKS covers a range of rank-step counts
@@ -439,20 +449,27 @@ struct ExpandBlockWidth {
 template <typename TW, typename TY, int NKS, int NSB, int CB>
 __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, TY* __restrict__ y, int ldy,
                                                  const TW* __restrict__ bk, int rs, int n, int on, int dn,
-                                                 int c00, int p0, int len, int tok, int r, int nks, float scale,
-                                                 float* __restrict__ ds) {
+                                                 int c00, int p0, int len, const int* __restrict__ tokp, int r,
+                                                 int nks, float scale, float* __restrict__ ds) {
   constexpr int BC = ExpandBlockWidth<TW, TY, NKS>::value;
   constexpr int NB = CB * (kMfmaCols / BC);                     // blocks of the unit
   using Blk = ExpandMfmaBlock<TW, TY, NKS, BC>;
   constexpr bool kPipe = Blk::kRegs <= 12;
   typename Blk::Rows Y;
-  Y.load(tok, y, ldy, on);
   uint4 uh[NKS], ul[NKS];
   Blk b0, b1;
   if constexpr (NSB > 0) {
+    // this lane's token id first, then the partials and the first block's B: loads
+    // complete in order, so the y rows can be addressed (and their loads issued) as
+    // soon as the token id is in, while the rest is still in flight
+    const int tok = *tokp;
+    sched_fence();
     UPartials<NSB> up;
     up.load(U, n, p0, len, r, 0);
-    b0.issue(Y, bk, rs, dn, c00, nks);
+    b0.issue_b(bk, rs, dn, c00, nks);
+    sched_fence();
+    Y.load(tok, y, ldy, on);
+    b0.issue_y(Y, dn, c00);
     sched_fence();
     up.finish(U, len, r, 0, uh[0], ul[0]);
 #pragma unroll
@@ -462,6 +479,7 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
       uq.finish(U, len, r, ks, uh[ks], ul[ks]);
     }
   } else {
+    Y.load(*tokp, y, ldy, on);
     b0.issue(Y, bk, rs, dn, c00, nks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) u_frag_by_token(R, U, n, p0, len, r, ks, uh[ks], ul[ks]);
@@ -491,25 +509,51 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
 // most (1, 2, 4 or 8); the body is specialised for the tile's own step count (1 or
 // 2; for KSM >= 4 one body with run-time bounds) and split batches.  Wave-uniform; ds is the wave's
 // kExpandMfmaWaveFloats floats of LDS.
+// Slot-table entries held lane-wise (pools of up to 128 slots): lane l holds slots l
+// and l + 64, loaded once per wave; a unit picks its slot's entry with lane
+// shuffles instead of a round trip of its own.
+struct LaneTable {
+  int4 t0, t1;
+  bool on;
+  __device__ __forceinline__ void load(const PoolView& P) {
+    on = P.S <= 128;
+    const int lane = lane_id();
+    t0 = *reinterpret_cast<const int4*>(P.table + min(lane, P.S - 1));
+    t1 = *reinterpret_cast<const int4*>(P.table + min(lane + 64, P.S - 1));
+  }
+  // slot < P.S, wave-uniform
+  __device__ __forceinline__ SlotEntry get(const PoolView& P, int slot) const {
+    SlotEntry e;
+    if (!on) return P.table[slot];
+    const int l = slot & 63;
+    const int4 a = slot < 64 ? t0 : t1;
+    e.rank = __builtin_amdgcn_readfirstlane(__shfl(a.x, l));
+    e.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__shfl(a.y, l)));
+    e.slice_mask = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(a.z, l));
+    e.pad = 0;
+    return e;
+  }
+};
+
 template <typename TW, typename TY, int KSM>
 __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
                                                  TY* __restrict__ y, int ldy, int tile, int grp, int cb,
-                                                 float* __restrict__ ds) {
+                                                 const LaneTable& lt, float* __restrict__ ds) {
   int blk0;
   const int n = mfma_group_slice(P, grp, cb, blk0);
   if (n < 0) return;
   const int on = P.o[n], dn = P.d[n], c00 = blk0 * kMfmaCols;
   const int4 td = R.tiles[tile];
   const int slot = td.x, p0 = td.y, len = td.z;
-  // the slot-table entry and this lane's token id (token lane % 16) in one round trip
-  const SlotEntry e = P.table[slot];
-  const int tok = R.sorted[p0 + min(lane_id() & 15, len - 1)];
+  const SlotEntry e = lt.get(P, slot);
+  // this lane's token id (token lane % 16): loaded by the body ahead of the partials
+  const int* __restrict__ tokp = R.sorted + p0 + min(lane_id() & 15, len - 1);
   if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
   const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
   const TW* __restrict__ bk = static_cast<const TW*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
   const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
 #define RAX_EXPAND_BODY(NK, NB, CB) \
-  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tok, r, nks, e.scale, ds)
+  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tokp, r, nks, e.scale, ds)
 #define RAX_EXPAND_BODIES(NK)                                                          \
   do {                                                                                 \
     if (cb == 1) {                                                                     \
