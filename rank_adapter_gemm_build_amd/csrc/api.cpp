@@ -398,6 +398,7 @@ lora_status route_linear_impl(const lora_pool* pool, lora_routing* routing, cons
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   routing->T = T;
   st = shrink_join_expand(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready, ids);
+  if (st != LORA_OK) routing->T = -1;   // the routing may not have been built: unusable until rebuilt
   return st == LORA_OK ? ok() : st;
 }
 
@@ -875,7 +876,10 @@ lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, c
   rax::SelfRoute sr{slot_ids, route_out(routing)};
   hipError_t e = rax::launch_embed_gather_tok(pool->wdtype, pool_view(pool), route_view(routing), slot_ids, vocab_ids,
                                               pool->k, U, fused ? &sr : nullptr, stream, timer_for(rax::kKGather));
-  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if (e != hipSuccess) {
+    if (fused) routing->T = -1;   // the routing was not built: unusable until rebuilt
+    return hip_fail(e, "gather launch");
+  }
   if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream)) != LORA_OK) return st;
   return ok();
 }
