@@ -131,8 +131,37 @@ def test_null_arguments_rejected_without_device():
     assert rx.lib.lora_shrink(None, None, None, 8, None, None) == rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_expand(None, None, None, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_linear(None, None, None, 8, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_route_linear(None, None, None, 0, None, 8, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_linear_join(None, None, None, 8, None, 8, rx.LORA_BF16, None, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_route_linear_join(None, None, None, 0, None, 8, None, 8, rx.LORA_BF16, None, None) == \
+        rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_build_routing_seq(None, None, 0, 1, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_embedding_pool_create(None, 0, 4, 16, 100, 64, rx.LORA_BF16, 8) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_embedding(None, None, None, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_route_embedding(None, None, None, 0, None, None, 8, rx.LORA_BF16, None) == \
+        rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_pool_destroy(None) == rx.LORA_OK
     assert rx.lib.lora_routing_destroy(None) == rx.LORA_OK
+
+
+def test_dtype_enum_matches_binding():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    enum = re.search(r"typedef enum \{([^}]*)\} lora_dtype;", text).group(1)
+    vals = dict((k.strip(), int(v)) for k, v in re.findall(r"(LORA_\w+)\s*=\s*(\d+)", enum))
+    assert vals == {"LORA_F32": rx.LORA_F32, "LORA_BF16": rx.LORA_BF16, "LORA_FP8E4M3": rx.LORA_FP8E4M3}
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 4, 16, 100, 64, rx.LORA_FP8E4M3, 8), rx.LORA_ERR_DTYPE),   # FP8 embedding pools are not offered
+    ((0, 4, 16, 100, 60, rx.LORA_BF16, 8), rx.LORA_ERR_ALIGN),      # output width % 8
+    ((0, 4, 0, 100, 64, rx.LORA_BF16, 8), rx.LORA_ERR_SHAPE),       # rank 0
+    ((0, 4, 16, 0, 64, rx.LORA_BF16, 8), rx.LORA_ERR_SHAPE),        # empty vocabulary
+])
+def test_embedding_pool_create_validation(args, code):
+    h = C.c_void_p()
+    st = rx.lib.lora_embedding_pool_create(C.byref(h), *args)
+    assert st == code, (rx.STATUS.get(st), rx.lora_last_error())
+    assert h.value is None
 
 
 def test_valid_create_reports_missing_device():
