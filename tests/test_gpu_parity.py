@@ -506,3 +506,25 @@ def test_shrink_matrix_cores_match_oracle(rx, S):
     assert not np.isnan(ug[mask]).any()
     assert np.abs(ug[mask] - u_ref[mask]).max() / np.abs(u_ref[mask]).max() < 1e-4
     pool.close(); R.close()
+
+
+@pytest.mark.parametrize("case", ["max-slots", "max-in-features"])
+def test_largest_pool_shapes(rx, case):
+    """The largest shapes the boundary admits: 1024 slots (no rank-ordered dispatch,
+    slot-table entries loaded per unit instead of held lane-wise, the workgroup
+    routing kernel with a 1025-key histogram), and in_features = 65536 (16 k splits
+    of 8 chunk steps each in the decode shrink)."""
+    import torch
+    if case == "max-slots":
+        ranks = {s: 1 + (s * 7) % 16 for s in range(0, 1024, 3)}
+        W = small_case(801, T=700, S=1024, k=512, slices=[256, 64], Rmax=16, ranks=ranks, invalid=4)
+    else:
+        W = small_case(802, T=0, S=3, k=65536, slices=[128], Rmax=8, segments=[1, 3, 20, 2])
+    mod = W.modules[0]
+    _log(f"{case}: T={W.T} S={W.S} k={mod.k} slices={mod.slices}")
+    ads = oracle_adapters(W, mod)
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(mod.slices))), ads, mod.slices, W.ids, W.S, "bf16",
+                       max_rank=W.Rmax)
+    y = _run_linear(rx, W, mod, np.zeros((W.T, sum(mod.slices)), dtype=np.float32), "f32")
+    err = check_close(from_device(y), ref, "bf16", f"delta ({case})")
+    _log(f"  normwise rel err {err:.2e}")
