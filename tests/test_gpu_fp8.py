@@ -169,3 +169,41 @@ def test_fp8_route_linear_matches_two_calls(rx):
     torch.cuda.synchronize()
     assert np.array_equal(bits(y1), bits(y2))
     pool.close(); R.close()
+
+
+@pytest.mark.parametrize("num", [2, 4])
+def test_fp8_full_workload_sampled_rows(rx, num):
+    """The decode workloads at full size with every A and B put on the e4m3 grid (as
+    the bench's FP8 measurement does), in the launch configuration it times (fused
+    call for the first module); sampled rows against the oracle's FP8 path."""
+    import torch
+    from synthetic import workload
+    W = workload(num)
+    rng = np.random.default_rng(900 + num)
+    ids = torch.from_numpy(np.ascontiguousarray(W.ids, dtype=np.int32)).cuda()
+    R = rx.Routing(0, W.T, W.S)
+    keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
+    rows = np.array(sorted(set(rng.choice(W.T, size=min(40, W.T), replace=False).tolist())
+                           | set(np.nonzero(keys == keys[0])[0].tolist())))
+    for i, mod in enumerate(W.modules):
+        _log(f"fp8 workload {num} module {mod.name} k={mod.k} slices={mod.slices}")
+        A = {s: [_fp8_bytes(O.bf16_bits_to_f64(a)) for a in mod.A[s]] for s in W.ranks}
+        B = {s: [_fp8_bytes(O.bf16_bits_to_f64(b)) for b in mod.B[s]] for s in W.ranks}
+        pool = rx.Pool(0, W.S, W.Rmax, mod.k, mod.slices, rx.LORA_FP8E4M3, W.T)
+        for s, r in W.ranks.items():
+            pool.register(s, A[s], B[s], W.alpha[s], r, W.rslora, W.adapter_scale)
+        yb = mod.y_base if mod.y_base is not None else _bf16(rng.standard_normal((W.T, sum(mod.slices))))
+        y = to_device(yb, "bf16")
+        if i == 0:
+            rx.route_linear(pool, R, ids, to_device(mod.x, "bf16"), y)
+        else:
+            rx.linear(pool, R, to_device(mod.x, "bf16"), y)
+        torch.cuda.synchronize()
+        ads = {s: O.Adapter(rank=r, A=[O.fp8_e4m3_decode(a) for a in A[s]], B=[O.fp8_e4m3_decode(b) for b in B[s]],
+                            alpha=W.alpha[s], rslora=W.rslora, adapter_scale=W.adapter_scale)
+               for s, r in W.ranks.items()}
+        ref = O.lora_apply_fp8(O.bf16_bits_to_f64(mod.x)[rows], O.bf16_bits_to_f64(yb)[rows], ads, mod.slices,
+                               W.ids[rows], W.S, max_rank=W.Rmax)
+        check_close(from_device(y)[rows], ref, "bf16", f"fp8 workload {num} {mod.name}")
+        pool.close()
+    R.close()
