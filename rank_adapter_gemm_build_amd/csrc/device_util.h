@@ -65,6 +65,8 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 w, float (&v)[8]) {
   v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1]; v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
 }
 constexpr float kFp8Max = 448.f;
+// clamp to [-448, 448] keeping NaN (a comparison with NaN is false), as torch's clamp does
+__device__ __forceinline__ float fp8_clamp(float v) { return v > kFp8Max ? kFp8Max : (v < -kFp8Max ? -kFp8Max : v); }
 // FP8 pools' input conversion of 8 bf16 activations: clamp to [-448, 448], round to
 // e4m3, back to bf16 (page "TensorRT-LLM 源码完全拆解(二十一)", section "前向替换")
 __device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
@@ -74,7 +76,7 @@ __device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
   v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
   v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -kFp8Max), kFp8Max);
+  for (int i = 0; i < 8; ++i) v[i] = fp8_clamp(v[i]);
   int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
   p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p0, true);
   int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
@@ -235,13 +237,18 @@ __device__ __forceinline__ void reduce_scatter64(float (&v)[64]) {
 // so all of the batch is in flight before the first wait.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Inclusive prefix sum over the 64 lanes, with all lanes active, by data-parallel
+// primitives (DPP) that read neighbouring lanes' registers without a trip through
+// the LDS crossbar: shifts right by 1, 2, 4, 8 within each row of 16 lanes (lanes
+// with no source add 0), then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then lanes 0..31's total into rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
   return x;
 }
 

@@ -22,7 +22,7 @@ __device__ __forceinline__ void from_f(float f, float& v) { v = f; }
 __device__ __forceinline__ float to_f(uint8_t v) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false)[0]; }
 __device__ __forceinline__ void from_f(float f, uint8_t& v) {
   const float b = __uint_as_float(f32_to_bf16(f) << 16);
-  const float c = fminf(fmaxf(b, -kFp8Max), kFp8Max);
+  const float c = fp8_clamp(b);
   v = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.f, 0, false) & 0xff);
 }
 
