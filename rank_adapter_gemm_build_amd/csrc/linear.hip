@@ -163,8 +163,11 @@ __host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + 
 // take their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead
 // of the routing outputs being written meanwhile.  T is the type of x, TW of the
 // weights (T, or FP8 with bf16 x).
+// Two waves per SIMD: asked of the compiler (which then keeps the matrix-core
+// accumulators in ordinary vector registers, 223 registers for the routing variant
+// instead of 240 + 24 accumulation registers, which allowed only one wave per SIMD)
 template <typename T, typename TW, bool SELF>
-__global__ __launch_bounds__(64) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
                                                     int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
   int b = blockIdx.x;
   if constexpr (SELF) {
@@ -537,8 +540,16 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
 }
 
 // One wave per workgroup: matrix-core (tile, column group) items, then decode items.
+// Waves per SIMD asked of the compiler: 2 where the body fits 256 registers without
+// spilling (up to two rank steps of 32, except FP8 weights with fp32 outputs); the
+// higher-rank bodies keep their natural allocation (one wave per SIMD).
 template <typename TW, typename TY, int KSM>
-__global__ __launch_bounds__(64) void expand_kernel(PoolView P, RouteView R, UView U,
+struct ExpandWaves {
+  static constexpr int value = (KSM <= 2 && !(sizeof(TW) == 1 && sizeof(TY) == 4)) ? 2 : 1;
+};
+
+template <typename TW, typename TY, int KSM>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_kernel(PoolView P, RouteView R, UView U,
                                                     TY* __restrict__ y, int ldy, Plan plan, int n_mfma_blocks) {
   extern __shared__ float smem[];
   const int b = blockIdx.x;
