@@ -73,6 +73,41 @@ def test_routing_edges(rx):
     _routing_case(rx, sorted(np.random.default_rng(9).integers(0, 32, 4352).tolist()), 32)  # prefill-like
 
 
+def _runs_ids(rng, T, S, max_run=300):
+    """Ids in runs: stretches of one slot (slots repeat across stretches) between
+    stretches of mixed ids, including no-LoRA and invalid ones."""
+    out = []
+    while len(out) < T:
+        n = int(rng.integers(1, max_run + 1))
+        if rng.random() < 0.6:
+            out += [int(rng.integers(-1, S))] * n
+        else:
+            mixed = rng.integers(-1, S, size=n)
+            mixed[rng.random(n) < 0.05] = S + 7
+            out += mixed.tolist()
+    return out[:T]
+
+
+# the workgroup kernel's scatter: 64-token groups of one key ranked by lane with the
+# key's running offset kept in registers over a run, mixed groups by key matching
+# (which may advance the cached key's offset); chunks held in registers and, above
+# 16384 tokens, re-read per batch
+@pytest.mark.parametrize("T,S,seed,max_run", [(6000, 24, 20, 300), (3000, 5, 21, 100), (5000, 1, 22, 200),
+                                              (30000, 40, 23, 700), (1500, 300, 24, 90), (700, 3, 25, 64)])
+def test_routing_runs(rx, T, S, seed, max_run):
+    ids = _runs_ids(np.random.default_rng(seed), T, S, max_run)
+    _log(f"routing runs T={T} S={S} max_run={max_run}")
+    _routing_case(rx, ids, S)
+
+
+def test_routing_single_key_batches(rx):
+    _routing_case(rx, [-1] * 5000, 6)              # every group the no-LoRA key
+    _routing_case(rx, [9] * 3000, 6)               # every id invalid
+    _routing_case(rx, [2] * 2048 + [-1] * 2048, 3)  # two keys, both in whole groups
+    _routing_case(rx, [0] * 64 * 16 * 16, 1)       # 16 waves of 16 whole groups each (the register limit)
+    _routing_case(rx, [0] * (64 * 16 * 16 + 1), 1)  # one token past it
+
+
 @pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
 def test_routing_workloads(rx, num):
     W = workload(num)

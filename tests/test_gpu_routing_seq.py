@@ -47,8 +47,8 @@ def test_routing_seq_golden(rx):
             _check(rx, c["seq_ids"], c["S"], c["tokens_per_seq"])
 
 
-# the one-wave kernel (T <= 128, S < 128), the workgroup kernel with ids staged in
-# LDS, and without staging (large T)
+# the one-wave kernel (T <= 128, S < 128), the workgroup kernel with each wave's ids
+# held in registers, and (large T) re-read per batch
 @pytest.mark.parametrize("Q,p,S,seed", [(1, 1, 1, 0), (16, 5, 8, 1), (32, 4, 127, 2), (40, 7, 16, 3),
                                         (300, 3, 64, 4), (1000, 4, 200, 5), (9000, 4, 64, 6)])
 def test_routing_seq_random(rx, Q, p, S, seed):
