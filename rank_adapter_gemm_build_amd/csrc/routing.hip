@@ -244,6 +244,9 @@ __global__ __launch_bounds__(64) void routing_small_kernel(const int32_t* __rest
   route_wave<kSmallRoutingT / 64, kSmallRoutingK / 64>(ids, T, tps, S, mfma_min, tile_m, max_tiles, o, lds);
 }
 
+// batches from this many tokens get 16 routing waves (when their histograms fit)
+constexpr int kRoutingWideT = 512;
+
 hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_min, int tile_m, int max_tiles,
                           int* counts, int* offs, int* sorted, int* active, int4* desc, int4* tiles,
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm) {
@@ -258,7 +261,7 @@ hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_mi
   // are bound by the one CU's vector throughput), else 8 (fewer waves to start and
   // synchronise)
   const size_t fixed = (size_t)(2 * (S + 1) + 4) * sizeof(int);
-  const int nw = T >= 2048 && fixed + (size_t)16 * (S + 1) * sizeof(int) <= 32768 ? 16 : 8;
+  const int nw = T >= kRoutingWideT && fixed + (size_t)16 * (S + 1) * sizeof(int) <= 32768 ? 16 : 8;
   const size_t lds = fixed + (size_t)nw * (S + 1) * sizeof(int);
   RAX_LAUNCH(tm, routing_kernel, dim3(1), dim3(64 * nw), (uint32_t)lds, stream, ids, T, tps, S,
              mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, rec, meta);
