@@ -33,8 +33,33 @@ notes of the repository):
     bit-untouched, as does a slice registered as missing.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(hand-derived fixtures in ``tests/golden``, closed forms, invariants, brute force
-on tiny inputs, and planted-mistake checks).  No function is "parity unpinned".
+against something other than itself (hand-derived fixtures in ``tests/golden``,
+closed forms, invariants, brute force on tiny inputs, a library implementation of
+a number format), and planted mistakes are checked to fail those pins:
+  lora_scale            scale_cases.json (the printed values), rank/alpha mutants
+  f32_to_bf16_bits      hand values with ties, torch's bfloat16 conversion
+  bf16_bits_to_f64      exact decode of every pattern class
+  round_to_dtype        through the integer and linearity pins (f32 / bf16 paths)
+  fp8_e4m3_decode       torch's float8_e4m3fn on all 256 bytes
+  fp8_e4m3_encode       torch's conversion on every value, every tie, random values
+  fp8_quantize          clamp cases, and fp8_case.json (conversion mutants fail it)
+  fp8_fold_scale        the page's fold expression evaluated by torch
+  effective_b           integer_case.json with and without premultiply, scale mutants
+  route_by_sort,        routing_cases.json, invariants, brute force over every ids
+  route_by_counting     vector of up to 6 tokens for S <= 3, unstable-sort mutant
+  route_tokens_per_seq  routing_seq_cases.json, brute force against a token-level sort
+  shrink_per_token,     integer_case.json (u and y), identity and single-entry
+  expand_per_token,     closed forms, zero branches, packed = separate slices,
+  lora_apply            rank padding, transposed-operand mutants
+  lora_apply_fp8        fp8_case.json: activations past +-448, ties, subnormals,
+                        integer e4m3 weights, an off-grid base (mutants: no
+                        conversion, clamp only, no clamp, truncation, converted
+                        base, dropped scale)
+  lora_apply_grouped    equal to lora_apply within 1e-12, and integer_case.json
+  merged_apply          equal to lora_apply within 1e-10 (linearity)
+  embedding_apply       embedding_case.json, equality with lora_apply on one-hot rows
+  extra_macs_per_token, the page's printed ratios and sizes (page_numbers.json)
+  adapter_params
 """
 from __future__ import annotations
 

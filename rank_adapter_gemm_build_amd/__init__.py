@@ -266,13 +266,29 @@ class Pool:
                  adapter_scale: float = 1.0, premultiply: bool = False, device_src: Optional[bool] = None,
                  stream=None) -> None:
         """A_slices[n] [rank, k], B_slices[n] [d_n, rank] (None for a missing slice), host
-        numpy arrays or device tensors of the pool dtype (bf16 as torch.bfloat16 or uint16)."""
-        arrs = [a for a in list(A_slices) + list(B_slices) if a is not None]
+        numpy arrays or device tensors of the pool dtype (bf16 as torch.bfloat16 or uint16;
+        FP8 as torch.float8_e4m3fn or uint8; an embedding pool's A is [rank, vocab])."""
+        A_slices, B_slices = list(A_slices), list(B_slices)
+        if len(A_slices) != len(self.slices) or len(B_slices) != len(self.slices):
+            raise ValueError(f"the pool has {len(self.slices)} slices: give one A and one B per slice (None if missing)")
+        arrs = [a for a in A_slices + B_slices if a is not None]
         if device_src is None:
             device_src = any(getattr(a, "is_cuda", False) for a in arrs)
+        for n, (a, b) in enumerate(zip(A_slices, B_slices)):
+            if (a is None) != (b is None):
+                raise ValueError(f"slice {n}: give both A and B, or neither")
+            if a is None:
+                continue
+            for t, shape, what in ((a, (rank, self.k), "A"), (b, (self.slices[n], rank), "B")):
+                if tuple(t.shape) != shape:
+                    raise ValueError(f"slice {n}: {what} must have shape {shape} (got {tuple(t.shape)})")
+                if _weight_dtype(t) != self.wdtype:
+                    raise TypeError(f"slice {n}: {what} must be {_DT_NAMES[self.wdtype]} (got {t.dtype})")
         for a in arrs:
             if getattr(a, "is_cuda", False) != device_src:
                 raise ValueError("all slices must live on the same side (host or device)")
+            if device_src and a.device.index != self.device:
+                raise ValueError(f"device slices must be on cuda:{self.device}")
             if hasattr(a, "is_contiguous") and not a.is_contiguous():
                 raise ValueError("slices must be contiguous")
             if not hasattr(a, "is_contiguous") and not a.flags["C_CONTIGUOUS"]:
@@ -318,14 +334,14 @@ class Routing:
 
     def build(self, ids, stream=None) -> None:
         """ids: device int32 tensor [T]."""
-        T = int(ids.numel())
+        T = _check_ids(ids, self.device, "ids")
         lora_build_routing(self.handle, _ptr(ids) if T else 0, T, _stream(stream))
         self.T = T
 
     def build_seq(self, seq_ids, tokens_per_seq: int, stream=None) -> None:
         """seq_ids: device int32 tensor [num_seqs], one slot per sequence of
         tokens_per_seq consecutive tokens (see lora_build_routing_seq)."""
-        n = int(seq_ids.numel())
+        n = _check_ids(seq_ids, self.device, "seq_ids")
         _check(lib.lora_build_routing_seq(self.handle, _ptr(seq_ids) if n else None, n, int(tokens_per_seq),
                                           _stream(stream) or None), "lora_build_routing_seq")
         self.T = n * int(tokens_per_seq)
@@ -364,36 +380,140 @@ def _dt(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _weight_dtype(a) -> int:
+    """Pool dtype code of a weight array: a torch tensor or a numpy array."""
+    if hasattr(a, "data_ptr"):
+        return _dt(a)
+    import numpy as np
+    dt = np.dtype(a.dtype)
+    if dt == np.float32:
+        return LORA_F32
+    if dt in (np.dtype(np.uint16), np.dtype(np.int16)):
+        return LORA_BF16
+    if dt == np.dtype(np.uint8):
+        return LORA_FP8E4M3
+    raise TypeError(f"unsupported weight dtype {dt}")
+
+
 def _act(pool) -> int:
     """dtype of the activations x a pool takes: bf16 for FP8 pools, else the pool's."""
     return LORA_BF16 if pool.wdtype == LORA_FP8E4M3 else pool.wdtype
 
 
+# ----------------------------------------------------------- argument checks
+# The kernels address raw pointers, so a tensor of the wrong dtype, device, shape or
+# stride would be read (or written) out of bounds.  These checks run before any call
+# into the library; the dtype, shape and stride checks come before the device check,
+# so every rule can be exercised without a GPU.
+_DT_NAMES = {LORA_F32: "float32", LORA_BF16: "bfloat16", LORA_FP8E4M3: "float8 e4m3 (uint8)"}
+
+
+def _check_on_device(t, device: int, what: str) -> None:
+    if not getattr(t, "is_cuda", False) or t.device.index != device:
+        raise ValueError(f"{what} must be a tensor on cuda:{device}")
+
+
+def _check_ids(t, device: int, what: str) -> int:
+    """An int32 vector of token (or sequence) ids on the object's GPU; returns its length."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32 (got {t.dtype}): the kernels read 4-byte ids")
+    if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+        raise ValueError(f"{what} must be a contiguous 1-D tensor")
+    if t.numel():
+        _check_on_device(t, device, what)
+    return int(t.numel())
+
+
+def _check_matrix(t, device: int, rows: int, cols: int, dtypes, what: str, exact_cols: bool = True) -> None:
+    """A row-major [>= rows, cols] tensor (unit column stride) of one of the dtypes."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    dt = _dt(t)
+    if dt not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(_DT_NAMES[d] for d in dtypes)} (got {t.dtype})")
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D (got shape {tuple(t.shape)})")
+    if (t.shape[1] != cols) if exact_cols else (t.shape[1] < cols):
+        raise ValueError(f"{what} must have {'' if exact_cols else 'at least '}{cols} columns (got {t.shape[1]})")
+    if t.shape[0] < rows:
+        raise ValueError(f"{what} has {t.shape[0]} rows, the batch has {rows} tokens")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit column stride (got stride {t.stride()})")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{what}: row stride {t.stride(0)} is below its width {t.shape[1]}")
+
+
+def _on_device(device: int, **tensors) -> None:
+    """The device rule, checked after every other rule of a call."""
+    for what, t in tensors.items():
+        _check_on_device(t, device, what)
+
+
+def _routing_tokens(routing) -> int:
+    return max(int(getattr(routing, "T", 0)), 0)
+
+
+def _check_x(pool, rows: int, x) -> None:
+    if pool.embedding:
+        raise ValueError("an embedding pool takes vocabulary ids (embedding), not activations")
+    _check_matrix(x, pool.device, rows, pool.k, (_act(pool),), "x")
+
+
+def _check_y(pool, rows: int, y) -> None:
+    _check_matrix(y, pool.device, rows, pool.D, (_act(pool), LORA_F32), "y", exact_cols=False)
+
+
+def _check_u(pool, rows: int, u) -> None:
+    import torch
+    if not isinstance(u, torch.Tensor):
+        raise TypeError("u must be a torch tensor")
+    if u.dtype != torch.float32:
+        raise TypeError(f"u must be float32 (got {u.dtype})")
+    want = (len(pool.slices), rows, pool.Rmax)
+    if tuple(u.shape) != want:
+        raise ValueError(f"u must have shape {want} (got {tuple(u.shape)})")
+    if not u.is_contiguous():
+        raise ValueError("u must be contiguous")
+
+
 def shrink(pool: Pool, routing: Routing, x, u, stream=None) -> None:
     """u [N, T, Rmax] fp32 = per-token A_slot x (see lora_shrink)."""
-    if _dt(x) != _act(pool):
-        raise TypeError("x dtype must be the pool's activation dtype")
+    T = _routing_tokens(routing)
+    _check_x(pool, T, x)
+    _check_u(pool, T, u)
+    _on_device(pool.device, x=x, u=u)
     lora_shrink(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(u), _stream(stream))
 
 
 def expand(pool: Pool, routing: Routing, u, y, stream=None) -> None:
     """y += s B_slot u in place (see lora_expand)."""
+    T = _routing_tokens(routing)
+    _check_u(pool, T, u)
+    _check_y(pool, T, y)
+    _on_device(pool.device, u=u, y=y)
     lora_expand(pool.handle, routing.handle, _ptr(u), _ptr(y), y.stride(0), _dt(y), _stream(stream))
 
 
 def linear(pool: Pool, routing: Routing, x, y, stream=None) -> None:
     """y += s B_slot (A_slot x) in place onto the caller's base output (see lora_linear)."""
-    if _dt(x) != _act(pool):
-        raise TypeError("x dtype must be the pool's activation dtype")
+    T = _routing_tokens(routing)
+    _check_x(pool, T, x)
+    _check_y(pool, T, y)
+    _on_device(pool.device, x=x, y=y)
     lora_linear(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y), _stream(stream))
 
 
 def route_linear(pool: Pool, routing: Routing, ids, x, y, stream=None) -> None:
     """routing.build(ids) then linear(pool, routing, x, y), in one fewer launch for small
     batches (see lora_route_linear)."""
-    if _dt(x) != _act(pool):
-        raise TypeError("x dtype must be the pool's activation dtype")
-    T = int(ids.numel())
+    T = _check_ids(ids, routing.device, "ids")
+    _check_x(pool, T, x)
+    _check_y(pool, T, y)
+    _on_device(pool.device, x=x, y=y)
     lora_route_linear(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
                       y.stride(0), _dt(y), _stream(stream))
     routing.T = T
@@ -403,14 +523,15 @@ def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=No
     """linear (or route_linear when ids is given) whose expand waits for the torch
     event y_ready, recorded after the base output was written into y on another
     stream (see lora_linear_join / lora_route_linear_join)."""
-    if _dt(x) != _act(pool):
-        raise TypeError("x dtype must be the pool's activation dtype")
+    T = _routing_tokens(routing) if ids is None else _check_ids(ids, routing.device, "ids")
+    _check_x(pool, T, x)
+    _check_y(pool, T, y)
+    _on_device(pool.device, x=x, y=y)
     ev = y_ready.cuda_event if y_ready is not None else 0
     if ids is None:
         lora_linear_join(pool.handle, routing.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0), _dt(y),
                          _stream(stream), ev)
     else:
-        T = int(ids.numel())
         lora_route_linear_join(pool.handle, routing.handle, _ptr(ids) if T else 0, T, _ptr(x), x.stride(0), _ptr(y),
                                y.stride(0), _dt(y), _stream(stream), ev)
         routing.T = T
@@ -418,13 +539,26 @@ def linear_join(pool: Pool, routing: Routing, x, y, y_ready, stream=None, ids=No
 
 def embedding(pool: Pool, routing: Routing, vocab_ids, y, stream=None) -> None:
     """y += s B_slot A_slot[:, vocab_id] per LoRA token (see lora_embedding)."""
+    if not pool.embedding:
+        raise ValueError("embedding() needs a pool made with embedding=True")
+    T = _routing_tokens(routing)
+    if _check_ids(vocab_ids, pool.device, "vocab_ids") < T:
+        raise ValueError(f"vocab_ids has fewer than the batch's {T} tokens")
+    _check_y(pool, T, y)
+    _on_device(pool.device, y=y)
     lora_embedding(pool.handle, routing.handle, _ptr(vocab_ids), _ptr(y), y.stride(0), _dt(y), _stream(stream))
 
 
 def route_embedding(pool: Pool, routing: Routing, slot_ids, vocab_ids, y, stream=None) -> None:
     """routing.build(slot_ids) then embedding(pool, routing, vocab_ids, y), in one fewer
     launch for small batches (see lora_route_embedding)."""
-    T = int(slot_ids.numel())
+    if not pool.embedding:
+        raise ValueError("route_embedding() needs a pool made with embedding=True")
+    T = _check_ids(slot_ids, routing.device, "slot_ids")
+    if _check_ids(vocab_ids, pool.device, "vocab_ids") != T:
+        raise ValueError("slot_ids and vocab_ids must have one entry per token")
+    _check_y(pool, T, y)
+    _on_device(pool.device, y=y)
     _check(lib.lora_route_embedding(pool.handle, routing.handle, _ptr(slot_ids) if T else None, T,
                                     _ptr(vocab_ids) if T else None, _ptr(y), y.stride(0), _dt(y),
                                     _stream(stream) or None), "lora_route_embedding")

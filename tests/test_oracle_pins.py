@@ -186,10 +186,10 @@ def check_rank_padding():
 
 PINS = [check_scale_golden, check_routing_golden, check_integer_golden, check_linearity,
         check_identity_closed_form, check_single_entry, check_zero_branches,
-        check_packed_equals_separate, check_rank_padding]
+        check_packed_equals_separate, check_rank_padding, lambda: check_fp8_golden()]
 
 
-@pytest.mark.parametrize("check", PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("check", PINS, ids=lambda f: getattr(f, "__name__", "pin"))
 def test_pin(check):
     msg = check()
     assert msg is None, msg
@@ -249,7 +249,7 @@ def _independent_invariants(ids, S, R):
 @pytest.mark.parametrize("S", [1, 2, 3])
 def test_routing_brute_force(S):
     vals = list(range(-2, S + 1))
-    for T in range(0, 5):
+    for T in range(0, 7):
         for ids in itertools.product(vals, repeat=T):
             a = O.route_by_sort(list(ids), S)
             b = O.route_by_counting(list(ids), S)
@@ -511,3 +511,89 @@ def test_fp8_fold_scale_matches_the_pages_expression():
         ref = (t.to(torch.bfloat16) * float(s)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64).numpy()
         got = O.fp8_fold_scale(vals, s)
         assert np.array_equal(got, ref), float(s)
+
+
+# ------------------------------------------------------- FP8 path, composition
+def _fp8_golden_apply():
+    g = _load("fp8_case.json")
+    a = g["adapter"]
+    ad = O.Adapter(rank=a["rank"], A=[np.array(a["A"], dtype=np.float64)], B=[np.array(a["B"], dtype=np.float64)],
+                   alpha=a["alpha"], rslora=a["rslora"], adapter_scale=a["adapter_scale"])
+    y = O.lora_apply_fp8(np.array(g["x"], dtype=np.float64), np.array(g["y_base"], dtype=np.float64), {0: ad},
+                         g["slices"], g["ids"], g["S"], max_rank=g["max_rank"])
+    return g, y
+
+
+def check_fp8_golden():
+    g, y = _fp8_golden_apply()
+    if not np.array_equal(y, np.array(g["y"], dtype=np.float64)):
+        return f"lora_apply_fp8: got {y.tolist()}"
+    return None
+
+
+def test_fp8_golden_inputs_are_on_their_grids():
+    """The fixture's weights are e4m3 values, its activations and base outputs bf16
+    values, and its converted rows are what the input conversion gives."""
+    g = _load("fp8_case.json")
+    for w in (g["adapter"]["A"], g["adapter"]["B"]):
+        v = np.array(w, dtype=np.float64)
+        assert np.array_equal(O.fp8_e4m3_decode(O.fp8_e4m3_encode(v)), v)
+    for a in (g["x"], g["y_base"]):
+        v = np.array(a, dtype=np.float64)
+        assert np.array_equal(O.bf16_bits_to_f64(O.f32_to_bf16_bits(v.astype(np.float32))), v)
+    conv = O.fp8_quantize(np.array(g["x"], dtype=np.float64))
+    assert np.array_equal(conv[:2], np.array(g["x_converted"]["rows"], dtype=np.float64))
+
+
+def test_fp8_golden():
+    """The FP8 path's composition on a hand-worked case (tests/golden/fp8_case.json):
+    activations past +-448, between grid points, at ties and in the subnormal range,
+    integer e4m3 weights, an off-grid bf16 base output and a no-LoRA token."""
+    assert check_fp8_golden() is None
+
+
+def _fp8_no_conversion(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _fp8_clamp_only(x):
+    return np.clip(np.asarray(x, dtype=np.float64), -O.FP8_MAX, O.FP8_MAX)
+
+
+def _fp8_round_without_clamp(x):
+    # a conversion without the clamp: magnitudes past the largest finite value are
+    # not e4m3 numbers (NaN in the "fn" format)
+    x = np.asarray(x, dtype=np.float64)
+    r = O.fp8_e4m3_decode(O.fp8_e4m3_encode(np.clip(x, -O.FP8_MAX, O.FP8_MAX)))
+    return np.where(np.abs(x) > O.FP8_MAX, np.nan, r)
+
+
+def _fp8_round_toward_zero(x):
+    # truncation instead of round-to-nearest-even
+    x = np.clip(np.asarray(x, dtype=np.float64), -O.FP8_MAX, O.FP8_MAX)
+    grid = np.unique(O.fp8_e4m3_decode(np.arange(0, 0x7F)))
+    mag = np.array([grid[grid <= abs(v)].max() for v in x.ravel()]).reshape(x.shape)
+    return np.sign(x) * mag
+
+
+@pytest.mark.parametrize("mutant", [_fp8_no_conversion, _fp8_clamp_only, _fp8_round_without_clamp,
+                                    _fp8_round_toward_zero], ids=lambda f: f.__name__)
+def test_fp8_planted_conversion_mistakes_fail_the_golden(monkeypatch, mutant):
+    monkeypatch.setattr(O, "fp8_quantize", mutant)
+    assert check_fp8_golden() is not None
+
+
+def test_fp8_planted_base_conversion_fails_the_golden(monkeypatch):
+    """Converting the base output to FP8 as well (the page converts only the input)."""
+    real = O.lora_apply
+
+    def converting_base(x, y_base, *a, **k):
+        return real(x, O.fp8_quantize(y_base), *a, **k)
+
+    monkeypatch.setattr(O, "lora_apply", converting_base)
+    assert check_fp8_golden() is not None
+
+
+def test_fp8_planted_dropped_scale_fails_the_golden(monkeypatch):
+    monkeypatch.setattr(O.Adapter, "scale", lambda self: np.float32(1.0))
+    assert check_fp8_golden() is not None
