@@ -152,14 +152,19 @@ def load_traffic(kernel: str, workload_name: str):
 
 # ----------------------------------------------------------------- cpu baseline
 def cpu_baseline(W, seconds: float):
-    """The oracle as it stands (per-token float64 definition), timed on this host."""
+    """The oracle as it stands, timed on this host: its grouped float64 formulation
+    (per slot: gather the slot's rows, two matmuls, scatter) over the whole batch,
+    with the BLAS threads set to the cores this process may run on; and, beside it,
+    its per-token definition on a bounded share of the same time."""
     import numpy as np
     import oracle.lora_oracle as O
+    import contextlib
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
     except Exception:
-        threads = 1
+        limit = contextlib.nullcontext()
     mods = []
     for m in W.modules:
         conv = (lambda a: None if a is None else O.bf16_bits_to_f64(a)) if W.dtype == "bf16" else \
@@ -168,17 +173,29 @@ def cpu_baseline(W, seconds: float):
                             rslora=W.rslora, adapter_scale=W.adapter_scale) for s, r in W.ranks.items()}
         yb = conv(m.y_base) if m.y_base is not None else np.zeros((W.T, sum(m.slices)))
         mods.append((conv(m.x), yb, ads, m.slices))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for x, yb, ads, slices in mods:
-            O.lora_apply(x, yb, ads, slices, W.ids, W.S, W.dtype, max_rank=W.Rmax)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": reps * W.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+
+    def timed(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for x, yb, ads, slices in mods:
+                fn(x, yb, ads, slices)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    with limit:
+        reps, el = timed(lambda x, yb, ads, sl: O.lora_apply_grouped(x, yb, ads, sl, W.ids, W.S, W.dtype),
+                         0.75 * seconds)
+        preps, pel = timed(lambda x, yb, ads, sl: O.lora_apply(x, yb, ads, sl, W.ids, W.S, W.dtype,
+                                                               max_rank=W.Rmax), 0.25 * seconds)
+    return {"value": reps * W.T / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"the whole {W.name} batch ({W.T} tokens, {len(W.modules)} module(s)) through "
-                      f"oracle.lora_apply (float64 per-token definition), repeated {reps} times in {el:.1f} s"}
+                      f"oracle.lora_apply_grouped (float64, per slot: gather, two matmuls, scatter; BLAS threads = "
+                      f"{cores} cores of the affinity mask), repeated {reps} times in {el:.1f} s",
+            "per_token_definition": {"value": preps * W.T / pel, "unit": "tokens/s",
+                                     "sample": f"oracle.lora_apply (float64 per-token loop), the same batch "
+                                               f"{preps} times in {pel:.1f} s"}}
 
 
 # ------------------------------------------------------- graph replay, overlap
@@ -340,6 +357,61 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
         res["gemm_then_lora_us_per_step"] = round(timed(serial), 3)
         res["gemm_beside_lora_us_per_step"] = round(timed(overlap), 3)
         res["gemm_beside_lora_independent_steps_us_per_step"] = round(timed(overlap_free), 3)
+
+        # the two forms captured in HIP graphs of G2 chained steps each: serial (GEMM then
+        # LoRA on one stream) and forked (each GEMM on a side stream that first waits for
+        # the previous step, the LoRA branch on the capturing stream joined to the GEMM's
+        # event); the graph holds the cross-stream edges instead of runtime event waits
+        G2 = min(16, M)
+        fa = torch.cuda.Stream()
+
+        def capture(forked):
+            gr = torch.cuda.CUDAGraph()
+            warm = torch.cuda.Stream()
+            warm.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(warm):
+                for i in range(G2):
+                    gemm(insts[i])
+                    step_on(insts[i], warm.cuda_stream)
+            torch.cuda.current_stream().wait_stream(warm)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr):
+                cs = torch.cuda.current_stream()
+                for i in range(G2):
+                    inst = insts[i]
+                    if forked:
+                        fa.wait_stream(cs)
+                        with torch.cuda.stream(fa):
+                            gemm(inst)
+                            evs[i].record(fa)
+                        pool, xp, ldx, yp, ldy = inst.calls[0]
+                        st = lib.lora_route_linear_join(pool, inst.routing.handle, inst.ids.data_ptr(), T, xp, ldx,
+                                                        yp, ldy, ydt, cs.cuda_stream, evs[i].cuda_event)
+                        if st:
+                            raise rx.LoraError(st, "lora_route_linear_join")
+                    else:
+                        gemm(inst)
+                        step_on(inst, cs.cuda_stream)
+                if forked:
+                    cs.wait_stream(fa)
+            torch.cuda.synchronize()
+            return gr
+
+        for key, forked in (("graph_gemm_then_lora_us_per_step", False), ("graph_gemm_beside_lora_us_per_step", True)):
+            gr = capture(forked)
+            gr.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(2, n // G2)
+            a.record()
+            for _ in range(reps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res[key] = round(a.elapsed_time(b) * 1e3 / (reps * G2), 3)
+            del gr
+        log(f"graphs of {G2} steps: GEMM then LoRA {res['graph_gemm_then_lora_us_per_step']:.2f} us/step, "
+            f"GEMM beside LoRA {res['graph_gemm_beside_lora_us_per_step']:.2f} us/step")
         res["base_gemm"] = f"torch.mm [{T},{W0T.shape[0]}] x [{W0T.shape[0]},{W0T.shape[1]}] bf16, one W0 for all instances"
         log(f"base GEMM {res['base_gemm_us']:.2f} us; GEMM then LoRA {res['gemm_then_lora_us_per_step']:.2f} us/step; "
             f"GEMM beside LoRA (joined) {res['gemm_beside_lora_us_per_step']:.2f} us/step; independent steps "
@@ -498,37 +570,15 @@ def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
     return res
 
 
-# ------------------------------------------------------------------------ main
-def run(args):
-    import numpy as np
-    import torch
-
-    import rank_adapter_gemm_build_amd as rx
-    from synthetic import workload
-
-    torch.cuda.set_device(0)
-    W = workload(args.workload)
-    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0"
-    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "4"))   # the library default
-    acc, flops, by_path = step_accounting(W, mfma_min, use_mfma)
-    step_bytes = sum(acc.values())
-    log(f"workload {W.name}: T={W.T} S={W.S} modules={[m.name for m in W.modules]} "
-        f"algorithmic bytes/step={step_bytes / 1e6:.2f} MB")
-    M = max(2, min(args.max_instances, math.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes, 1))))
-    src = upload_sources(torch, W)
-    insts = []
-    for i in range(M):
-        insts.append(Instance(rx, torch, W, src, None))
-    torch.cuda.synchronize()
-    log(f"{M} rotation instances registered")
-    stream = torch.cuda.current_stream().cuda_stream
-    ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
-    lib, T = rx.lib, W.T
+# ------------------------------------------------------------------ timing core
+def make_step(rx, lib, insts, T, ydt, stream, separate_routing: bool):
+    """One step on instance i % M: the routing and every module's fused call."""
+    M = len(insts)
 
     def step(i):
         inst = insts[i % M]
         calls = inst.calls
-        if args.separate_routing:
+        if separate_routing:
             st = lib.lora_build_routing(inst.routing.handle, inst.ids.data_ptr(), T, stream)
             if st:
                 raise rx.LoraError(st, "lora_build_routing")
@@ -543,33 +593,173 @@ def run(args):
             st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, stream)
             if st:
                 raise rx.LoraError(st, "lora_linear")
+    return step
+
+
+def time_steps(torch, step, steps: int):
+    """Events around `steps` back-to-back steps: (ms per step, host wall us per step)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall * 1e6 / steps
+
+
+def kernel_times(rx, torch, step, steps: int):
+    """Per-kernel average durations: the same steps again, each launch stamped by a
+    pair of events at the kernel's own start and end (on the launch's stream)."""
+    rx.lora_timing_enable(True)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    rep = rx.lora_timing_report()
+    rx.lora_timing_enable(False)
+    return {k: {"avg_us": 1e3 * ms / n, "launches_per_step": n / steps} for k, (ms, n) in rep.items() if n}
+
+
+def family_roofline(acc, kern):
+    """Per kernel family: algorithmic bytes per launch over its average launch time."""
+    out = {}
+    for k, v in kern.items():
+        if k not in acc or v["launches_per_step"] <= 0:
+            continue
+        per_launch = acc[k] / v["launches_per_step"]
+        gbps = per_launch / (v["avg_us"] * 1e-6) / 1e9
+        out[k] = {"bytes_per_launch": int(per_launch), "avg_launch_us": round(v["avg_us"], 3),
+                  "launches_per_step": round(v["launches_per_step"], 3), "achieved_gbps": round(gbps, 1),
+                  "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    return out
+
+
+def build_instances(rx, torch, W, args, step_bytes):
+    M = max(2, min(args.max_instances, math.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes, 1))))
+    src = upload_sources(torch, W)
+    insts = [Instance(rx, torch, W, src, None) for _ in range(M)]
+    torch.cuda.synchronize()
+    return src, insts
+
+
+def measure_workload(torch, rx, num: int, args):
+    """A further workload timed like the headline one (rotating instances, events
+    around the steps, per-kernel event stamps): µs per step, tokens/s, the step's
+    algorithmic bytes and rate, and each kernel family's rate per launch."""
+    from synthetic import workload
+    t0 = time.perf_counter()
+    W = workload(num)
+    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0"
+    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "4"))
+    acc, flops, by_path = step_accounting(W, mfma_min, use_mfma)
+    step_bytes = sum(acc.values())
+    src, insts = build_instances(rx, torch, W, args, step_bytes)
+    ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
+    step = make_step(rx, rx.lib, insts, W.T, ydt, torch.cuda.current_stream().cuda_stream, False)
+    steps = max(args.steps, 20)
+    for i in range(max(args.warmup, len(insts))):
+        step(i)
+    ms, wall = time_steps(torch, step, steps)
+    kern = kernel_times(rx, torch, step, steps)
+    for inst in insts:
+        inst.close()
+    del insts, src
+    torch.cuda.synchronize()
+    us = ms * 1e3
+    res = {"us_per_step": round(us, 3), "tokens_per_s": round(W.T / (us * 1e-6), 1), "tokens": W.T,
+           "modules": [m.name for m in W.modules], "launches_per_step": round(sum(v["launches_per_step"]
+                                                                                   for v in kern.values()), 2),
+           "step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+           "step_frac_of_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "kernels": family_roofline(acc, kern),
+           "routing_avg_us": round(kern["routing"]["avg_us"], 3) if "routing" in kern else None,
+           "steps_timed": steps, "setup_s": round(time.perf_counter() - t0, 1)}
+    log(f"workload {W.name}: {us:.1f} us/step, {res['step_hbm_gbps']} GB/s over the step "
+        f"({100 * res['step_frac_of_peak']:.1f} % of 8 TB/s), kernels "
+        + ", ".join(f"{k} {v['avg_launch_us']} us x{v['launches_per_step']} ({100 * v['frac_of_peak']:.1f} %)"
+                    for k, v in res["kernels"].items()))
+    return W.name, res
+
+
+def device_ceilings(torch, rx):
+    """The device's own floors and ceilings, measured in the same run: the shortest
+    kernel (a one-element fill, back to back), a 512 MiB device copy (ROCclr), and
+    the library's streaming probe (a 1 GiB read; a 1 GiB read with 256 MiB written)."""
+    tiny = torch.zeros(1, device="cuda")
+    src_c = torch.empty(1024 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    dst_c = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    half = src_c[: 512 * 2 ** 20]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(ratio):
+        st = rx.lib.lora_bandwidth_probe(src_c.data_ptr(), src_c.numel(), dst_c.data_ptr(), dst_c.numel(), ratio,
+                                         stream)
+        if st:
+            raise rx.LoraError(st, "lora_bandwidth_probe")
+
+    for _ in range(5):
+        tiny.fill_(1.0)
+        dst_c.copy_(half)
+        probe(0)
+        probe(4)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, n):
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n   # ms per call
+
+    floor_us = rate(lambda: tiny.fill_(1.0), 100) * 1e3
+    copy_gbps = 2 * half.numel() / (rate(lambda: dst_c.copy_(half), 10) * 1e-3) / 1e9
+    read_gbps = src_c.numel() / (rate(lambda: probe(0), 10) * 1e-3) / 1e9
+    rw_gbps = (src_c.numel() * 5 // 4) / (rate(lambda: probe(4), 10) * 1e-3) / 1e9
+    del src_c, dst_c, half
+    torch.cuda.synchronize()
+    log(f"shortest-kernel floor {floor_us:.2f} us; copy {copy_gbps:.0f} GB/s; streaming read {read_gbps:.0f} GB/s; "
+        f"read 4 : write 1 {rw_gbps:.0f} GB/s")
+    return {"shortest_kernel_floor_us": round(floor_us, 3), "copy_gbps": round(copy_gbps, 1),
+            "read_gbps": round(read_gbps, 1), "read4_write1_gbps": round(rw_gbps, 1)}
+
+
+# ------------------------------------------------------------------------ main
+def run(args):
+    import torch
+
+    import rank_adapter_gemm_build_amd as rx
+    from synthetic import workload
+
+    torch.cuda.set_device(0)
+    W = workload(args.workload)
+    use_mfma = W.dtype == "bf16" and os.environ.get("RAXLORA_DISABLE_MFMA", "0") == "0"
+    mfma_min = int(os.environ.get("RAXLORA_MFMA_MIN_SEG", "4"))   # the library default
+    acc, flops, by_path = step_accounting(W, mfma_min, use_mfma)
+    step_bytes = sum(acc.values())
+    log(f"workload {W.name}: T={W.T} S={W.S} modules={[m.name for m in W.modules]} "
+        f"algorithmic bytes/step={step_bytes / 1e6:.2f} MB")
+    src, insts = build_instances(rx, torch, W, args, step_bytes)
+    M = len(insts)
+    log(f"{M} rotation instances registered")
+    stream = torch.cuda.current_stream().cuda_stream
+    ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
+    lib, T = rx.lib, W.T
+    step = make_step(rx, lib, insts, T, ydt, stream, args.separate_routing)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us/step)")
+    ms_per_step, wall_us = time_steps(torch, step, args.steps)
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall_us:.2f} us/step)")
 
-    # per-kernel durations: same steps again, each launch stamped by its own events
-    rx.lora_timing_enable(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    rep = rx.lora_timing_report()
-    rx.lora_timing_enable(False)
-    kern = {k: {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps} for k, (ms, n) in rep.items() if n}
+    kern = kernel_times(rx, torch, step, args.steps)
     log("kernels: " + ", ".join(f"{k} {v['avg_us']:.2f} us" for k, v in kern.items()))
+    families = family_roofline(acc, kern)
 
     # dominant kernel: most time per step among the shrink/expand kernels
     cand = {k: v for k, v in kern.items() if k in acc}
@@ -581,8 +771,7 @@ def run(args):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
                 "bytes_per_launch": int(per_launch), "avg_launch_us": round(cand[dom]["avg_us"], 3)}
 
-    # per-step distribution (events around each step) and the device's own floors:
-    # the shortest kernel (a one-element fill) and a plain copy of 512 MiB
+    # per-step distribution (events around each step)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record()
@@ -591,31 +780,13 @@ def run(args):
     torch.cuda.synchronize()
     per_step = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
     pct = {f"p{q}": round(per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))], 3) for q in (10, 50, 90)}
-    tiny = torch.zeros(1, device="cuda")
-    src_c = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
-    dst_c = torch.empty_like(src_c)
-    for _ in range(5):
-        tiny.fill_(1.0)
-        dst_c.copy_(src_c)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(100):
-        tiny.fill_(1.0)
-    b.record()
-    torch.cuda.synchronize()
-    floor_us = a.elapsed_time(b) * 10.0
-    a.record()
-    for _ in range(10):
-        dst_c.copy_(src_c)
-    b.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src_c.numel() * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src_c, dst_c
-    log(f"per-step p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']} us; shortest-kernel floor {floor_us:.2f} us; "
-        f"copy ceiling {copy_gbps:.0f} GB/s")
-    roofline["copy_ceiling_gbps"] = round(copy_gbps, 1)
-    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+    log(f"per-step p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']} us")
+
+    ceil = device_ceilings(torch, rx)
+    roofline["copy_ceiling_gbps"] = ceil["copy_gbps"]
+    roofline["read_ceiling_gbps"] = ceil["read_gbps"]
+    roofline["frac_of_copy"] = round(achieved / ceil["copy_gbps"], 4)
+    roofline["frac_of_read_ceiling"] = round(achieved / ceil["read_gbps"], 4)
 
     graph_overlap = None if args.no_extras else measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
     for inst in insts:
@@ -623,6 +794,8 @@ def run(args):
     insts = []
     embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
     fp8 = None if args.no_extras else measure_fp8(torch, rx, lib, W, src, args, step_bytes, acc)
+    del src
+    torch.cuda.synchronize()
 
     # matrix-core path: its algorithmic FLOPs over the shrink + expand kernel time of a
     # step (a lower bound of the MFMA utilisation: those launches also run the vector
@@ -634,6 +807,13 @@ def run(args):
         tf = mfma_flops / (kt * 1e-6) / 1e12
         mfma_path = {"algorithmic_flop_per_step": int(mfma_flops), "tflops_over_shrink_expand_time": round(tf, 2),
                      "peak_tflops_bf16_dense": 2500.0, "frac": round(tf / 2500.0, 5)}
+
+    others = {}
+    for num in ([] if args.no_workloads else [int(v) for v in args.workloads.split(",") if v.strip()]):
+        if num == args.workload:
+            continue
+        name, res = measure_workload(torch, rx, num, args)
+        others[name] = res
 
     tokens_per_s = T / (ms_per_step * 1e-3)
     out = {
@@ -647,14 +827,12 @@ def run(args):
                             "lora_route_linear + lora_linear"},
         "roofline": roofline,
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
-                  "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "rotation_instances": M,
-                  "wall_us_per_step": round(wall * 1e6 / args.steps, 3), "step_us_percentiles": pct,
-                  "shortest_kernel_floor_us": round(floor_us, 3), "source_digest": source_digest(),
+                  "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "kernel_families": families,
+                  "rotation_instances": M, "wall_us_per_step": round(wall_us, 3), "step_us_percentiles": pct,
+                  "device": ceil, "source_digest": source_digest(),
                   "graph_and_overlap": graph_overlap, "embedding_lora": embedding, "fp8_pools": fp8,
-                  "mfma_path": mfma_path},
+                  "mfma_path": mfma_path, "workloads": others},
     }
-    for inst in insts:
-        inst.close()
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
@@ -673,7 +851,11 @@ def main():
     ap.add_argument("--max-instances", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the graph-replay and base-GEMM overlap timings")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the graph-replay, base-GEMM overlap, embedding and FP8 timings")
+    ap.add_argument("--workloads", default="3,4,5",
+                    help="further workloads timed after the headline one, reported under extra.workloads")
+    ap.add_argument("--no-workloads", action="store_true", help="time the headline workload only")
     ap.add_argument("--separate-routing", action="store_true",
                     help="lora_build_routing + lora_linear per step instead of lora_route_linear for the first module")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")

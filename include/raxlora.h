@@ -346,6 +346,18 @@ lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, c
                                  const int32_t* vocab_ids, void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
+ * Bandwidth probe (diagnostics): the rate this GPU's memory gives a plain streaming
+ * kernel, the ceiling against which the LoRA kernels' traffic is read.  ratio <= 0:
+ * read read_bytes from src (device, 16-byte aligned), 16 bytes per lane, and write
+ * one 4-byte word per thread into dst (needs dst_bytes >= 4 MiB).  ratio > 0: read
+ * read_bytes and write read_bytes / ratio bytes to dst (each 16-byte chunk of dst is
+ * the xor of `ratio` chunks of src).  One launch, enqueued on `stream`.
+ * Errors: NULL -> INVALID_ARG; alignment -> ALIGN; sizes -> SHAPE.
+ */
+lora_status lora_bandwidth_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t dst_bytes, int ratio,
+                                 hipStream_t stream);
+
+/*
  * Kernel timing (diagnostics).  While enabled (process-wide), every kernel that
  * the routing, shrink, expand, linear and embedding calls launch is started
  * with hipExtLaunchKernel and a pair of events stamped at that kernel's own start

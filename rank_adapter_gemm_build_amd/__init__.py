@@ -53,6 +53,7 @@ SIGNATURES = {
     "lora_route_embedding": (_I, [_P, _P, _VP, _I, _VP, _VP, _I, _I, _VP]),
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
+    "lora_bandwidth_probe": (_I, [_VP, C.c_uint64, _VP, C.c_uint64, _I, _VP]),
     "lora_timing_enable": (_I, [_I]),
     "lora_timing_report": (_I, [C.POINTER(C.c_double), C.POINTER(C.c_int), _I]),
     "lora_timing_kernel_name": (C.c_char_p, [_I]),

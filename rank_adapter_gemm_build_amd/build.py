@@ -55,12 +55,25 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra=()) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
+def _stale(src: str, headers) -> bool:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(f) > t for f in [src, *headers])
+
+
+def build(verbose: bool = True, extra=(), incremental: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared library; returns its path.
+    incremental: recompile only sources older than themselves or any header."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    todo = [s for s in srcs if not incremental or extra or _stale(s, headers)]
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
+        list(ex.map(lambda s: _compile(s, list(extra)), todo))
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,4 +86,4 @@ def build(verbose: bool = True, extra=()) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])

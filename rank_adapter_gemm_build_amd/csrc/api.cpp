@@ -884,6 +884,20 @@ lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, c
   return ok();
 }
 
+lora_status lora_bandwidth_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t dst_bytes, int ratio,
+                                 hipStream_t stream) {
+  if (!src || !dst) return fail(LORA_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(LORA_ERR_ALIGN, "src and dst must be 16-byte aligned");
+  if (read_bytes < 16) return fail(LORA_ERR_SHAPE, "read_bytes %llu < 16", (unsigned long long)read_bytes);
+  if (ratio <= 0 && dst_bytes < (uint64_t)256 * 16 * 256 * sizeof(uint32_t))
+    return fail(LORA_ERR_SHAPE, "the read form needs dst_bytes >= 4 MiB");
+  if (ratio > 0 && (read_bytes / 16 / (uint64_t)ratio == 0 || read_bytes / 16 / (uint64_t)ratio * 16 > dst_bytes))
+    return fail(LORA_ERR_SHAPE, "dst_bytes below read_bytes / ratio");
+  hipError_t e = rax::launch_bandwidth_probe(src, read_bytes, dst, dst_bytes, ratio, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
 lora_status lora_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   g_timing_on = on != 0;

@@ -165,6 +165,10 @@ hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R
 hipError_t launch_embed_gather_tok(int wdtype, const PoolView& P, const RouteView& R, const int32_t* slot_ids,
                                    const int32_t* vocab_ids, int V, const UView& W, const SelfRoute* sr,
                                    hipStream_t stream, const KTimer& tm);
+// diagnostics: a streaming read of read_bytes (ratio <= 0; one word per thread into dst),
+// or a read with one 16-byte chunk written per `ratio` chunks read
+hipError_t launch_bandwidth_probe(const void* src, size_t read_bytes, void* dst, size_t dst_bytes, int ratio,
+                                  hipStream_t stream);
 // finished u of a standalone shrink: workspace partials -> caller's [N][T][Rmax]
 hipError_t launch_finish_u(const PoolView& P, const RouteView& R, const UView& W, const UView& U,
                            const Plan& plan, hipStream_t stream, const KTimer& tm);

@@ -2,6 +2,8 @@
 binding, and turn them into oracle inputs (test infrastructure)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import oracle.lora_oracle as O
@@ -89,11 +91,23 @@ def normwise_rel(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max() / den) if den > 0 else float(np.abs(got).max())
 
 
+# Measured errors of this session, printed as a table at the end of the run
+# (tests/conftest.py): (test, what, measure, value, bar).
+MEASURED = []
+
+
+def record_error(what: str, measure: str, value: float, bar: float) -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    MEASURED.append((test, what, measure, float(value), float(bar)))
+
+
 def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> float:
     if dtype == "f32":
         err = float(np.abs(got - ref).max()) if got.size else 0.0
+        record_error(what, "max-abs", err, F32_TOL)
         assert err <= F32_TOL, f"{what}: max-abs error {err:.3e} > {F32_TOL}"
     else:
         err = normwise_rel(got, ref) if got.size else 0.0
+        record_error(what, "normwise-rel", err, BF16_TOL)
         assert err <= BF16_TOL, f"{what}: normwise relative error {err:.3e} > {BF16_TOL}"
     return err

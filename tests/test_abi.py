@@ -140,6 +140,7 @@ def test_null_arguments_rejected_without_device():
     assert rx.lib.lora_embedding(None, None, None, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_route_embedding(None, None, None, 0, None, None, 8, rx.LORA_BF16, None) == \
         rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_bandwidth_probe(None, 1 << 20, None, 1 << 22, 0, None) == rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_pool_destroy(None) == rx.LORA_OK
     assert rx.lib.lora_routing_destroy(None) == rx.LORA_OK
 

@@ -414,7 +414,11 @@ def _sample_rows(W, rng, n=48):
 @pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
 def test_workload_parity(rx, num):
     """Each workload at its full size, in the launch configuration the benchmark
-    times; all rows checked where the oracle is quick, sampled rows otherwise."""
+    times (bf16 or fp32 output as the workload's).  The branch alone (base 0, fp32
+    output) is checked on every row of every module against the oracle's grouped
+    formulation (equal to the per-token definition within 1e-12); y on its base
+    against the per-token definition, on all rows where that is quick (workloads 1
+    and 2) and on sampled rows otherwise."""
     import torch
     W = workload(num)
     rng = np.random.default_rng(100 + num)
@@ -422,20 +426,28 @@ def test_workload_parity(rx, num):
     for mod in W.modules:
         _log(f"workload {num} module {mod.name} k={mod.k} slices={mod.slices} T={W.T}")
         pool = make_pool(rx, W, mod)
+        ads = oracle_adapters(W, mod)
+        x = to_device(mod.x, W.dtype)
+        x64 = to_f64(mod.x, W.dtype)
+        # the branch alone on every row
+        d0 = torch.zeros((W.T, sum(mod.slices)), dtype=torch.float32, device="cuda")
+        rx.linear(pool, R, x, d0)
         yb = y_base_of(W, mod)
         y = to_device(yb, W.dtype)
-        rx.linear(pool, R, to_device(mod.x, W.dtype), y)
+        rx.linear(pool, R, x, y)
         torch.cuda.synchronize()
+        ref0 = O.lora_apply_grouped(x64, np.zeros(tuple(d0.shape)), ads, mod.slices, W.ids, W.S, W.dtype)
+        check_close(d0.double().cpu().numpy(), ref0, W.dtype, f"workload {num} {mod.name} delta, all {W.T} rows")
         rows = np.arange(W.T) if num <= 2 else _sample_rows(W, rng)
-        ads = oracle_adapters(W, mod)
-        x64 = to_f64(mod.x, W.dtype)[rows]
-        ref = O.lora_apply(x64, to_f64(yb, W.dtype)[rows], ads, mod.slices, W.ids[rows], W.S, W.dtype,
+        ref = O.lora_apply(x64[rows], to_f64(yb, W.dtype)[rows], ads, mod.slices, W.ids[rows], W.S, W.dtype,
                            max_rank=W.Rmax)
         got = from_device(y)[rows]
-        check_close(got, ref, W.dtype, f"workload {num} {mod.name} y")
+        check_close(got, ref, W.dtype, f"workload {num} {mod.name} y, {len(rows)} rows")
+        untouched = (W.ids < 0) | (W.ids >= W.S)
+        assert np.array_equal(bits(y)[untouched], (yb if W.dtype == "bf16" else yb.view(np.uint32))[untouched])
         if num == 2:
             W0 = to_f64(mod.W0, W.dtype)
-            merged = O.merged_apply(to_f64(mod.x, W.dtype), W0, ads, mod.slices, W.ids, W.S, W.dtype)
+            merged = O.merged_apply(x64, W0, ads, mod.slices, W.ids, W.S, W.dtype)
             check_close(got, merged, W.dtype, "merged-weight form")
         pool.close()
     R.close()
