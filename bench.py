@@ -95,6 +95,12 @@ class Instance:
             y = src["y"].clone()
             self.mods.append((pool, x, y))
         self.calls = [(p.handle, x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0)) for p, x, y in self.mods]
+        # the arguments of one grouped call over every module
+        import ctypes as C
+        n = len(self.calls)
+        self.group = (n, (C.c_void_p * n)(*[c[0] for c in self.calls]), (C.c_void_p * n)(*[c[1] for c in self.calls]),
+                      (C.c_int * n)(*[c[2] for c in self.calls]), (C.c_void_p * n)(*[c[3] for c in self.calls]),
+                      (C.c_int * n)(*[c[4] for c in self.calls]))
 
     def close(self):
         for p, _, _ in self.mods:
@@ -571,9 +577,17 @@ def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
 
 
 # ------------------------------------------------------------------ timing core
-def make_step(rx, lib, insts, T, ydt, stream, separate_routing: bool):
-    """One step on instance i % M: the routing and every module's fused call."""
+def make_step(rx, lib, insts, T, ydt, stream, separate_routing: bool, grouped: bool = False):
+    """One step on instance i % M: the routing and every module's fused call; grouped:
+    the routing and one grouped call over all modules (lora_route_linear_group)."""
     M = len(insts)
+
+    def group_step(i):
+        inst = insts[i % M]
+        n, P, X, LX, Y, LY = inst.group
+        st = lib.lora_route_linear_group(P, n, inst.routing.handle, inst.ids.data_ptr(), T, X, LX, Y, LY, ydt, stream)
+        if st:
+            raise rx.LoraError(st, "lora_route_linear_group")
 
     def step(i):
         inst = insts[i % M]
@@ -593,7 +607,7 @@ def make_step(rx, lib, insts, T, ydt, stream, separate_routing: bool):
             st = lib.lora_linear(pool, inst.routing.handle, xp, ldx, yp, ldy, ydt, stream)
             if st:
                 raise rx.LoraError(st, "lora_linear")
-    return step
+    return group_step if grouped and len(insts[0].calls) > 1 else step
 
 
 def time_steps(torch, step, steps: int):
@@ -657,12 +671,21 @@ def measure_workload(torch, rx, num: int, args):
     step_bytes = sum(acc.values())
     src, insts = build_instances(rx, torch, W, args, step_bytes)
     ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
-    step = make_step(rx, rx.lib, insts, W.T, ydt, torch.cuda.current_stream().cuda_stream, False)
+    stream = torch.cuda.current_stream().cuda_stream
+    grouped = len(W.modules) > 1 and not args.per_module
+    step = make_step(rx, rx.lib, insts, W.T, ydt, stream, False, grouped=grouped)
     steps = max(args.steps, 20)
     for i in range(max(args.warmup, len(insts))):
         step(i)
     ms, wall = time_steps(torch, step, steps)
     kern = kernel_times(rx, torch, step, steps)
+    per_module_us = None
+    if grouped:
+        # the same step as one fused call per module, for comparison
+        pm = make_step(rx, rx.lib, insts, W.T, ydt, stream, False, grouped=False)
+        for i in range(len(insts)):
+            pm(i)
+        per_module_us = round(time_steps(torch, pm, steps)[0] * 1e3, 3)
     for inst in insts:
         inst.close()
     del insts, src
@@ -675,8 +698,12 @@ def measure_workload(torch, rx, num: int, args):
            "step_frac_of_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
            "kernels": family_roofline(acc, kern),
            "routing_avg_us": round(kern["routing"]["avg_us"], 3) if "routing" in kern else None,
-           "steps_timed": steps, "setup_s": round(time.perf_counter() - t0, 1)}
-    log(f"workload {W.name}: {us:.1f} us/step, {res['step_hbm_gbps']} GB/s over the step "
+           "steps_timed": steps, "setup_s": round(time.perf_counter() - t0, 1),
+           "calls": "lora_route_linear_group (all modules in one shrink and one expand launch)" if grouped else
+                    "lora_route_linear + lora_linear per further module",
+           "per_module_calls_us_per_step": per_module_us}
+    log(f"workload {W.name}: {us:.1f} us/step ({'grouped' if grouped else 'per module'}; per-module calls "
+        f"{per_module_us} us/step), {res['step_hbm_gbps']} GB/s over the step "
         f"({100 * res['step_frac_of_peak']:.1f} % of 8 TB/s), kernels "
         + ", ".join(f"{k} {v['avg_launch_us']} us x{v['launches_per_step']} ({100 * v['frac_of_peak']:.1f} %)"
                     for k, v in res["kernels"].items()))
@@ -748,7 +775,8 @@ def run(args):
     stream = torch.cuda.current_stream().cuda_stream
     ydt = rx.LORA_BF16 if W.dtype == "bf16" else rx.LORA_F32
     lib, T = rx.lib, W.T
-    step = make_step(rx, lib, insts, T, ydt, stream, args.separate_routing)
+    grouped = len(W.modules) > 1 and not (args.per_module or args.separate_routing)
+    step = make_step(rx, lib, insts, T, ydt, stream, args.separate_routing, grouped=grouped)
 
     for i in range(args.warmup):
         step(i)
@@ -824,7 +852,7 @@ def run(args):
                    "slices": [m.slices for m in W.modules], "ranks": sorted(set(W.ranks.values())),
                    "max_lora_rank": W.Rmax, "parallelism": "none (1 GPU)",
                    "calls": "lora_build_routing + lora_linear" if args.separate_routing else
-                            "lora_route_linear + lora_linear"},
+                            "lora_route_linear_group" if grouped else "lora_route_linear + lora_linear"},
         "roofline": roofline,
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
                   "step_flops": flops, "bytes_by_path": by_path, "kernels": kern, "kernel_families": families,
@@ -856,6 +884,8 @@ def main():
     ap.add_argument("--workloads", default="3,4,5",
                     help="further workloads timed after the headline one, reported under extra.workloads")
     ap.add_argument("--no-workloads", action="store_true", help="time the headline workload only")
+    ap.add_argument("--per-module", action="store_true",
+                    help="multi-module workloads: one fused call per module instead of one grouped call")
     ap.add_argument("--separate-routing", action="store_true",
                     help="lora_build_routing + lora_linear per step instead of lora_route_linear for the first module")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")

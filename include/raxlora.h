@@ -95,6 +95,7 @@ typedef int lora_status;
 #define LORA_MAX_SLOTS     1024
 #define LORA_MAX_RANK      256
 #define LORA_MAX_IN_FEATURES 65536
+#define LORA_MAX_GROUP     8      /* target modules of one grouped call */
 
 /* Message for the last failing call on this thread ("" if none). Never NULL. */
 const char* lora_last_error(void);
@@ -318,6 +319,42 @@ lora_status lora_linear_join(const lora_pool* pool, const lora_routing* routing,
 lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing, const int32_t* token_slot_ids,
                                    int T, const void* x, int ldx, void* y, int ldy, lora_dtype ydtype,
                                    hipStream_t stream, hipEvent_t y_ready);
+
+/*
+ * Several target modules of one batch in one shrink and one expand launch: for each
+ * m < num_pools, lora_linear(pools[m], routing, x[m], ldx[m], y[m], ldy[m], ydtype),
+ * with the same results bitwise (every module's units compute what its own call
+ * computes).  This is the grouped form of the pages' layer step: [TRT-LLM] "前向替换:
+ * LoraLayer 的三条路径" sizes one intermediate buffer [num_layer_modules, batch_size,
+ * max_rank] and runs one grouped product over every (module, slot) problem of the
+ * layer; [vLLM-book] §16.4.4 add_shrink / add_expand take several slices in one call.
+ * A layer's q/k/v/o/gate/up/down modules then cost two launches instead of two each
+ * ([llama.cpp] "性能与工程取舍": in decode the extra cost of LoRA is mostly launches).
+ *   pools[m]: distinct linear pools with the routing's slot count, all of one weight
+ *   dtype and of max_lora_rank padding to one multiple of 32; each keeps its own
+ *   workspace, so no pool may appear twice.  x[m] is [T, in_features of pools[m]]
+ *   with row stride ldx[m]; y[m] is [T, D of pools[m]] with row stride ldy[m]; the y
+ *   of different modules must not share elements (they may be column ranges of one
+ *   buffer).  Host arrays pools, x, ldx, y, ldy are read during the call.
+ * Errors: INVALID_ARG (NULL array or entry, a repeated pool, an embedding pool),
+ * SHAPE (num_pools outside [1, LORA_MAX_GROUP], slot count or rank padding differing),
+ * DTYPE (weight dtypes differing, or as lora_linear), plus those of lora_linear for
+ * each module.
+ */
+lora_status lora_linear_group(const lora_pool* const* pools, int num_pools, const lora_routing* routing,
+                              const void* const* x, const int* ldx, void* const* y, const int* ldy, lora_dtype ydtype,
+                              hipStream_t stream);
+
+/*
+ * lora_build_routing(routing, token_slot_ids, T) followed by lora_linear_group: for
+ * 1 <= T <= 256 tokens and at most 255 slots the routing is built inside the grouped
+ * shrink launch (two launches for the whole layer step); larger batches take the
+ * routing launch first.  Routing outputs and y bitwise those of the separate calls.
+ * Arguments and errors as lora_build_routing and lora_linear_group.
+ */
+lora_status lora_route_linear_group(const lora_pool* const* pools, int num_pools, lora_routing* routing,
+                                    const int32_t* token_slot_ids, int T, const void* const* x, const int* ldx,
+                                    void* const* y, const int* ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
  * Embedding LoRA onto the caller's lookup result ([llama.cpp] "嵌入层:查表后再加增量"):

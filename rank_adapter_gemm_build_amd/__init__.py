@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libraxlora.so")
 LORA_F32, LORA_BF16, LORA_FP8E4M3 = 0, 1, 2
 LORA_SRC_DEVICE, LORA_PREMULTIPLY = 1, 2
 LORA_MAX_SLICES, LORA_MAX_SLOTS, LORA_MAX_RANK, LORA_MAX_IN_FEATURES = 8, 1024, 256, 65536
+LORA_MAX_GROUP = 8
 
 STATUS = {
     0: "LORA_OK", -1: "LORA_ERR_INVALID_ARG", -2: "LORA_ERR_SHAPE", -3: "LORA_ERR_DTYPE",
@@ -54,6 +55,10 @@ SIGNATURES = {
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_bandwidth_probe": (_I, [_VP, C.c_uint64, _VP, C.c_uint64, _I, _VP]),
+    "lora_linear_group": (_I, [C.POINTER(_P), _I, _P, C.POINTER(_VP), C.POINTER(C.c_int), C.POINTER(_VP),
+                               C.POINTER(C.c_int), _I, _VP]),
+    "lora_route_linear_group": (_I, [C.POINTER(_P), _I, _P, _VP, _I, C.POINTER(_VP), C.POINTER(C.c_int),
+                                     C.POINTER(_VP), C.POINTER(C.c_int), _I, _VP]),
     "lora_timing_enable": (_I, [_I]),
     "lora_timing_report": (_I, [C.POINTER(C.c_double), C.POINTER(C.c_int), _I]),
     "lora_timing_kernel_name": (C.c_char_p, [_I]),
@@ -563,4 +568,48 @@ def route_embedding(pool: Pool, routing: Routing, slot_ids, vocab_ids, y, stream
     _check(lib.lora_route_embedding(pool.handle, routing.handle, _ptr(slot_ids) if T else None, T,
                                     _ptr(vocab_ids) if T else None, _ptr(y), y.stride(0), _dt(y),
                                     _stream(stream) or None), "lora_route_embedding")
+    routing.T = T
+
+
+def _group_arrays(pools, xs, ys):
+    n = len(pools)
+    P = (C.c_void_p * n)(*[p.handle for p in pools])
+    X = (C.c_void_p * n)(*[_ptr(x) or None for x in xs])
+    LX = (C.c_int * n)(*[x.stride(0) for x in xs])
+    Y = (C.c_void_p * n)(*[_ptr(y) or None for y in ys])
+    LY = (C.c_int * n)(*[y.stride(0) for y in ys])
+    return n, P, X, LX, Y, LY
+
+
+def _check_group(pools, xs, ys, T):
+    if not (len(pools) == len(xs) == len(ys)) or not 1 <= len(pools) <= LORA_MAX_GROUP:
+        raise ValueError(f"give 1..{LORA_MAX_GROUP} pools with one x and one y each")
+    dts = {_dt(y) for y in ys}
+    if len(dts) != 1:
+        raise TypeError("every y of a grouped call has the same dtype")
+    for p, x, y in zip(pools, xs, ys):
+        _check_x(p, T, x)
+        _check_y(p, T, y)
+    for p, x, y in zip(pools, xs, ys):
+        _on_device(p.device, x=x, y=y)
+
+
+def linear_group(pools, routing: Routing, xs, ys, stream=None) -> None:
+    """linear(pools[m], routing, xs[m], ys[m]) for every m, in one shrink and one expand
+    launch (see lora_linear_group)."""
+    _check_group(pools, xs, ys, _routing_tokens(routing))
+    n, P, X, LX, Y, LY = _group_arrays(pools, xs, ys)
+    _check(lib.lora_linear_group(P, n, routing.handle, X, LX, Y, LY, _dt(ys[0]), _stream(stream) or None),
+           "lora_linear_group")
+
+
+def route_linear_group(pools, routing: Routing, ids, xs, ys, stream=None) -> None:
+    """routing.build(ids) then linear_group(pools, routing, xs, ys); for batches of up to
+    256 tokens the routing is built inside the grouped shrink launch (see
+    lora_route_linear_group)."""
+    T = _check_ids(ids, routing.device, "ids")
+    _check_group(pools, xs, ys, T)
+    n, P, X, LX, Y, LY = _group_arrays(pools, xs, ys)
+    _check(lib.lora_route_linear_group(P, n, routing.handle, _ptr(ids) if T else None, T, X, LX, Y, LY, _dt(ys[0]),
+                                       _stream(stream) or None), "lora_route_linear_group")
     routing.T = T

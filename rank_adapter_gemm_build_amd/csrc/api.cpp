@@ -172,9 +172,14 @@ rax::PoolView pool_view(const lora_pool* p) {
     v.tile0[n] = n <= p->N ? p->tile0[n] : p->tile0[p->N];
     v.mblk0[n] = n <= p->N ? p->mblk0[n] : p->mblk0[p->N];
   }
-  v.ordered = (int)p->order.size() == p->S ? 1 : 0;
-  for (size_t i = 0; i < p->order.size(); ++i) v.slot_order[i] = p->order[i];
   return v;
+}
+
+rax::SlotOrder slot_order(const lora_pool* p) {
+  rax::SlotOrder o{};
+  o.ordered = (int)p->order.size() == p->S ? 1 : 0;
+  for (size_t i = 0; i < p->order.size(); ++i) o.s[i] = p->order[i];
+  return o;
 }
 
 rax::RouteOut route_out(const lora_routing* r) {
@@ -332,8 +337,8 @@ lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const
 lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const rax::UView& U,
                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
   const rax::Plan pl = make_plan(pool, routing, true);
-  hipError_t e = rax::launch_expand(pool->wdtype, ydtype, pool_view(pool), route_view(routing), U, y, ldy,
-                                    pl, stream, timer_for(rax::kKExpand));
+  hipError_t e = rax::launch_expand(pool->wdtype, ydtype, pool_view(pool), slot_order(pool), route_view(routing), U,
+                                    y, ldy, pl, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "expand launch");
   return LORA_OK;
 }
@@ -400,6 +405,59 @@ lora_status route_linear_impl(const lora_pool* pool, lora_routing* routing, cons
   st = shrink_join_expand(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready, ids);
   if (st != LORA_OK) routing->T = -1;   // the routing may not have been built: unusable until rebuilt
   return st == LORA_OK ? ok() : st;
+}
+
+// Checks of a grouped call: 1..LORA_MAX_GROUP distinct linear pools on the routing's
+// device with its slot count, one weight dtype and one padded rank, each with its
+// own input and output.
+lora_status check_group(const lora_pool* const* pools, int n, const lora_routing* routing, int T,
+                        const void* const* x, const int* ldx, void* const* y, const int* ldy, lora_dtype ydtype) {
+  if (!pools || !x || !ldx || !y || !ldy) return fail(LORA_ERR_INVALID_ARG, "pools, x, ldx, y and ldy must not be NULL");
+  if (n < 1 || n > LORA_MAX_GROUP) return fail(LORA_ERR_SHAPE, "num_pools = %d outside [1, %d]", n, LORA_MAX_GROUP);
+  for (int m = 0; m < n; ++m) {
+    const lora_pool* p = pools[m];
+    if (!p) return fail(LORA_ERR_INVALID_ARG, "pools[%d] is NULL", m);
+    for (int q = 0; q < m; ++q)
+      if (pools[q] == p) return fail(LORA_ERR_INVALID_ARG, "pools[%d] repeats pools[%d] (one workspace per pool)", m, q);
+    if (p->embedding) return fail(LORA_ERR_INVALID_ARG, "pools[%d] is an embedding pool", m);
+    if (p->S != routing->S) return fail(LORA_ERR_SHAPE, "pools[%d] has %d slots, the routing %d", m, p->S, routing->S);
+    if (p->device != routing->device) return fail(LORA_ERR_INVALID_ARG, "pools[%d] is on another device", m);
+    if (p->wdtype != pools[0]->wdtype) return fail(LORA_ERR_DTYPE, "pools[%d] has another weight dtype", m);
+    if (p->Rk != pools[0]->Rk)
+      return fail(LORA_ERR_SHAPE, "pools[%d]: max_lora_rank %d pads to another rank step than pools[0]'s %d", m,
+                  p->Rmax, pools[0]->Rmax);
+    if (T > p->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds pools[%d]'s max_tokens = %d", T, m, p->max_tokens);
+    lora_status st = check_x(p, T, x[m], ldx[m]);
+    if (st != LORA_OK) return st;
+    if ((st = check_y(p, T, y[m], ldy[m], ydtype)) != LORA_OK) return st;
+  }
+  return LORA_OK;
+}
+
+lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing* routing, const void* const* x,
+                       const int* ldx, void* const* y, const int* ldy, lora_dtype ydtype, hipStream_t stream,
+                       const int32_t* self_ids) {
+  rax::GroupView G{};
+  G.n = n;
+  for (int m = 0; m < n; ++m) {
+    rax::GroupEntry& e = G.e[m];
+    e.P = pool_view(pools[m]);
+    e.x = x[m];
+    e.ldx = ldx[m];
+    e.y = y[m];
+    e.ldy = ldy[m];
+    e.U = workspace_view(pools[m], call_split(pools[m], routing).nsplit);
+    e.plan = make_plan(pools[m], routing, false);
+  }
+  const rax::RouteView R = route_view(routing);
+  rax::SelfRoute sr{self_ids, route_out(routing)};
+  hipError_t e = rax::launch_shrink_group(pools[0]->wdtype, G, R, self_ids ? &sr : nullptr, stream,
+                                          timer_for(rax::kKShrink));
+  if (e != hipSuccess) return hip_fail(e, "grouped shrink launch");
+  for (int m = 0; m < n; ++m) G.e[m].plan = make_plan(pools[m], routing, true);
+  e = rax::launch_expand_group(pools[0]->wdtype, ydtype, G, R, stream, timer_for(rax::kKExpand));
+  if (e != hipSuccess) return hip_fail(e, "grouped expand launch");
+  return LORA_OK;
 }
 
 }  // namespace
@@ -831,6 +889,42 @@ lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing,
                                    const void* x, int ldx, void* y, int ldy, lora_dtype ydtype, hipStream_t stream,
                                    hipEvent_t y_ready) {
   return route_linear_impl(pool, routing, ids, T, x, ldx, y, ldy, ydtype, stream, y_ready);
+}
+
+lora_status lora_linear_group(const lora_pool* const* pools, int num_pools, const lora_routing* routing,
+                              const void* const* x, const int* ldx, void* const* y, const int* ldy, lora_dtype ydtype,
+                              hipStream_t stream) {
+  if (!routing) return fail(LORA_ERR_INVALID_ARG, "routing is NULL");
+  if (routing->T < 0) return fail(LORA_ERR_STATE, "routing was never built");
+  lora_status st = check_group(pools, num_pools, routing, routing->T, x, ldx, y, ldy, ydtype);
+  if (st != LORA_OK) return st;
+  if (routing->T == 0) return ok();
+  DeviceGuard g(routing->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  st = group_impl(pools, num_pools, routing, x, ldx, y, ldy, ydtype, stream, nullptr);
+  return st == LORA_OK ? ok() : st;
+}
+
+lora_status lora_route_linear_group(const lora_pool* const* pools, int num_pools, lora_routing* routing,
+                                    const int32_t* ids, int T, const void* const* x, const int* ldx, void* const* y,
+                                    const int* ldy, lora_dtype ydtype, hipStream_t stream) {
+  if (!routing) return fail(LORA_ERR_INVALID_ARG, "routing is NULL");
+  if (T < 0) return fail(LORA_ERR_SHAPE, "T = %d < 0", T);
+  if (T > routing->max_tokens) return fail(LORA_ERR_CAPACITY, "T = %d exceeds max_tokens = %d", T, routing->max_tokens);
+  if (T > 0 && !ids) return fail(LORA_ERR_INVALID_ARG, "token_slot_ids is NULL");
+  lora_status st = check_group(pools, num_pools, routing, T, x, ldx, y, ldy, ydtype);
+  if (st != LORA_OK) return st;
+  // batches the shrink launch can route itself; others: the routing launch first
+  if (T < 1 || T > rax::kSelfRouteTokens || routing->S + 1 > rax::kSelfRouteKeys) {
+    if ((st = lora_build_routing(routing, ids, T, stream)) != LORA_OK) return st;
+    return lora_linear_group(pools, num_pools, routing, x, ldx, y, ldy, ydtype, stream);
+  }
+  DeviceGuard g(routing->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  routing->T = T;
+  st = group_impl(pools, num_pools, routing, x, ldx, y, ldy, ydtype, stream, ids);
+  if (st != LORA_OK) routing->T = -1;   // the routing may not have been built: unusable until rebuilt
+  return st == LORA_OK ? ok() : st;
 }
 
 lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, const int32_t* vocab_ids, void* y,

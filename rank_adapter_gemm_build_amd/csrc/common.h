@@ -61,9 +61,14 @@ struct PoolView {
   int d[kMaxSlices];
   int o[kMaxSlices];
   int tile0[kMaxSlices + 1];  // first expand column tile of each slice; tile0[N] = n_ctiles
-  int ordered;                // 1: slot_order below is valid (S <= kMaxOrderedSlots)
-  uint8_t slot_order[256];    // slots by descending rank (decode expand dispatch order)
   int mblk0[kMaxSlices + 1];  // first matrix-core column block of each slice; mblk0[N] = n_mblocks
+};
+
+// Dispatch order of a pool's slots for the decode expand units (a single-module
+// launch): slots by descending rank when `ordered`, else by index.
+struct SlotOrder {
+  int ordered;                // 1: s below is valid (S <= kMaxOrderedSlots)
+  uint8_t s[kMaxOrderedSlots];
 };
 
 struct RouteView {
@@ -111,6 +116,27 @@ struct Plan {
   int xcd_group;           // consecutive units dealt to one XCD (1 = plain round-robin)
 };
 
+// One module of a grouped launch (several target modules of one batch, sharing its
+// routing, in one shrink and one expand launch): its pool, input, output, rank-space
+// buffer and launch shape, and where its workgroups start in the launch.  A module's
+// workgroups are laid out exactly as in a launch of its own (matrix-core workers,
+// then decode units), so its units compute what they would compute there.
+constexpr int kMaxGroup = LORA_MAX_GROUP;
+struct GroupEntry {
+  PoolView P;
+  const void* x;
+  void* y;
+  int ldx, ldy;
+  UView U;
+  Plan plan;
+  int blk0;   // first workgroup of the module (a multiple of 8, so XCD numbering is kept)
+  int nm;     // its matrix-core workers
+};
+struct GroupView {
+  int n;
+  GroupEntry e[kMaxGroup];
+};
+
 // Optional per-launch timing: when start is non-null the kernel is launched with
 // hipExtLaunchKernel, which stamps the two events at the kernel's own start and end.
 struct KTimer {
@@ -153,9 +179,23 @@ hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, cons
                          const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
                          const KTimer& tm);
 
-hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
+hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const SlotOrder& order, const RouteView& R,
                          const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,
                          const KTimer& tm);
+// Workgroups of one module in a launch of its own (matrix-core workers, then decode
+// units rounded up for the XCD renumbering); a grouped launch concatenates them.
+int shrink_blocks(int wdtype, const PoolView& P, const Plan& plan, int& n_mfma_blocks);
+int expand_blocks(int wdtype, const PoolView& P, const Plan& plan, int& n_mfma_blocks);
+size_t expand_smem_bytes(int wdtype, int Rmax, int use_mfma);
+// Layout of a grouped launch: every module checked (shrink shapes) and its workgroups
+// placed after the previous module's (G.e[m].blk0 / nm set); false if any is invalid
+bool group_layout(int wdtype, GroupView& G, const RouteView& R, const SelfRoute* sr, bool expand, int& blocks);
+// Grouped launches: G.e[m].blk0 / nm set from the functions above; with sr the shrink
+// launch also builds the routing (T <= 256 tokens, S < 256 slots)
+hipError_t launch_shrink_group(int wdtype, const GroupView& G, const RouteView& R, const SelfRoute* sr,
+                               hipStream_t stream, const KTimer& tm);
+hipError_t launch_expand_group(int wdtype, int ydtype, const GroupView& G, const RouteView& R, hipStream_t stream,
+                               const KTimer& tm);
 // embedding pools: u (workspace split 0, rows by sorted position) = the rows of the
 // transposed A [V][Rmax] of each token's slot at its vocabulary id
 hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R, const int32_t* vocab_ids, int V,

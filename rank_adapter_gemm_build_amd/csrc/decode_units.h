@@ -25,6 +25,8 @@ namespace rax {
 constexpr int kShrinkRows = 16;   // rank rows per decode shrink block
 constexpr int kShrinkTok = 4;     // tokens per decode tile
 constexpr int kExpandTok = 4;
+// LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
+__host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }
 
 // Token ids at positions tt .. tt + 3 of slot s's segment: from the slot's routing
 // record when they are among its first kRecTokens (the record repeats the segment's

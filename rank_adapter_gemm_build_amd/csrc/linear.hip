@@ -1,4 +1,6 @@
-// Shrink and expand kernels: one launch each per call, covering both the short
+// Shrink kernels (and the launches shared with the expand: the grouped layout, the
+// embedding gather, the finishing pass of a standalone shrink): one launch each per
+// call, covering both the short
 // (decode) segments on the vector ALUs and the long segments on the matrix cores.
 //
 // Page "第16章 LoRA 适配器热切换", §16.4.2: with tokens grouped by slot, all LoRA branches
@@ -31,13 +33,8 @@
 // are added in split order where they are read (the expand), so the result does not
 // depend on timing and no atomics or cross-workgroup fences are needed.
 //
-// Decode expand unit (one wave: slot, column tile of one slice, token tiles).  Lanes
-// own 8 consecutive output columns, so each rank-major row of B^T streams as one
-// contiguous 1 KB request; the tile's rank-space values (split partials added) are
-// staged in the wave's LDS and read as broadcasts; the contraction over the rank
-// stays in registers.  The epilogue updates the token's row of y at its original
-// index (no permutation pass; page "TensorRT-LLM 源码完全拆解(二十一)", section "前向替换",
-// restores the order with index_copy_ instead), adding s * acc in fp32, one rounding.
+// The expand kernels (decode units and matrix-core units) are in expand_kernels.h,
+// compiled once per weight / output type pair.
 //
 // Operand loads are unconditional (addresses clamped into the operand, unused values
 // replaced by zero) and issued as one batch before the math.
@@ -47,6 +44,7 @@
 
 #include "device_util.h"
 #include "decode_units.h"
+#include "launch_util.h"
 #include "mfma_tiles.h"
 #include "route_wave.h"
 
@@ -135,54 +133,21 @@ __device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const
   });
 }
 
-// Matrix-core work items of one launch, split over the XCDs: workgroup b runs on XCD
-// b % 8, and XCD x takes the x-th contiguous eighth of the items (tiles in slot
-// order within).  Consecutive tiles of a segment share their slot's weights, and the
-// items of one tile share its tokens' data, so each XCD's L2 serves its own stretch
-// of the batch and weights and partial sums are fetched from HBM about once.
-// Worker i of an XCD takes items start + i, start + i + upx, ... (upx workers per
-// XCD; the launch provides at least one worker per item).
-struct MfmaItems {
-  int j, end, step;
-  __device__ __forceinline__ MfmaItems(int b, int n_blocks, int n_items) {
-    const int x = b % kXcds, upx = n_blocks / kXcds;
-    const int per = (n_items + kXcds - 1) / kXcds;
-    j = min(n_items, x * per) + b / kXcds;
-    end = min(n_items, (x + 1) * per);
-    step = upx;
-  }
-};
-
-// Workgroups of a launch: first the matrix-core workers (a multiple of 8, so the XCD
-// of a worker is its index mod 8), then the decode units.
-__host__ __device__ inline int mfma_blocks(int items_max) { return (items_max + kXcds - 1) / kXcds * kXcds; }
-
-// One wave per workgroup: matrix-core (k part, tile, row group) items, then decode
-// units.  SELF: the launch also builds the routing (route_wave in workgroup 0;
-// workgroups 1-7 are idle, so the others keep their XCD numbering), and the units
-// take their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead
-// of the routing outputs being written meanwhile.  T is the type of x, TW of the
-// weights (T, or FP8 with bf16 x).
-// Two waves per SIMD: asked of the compiler (which then keeps the matrix-core
-// accumulators in ordinary vector registers, 223 registers for the routing variant
-// instead of 240 + 24 accumulation registers, which allowed only one wave per SIMD)
+// One module's shrink workgroup b (b counted from the module's first workgroup):
+// matrix-core (k part, tile, row group) items, then decode units.  SELF: the launch
+// also builds the routing (route_wave in its first workgroup), and the units take
+// their segments and tiles from the batch's ids (BatchKeys, BatchTiles) instead of
+// the routing outputs being written meanwhile; sh is the wave's LDS for that.  T is
+// the type of x, TW of the weights (T, or FP8 with bf16 x).
 template <typename T, typename TW, bool SELF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
-                                                    int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
-  int b = blockIdx.x;
+__device__ __forceinline__ void shrink_body(const PoolView& P, const RouteView& R, const T* __restrict__ x, int ldx,
+                                            const UView& U, const Plan& plan, int n_mfma_blocks,
+                                            const int32_t* __restrict__ ids, int b, int* __restrict__ sh) {
   if constexpr (SELF) {
-    __shared__ __align__(16) int sh[route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64)];
-    static_assert(route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64) >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
-    if (b < kXcds) {
-      if (b == 0)
-        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
-      return;
-    }
-    b -= kXcds;
     int* tok = sh + kSelfRouteK;
     if (b >= n_mfma_blocks) {
       const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
-      if (d < plan.n_dec_blocks) shrink_decode_unit_self<T, TW>(P, R, sr.ids, x, ldx, U, plan, d, tok);
+      if (d < plan.n_dec_blocks) shrink_decode_unit_self<T, TW>(P, R, ids, x, ldx, U, plan, d, tok);
       return;
     }
     if constexpr (sizeof(T) == 2 && sizeof(TW) <= 2) {
@@ -195,7 +160,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sh
       const int4 te = *reinterpret_cast<const int4*>(P.table + min(lane_id(), P.S - 1));
       {
         BatchKeys K;
-        K.load(sr.ids, R.T, R.S);
+        K.load(ids, R.T, R.S);
         K.store(keys);
         ntiles = BatchTiles::build(K, R.S, R.mfma_min, R.tile_m, R.max_tiles, sh);
       }
@@ -243,12 +208,67 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sh
   }
 }
 
+// LDS ints of a self-routing shrink workgroup
+constexpr int kShrinkSelfLds = route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64);
+static_assert(kShrinkSelfLds >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
+
+// One wave per workgroup.  SELF: workgroup 0 runs route_wave and workgroups 1-7 are
+// idle, so the others keep their XCD numbering.
+// Two waves per SIMD: asked of the compiler (which then keeps the matrix-core
+// accumulators in ordinary vector registers, 223 registers for the routing variant
+// instead of 240 + 24 accumulation registers, which allowed only one wave per SIMD)
+template <typename T, typename TW, bool SELF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void shrink_kernel(PoolView P, RouteView R, const T* __restrict__ x,
+                                                    int ldx, UView U, Plan plan, int n_mfma_blocks, SelfRoute sr) {
+  int b = blockIdx.x;
+  if constexpr (SELF) {
+    __shared__ __align__(16) int sh[kShrinkSelfLds];
+    if (b < kXcds) {
+      if (b == 0)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
+      return;
+    }
+    shrink_body<T, TW, true>(P, R, x, ldx, U, plan, n_mfma_blocks, sr.ids, b - kXcds, sh);
+  } else {
+    shrink_body<T, TW, false>(P, R, x, ldx, U, plan, n_mfma_blocks, nullptr, b, nullptr);
+  }
+}
+
+// Several modules of one batch in one launch: workgroup b runs as workgroup
+// b - blk0 of its module's own launch would.
+template <typename T, typename TW, bool SELF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void shrink_group_kernel(GroupView G, RouteView R, SelfRoute sr) {
+  int b = blockIdx.x;
+  if constexpr (SELF) {
+    __shared__ __align__(16) int sh[kShrinkSelfLds];
+    if (b < kXcds) {
+      if (b == 0)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out, sh);
+      return;
+    }
+    b -= kXcds;
+    const GroupEntry& e = G.e[group_module(G, b)];
+    shrink_body<T, TW, true>(e.P, R, static_cast<const T*>(e.x), e.ldx, e.U, e.plan, e.nm, sr.ids, b - e.blk0, sh);
+  } else {
+    const GroupEntry& e = G.e[group_module(G, b)];
+    shrink_body<T, TW, false>(e.P, R, static_cast<const T*>(e.x), e.ldx, e.U, e.plan, e.nm, nullptr, b - e.blk0,
+                              nullptr);
+  }
+}
+
+int shrink_blocks(int wdtype, const PoolView& P, const Plan& plan, int& n_mfma_blocks) {
+  (void)wdtype;
+  (void)P;
+  n_mfma_blocks = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
+  const int q = kXcds * plan.xcd_group;
+  return n_mfma_blocks + (plan.n_dec_blocks + q - 1) / q * q;
+}
+
 template <typename T, typename TW>
 static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, int ldx, const UView& U,
                             const Plan& plan, const SelfRoute* sr, hipStream_t stream, const KTimer& tm) {
-  const int nm = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
-  const int q = kXcds * plan.xcd_group;
-  const int blocks = nm + (plan.n_dec_blocks + q - 1) / q * q;
+  int nm;
+  const int blocks = shrink_blocks(0, P, plan, nm);
   if (sr)
     RAX_LAUNCH(tm, (shrink_kernel<T, TW, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
                *sr);
@@ -257,23 +277,71 @@ static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, i
                SelfRoute{});
 }
 
+// The checks of a shrink launch's shape, shared by single and grouped launches
+static bool shrink_shape_ok(int wdtype, const PoolView& P, const RouteView& R, const UView& U, const Plan& plan,
+                            const SelfRoute* sr) {
+  const int cw = 64 * (wdtype == LORA_F32 ? 4 : 8);   // x is bf16 for FP8 pools
+  const int chunks = (P.k + cw - 1) / cw;
+  return !(plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit ||
+           plan.ns < 1 || plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
+           plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
+           (plan.use_mfma && (wdtype == LORA_F32 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)) ||
+           (sr && (!sr->ids || R.T < 1 || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)));
+}
+
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
                          const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
                          const KTimer& tm) {
-  const int cw = 64 * (wdtype == LORA_F32 ? 4 : 8);   // x is bf16 for FP8 pools
-  const int chunks = (P.k + cw - 1) / cw;
-  if (plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit || plan.ns < 1 ||
-      plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
-      plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
-      (plan.use_mfma && (wdtype == LORA_F32 || plan.tile_slots < 1 || plan.nrg * 64 < P.N * P.Rmax)) ||
-      (sr && (!sr->ids || R.T < 1 || R.T > kSelfRouteT || R.S + 1 > kSelfRouteK)))
-    return hipErrorInvalidValue;
+  if (!shrink_shape_ok(wdtype, P, R, U, plan, sr)) return hipErrorInvalidValue;
   if (wdtype == LORA_BF16)
     launch_shrink_t<uint16_t, uint16_t>(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
   else if (wdtype == LORA_FP8E4M3)
     launch_shrink_t<uint16_t, uint8_t>(P, R, static_cast<const uint16_t*>(x), ldx, U, plan, sr, stream, tm);
   else
     launch_shrink_t<float, float>(P, R, static_cast<const float*>(x), ldx, U, plan, sr, stream, tm);
+  return hipGetLastError();
+}
+
+// Every module's shape checked, and its workgroups laid out as in a launch of its
+// own, one module after the other (blk0 and nm set here).
+bool group_layout(int wdtype, GroupView& G, const RouteView& R, const SelfRoute* sr, bool expand,
+                         int& blocks) {
+  if (G.n < 1 || G.n > kMaxGroup) return false;
+  blocks = 0;
+  for (int m = 0; m < G.n; ++m) {
+    GroupEntry& e = G.e[m];
+    if (!e.x && !expand) return false;
+    if (!e.y && expand) return false;
+    int nm;
+    const int nb = expand ? expand_blocks(wdtype, e.P, e.plan, nm) : shrink_blocks(wdtype, e.P, e.plan, nm);
+    if (!expand && !shrink_shape_ok(wdtype, e.P, R, e.U, e.plan, sr)) return false;
+    e.blk0 = blocks;
+    e.nm = nm;
+    blocks += nb;
+  }
+  return blocks > 0;
+}
+
+template <typename T, typename TW>
+static void launch_shrink_group_t(const GroupView& G, int blocks, const RouteView& R, const SelfRoute* sr,
+                                  hipStream_t stream, const KTimer& tm) {
+  if (sr)
+    RAX_LAUNCH(tm, (shrink_group_kernel<T, TW, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, G, R, *sr);
+  else
+    RAX_LAUNCH(tm, (shrink_group_kernel<T, TW, false>), dim3(blocks), dim3(64), 0u, stream, G, R, SelfRoute{});
+}
+
+hipError_t launch_shrink_group(int wdtype, const GroupView& G0, const RouteView& R, const SelfRoute* sr,
+                               hipStream_t stream, const KTimer& tm) {
+  GroupView G = G0;
+  int blocks;
+  if (!group_layout(wdtype, G, R, sr, false, blocks)) return hipErrorInvalidValue;
+  if (wdtype == LORA_BF16)
+    launch_shrink_group_t<uint16_t, uint16_t>(G, blocks, R, sr, stream, tm);
+  else if (wdtype == LORA_FP8E4M3)
+    launch_shrink_group_t<uint16_t, uint8_t>(G, blocks, R, sr, stream, tm);
+  else
+    launch_shrink_group_t<float, float>(G, blocks, R, sr, stream, tm);
   return hipGetLastError();
 }
 
@@ -409,212 +477,6 @@ hipError_t launch_embed_gather_tok(int wdtype, const PoolView& P, const RouteVie
     else
       RAX_LAUNCH(tm, (embed_gather_tok_kernel<float, false>), dim3(blocks), dim3(256), 0u, stream, P, R, slot_ids,
                  vocab_ids, V, W, none);
-  }
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ decode expand
-// LDS floats per wave for the decode expand: the rank padded to 16, times 4 tokens
-__host__ __device__ constexpr int expand_usm_floats(int Rmax) { return kExpandTok * ((Rmax + 15) / 16 * 16); }
-
-// Split partials of a decode expand tile's rank-space values, QV per lane: value
-// idx = lane + 64 q is rank idx / 4 of token idx % 4 (token-fastest, as the tile reads
-// them from LDS).  load() issues the first kUSplitBatch splits of every value
-// unconditionally (clamped addresses; splits past nsplit re-read the last), so it
-// can go out in the same batch as the tile's B^T and y rows; stage() adds them in
-// split order (-0.0f, the exact identity, for splits past nsplit; any further batch
-// loaded there) and writes usm, zero past the rank or the tile's tokens.
-template <int QV>
-struct DecodeUPartials {
-  float pv[QV][kUSplitBatch];
-  const float* base[QV];
-  bool ok[QV];
-  __device__ __forceinline__ void load(const UView& U, int n, int row0, int nt, int r) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int qv = 0; qv < QV; ++qv) {
-      const int idx = lane + 64 * qv, j = idx >> 2, i = idx & 3;
-      ok[qv] = i < nt && j < r;
-      base[qv] = U.p + n * U.n_stride + (long long)(row0 + (ok[qv] ? i : 0)) * U.row_stride + (ok[qv] ? j : 0);
-#pragma unroll
-      for (int q = 0; q < kUSplitBatch; ++q) pv[qv][q] = base[qv][(long long)min(q, U.nsplit - 1) * U.split_stride];
-    }
-  }
-  __device__ __forceinline__ void stage(const UView& U, int rp, float* __restrict__ usm) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int qv = 0; qv < QV; ++qv) {
-      float v = pv[qv][0];
-#pragma unroll
-      for (int q = 1; q < kUSplitBatch; ++q) v += q < U.nsplit ? pv[qv][q] : -0.f;
-      for (int q0 = kUSplitBatch; q0 < U.nsplit; q0 += 4) {
-        float w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = base[qv][(long long)min(q0 + q, U.nsplit - 1) * U.split_stride];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v += q0 + q < U.nsplit ? w[q] : -0.f;
-      }
-      const int idx = lane + 64 * qv;
-      if (idx < kExpandTok * rp) usm[idx] = ok[qv] ? v : 0.f;
-    }
-  }
-};
-
-// One decode expand item: column tile [c0, c0 + 512) of slice n, token tiles
-// tt0, tt0 + 4 * ntg, ... of slot s.  Per tile: the tile's rank-space values (split
-// partials added in split order, from L2) are staged in the wave's LDS token-fastest,
-// and the B^T rows and y rows are loaded, then the contraction.  For the first tile,
-// when the padded rank gives at most QV values per lane (QV > 0), the partials go
-// out in the same batch as the B^T and y rows, so the tile waits for one round trip
-// after its record; other tiles stage first, then load B^T and y.
-template <typename TW, typename TY, int QV>
-__device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const RouteView& R, const UView& U,
-                                                    TY* __restrict__ y, int ldy, int s, const SlotEntry& e,
-                                                    int n, int c0, int L, int p0, int tt0, int4 tq0, int ntg,
-                                                    float* __restrict__ usm) {
-  using Tile = ExpandTile<TW, TY>;
-  const int lane = lane_id();
-  const int r = e.rank;
-  const int rp = (r + Tile::RB - 1) / Tile::RB * Tile::RB;   // rank padded to the row batch
-  const TW* __restrict__ bt_slot = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n];
-  int tt = tt0;
-  if constexpr (QV > 0) {
-    if (!U.by_token && kExpandTok * rp <= 64 * QV) {
-      const int nt = min(kExpandTok, L - tt);
-      DecodeUPartials<QV> up;
-      up.load(U, n, p0 + tt, nt, r);
-      Tile tile;
-      tile.issue(P, bt_slot, y, ldy, n, c0, r, tq0);
-      sched_fence();
-      up.stage(U, rp, usm);
-      wave_lds_sync();
-      tile.finish(P, r, nt, e.scale, reinterpret_cast<const float4*>(usm));
-      wave_lds_sync();
-      tt += ntg * kExpandTok;
-    }
-  }
-  for (; tt < L; tt += ntg * kExpandTok) {
-    const int nt = min(kExpandTok, L - tt);
-    const int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
-    for (int idx = lane; idx < kExpandTok * rp; idx += 64) {
-      const int j = idx >> 2, i = idx & 3;
-      const bool ok = i < nt && j < r;
-      const int ic = ok ? i : 0, jc = ok ? j : 0;
-      const long long row = U.by_token ? (long long)R.sorted[p0 + tt + ic] : (long long)(p0 + tt + ic);
-      const float v = sum_splits(U.p + n * U.n_stride + row * U.row_stride + jc, U.split_stride, U.nsplit);
-      usm[idx] = ok ? v : 0.f;
-    }
-    Tile tile;
-    tile.issue(P, bt_slot, y, ldy, n, c0, r, tq);
-    wave_lds_sync();
-    tile.finish(P, r, nt, e.scale, reinterpret_cast<const float4*>(usm));
-    wave_lds_sync();
-  }
-}
-
-template <typename TW, typename TY, int QV>
-__device__ __forceinline__ void expand_decode_item(const PoolView& P, const RouteView& R, const UView& U,
-                                                   TY* __restrict__ y, int ldy, const Plan& plan,
-                                                   int item, float* __restrict__ usm) {
-  // token-tile siblings (same slot and columns, same rows of B^T) are neighbours
-  const int tg = item % plan.ntg;
-  const int rest = item / plan.ntg;
-  const int ct = rest % P.n_ctiles, si = rest / P.n_ctiles;
-  const int s = P.ordered ? (int)P.slot_order[si] : si;   // high-rank slots first
-  // first round trip: record header, token ids of the first tile, slot-table entry
-  const int tt0 = tg * kExpandTok;
-  const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
-  int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
-                                   : make_int4(0, 0, 0, 0);
-  const SlotEntry e = P.table[s];
-  const int L = hdr.x, p0 = hdr.y;
-  if (tt0 >= L) return;
-  if (plan.use_mfma && L >= R.mfma_min) return;
-  if (e.rank == 0 || e.scale == 0.f) return;
-  if (tt0 + 4 > kRecTokens) tq0 = segment_tokens(R, s, tt0, p0, L);
-  int n = 0;
-  while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
-  if (!((e.slice_mask >> n) & 1u)) return;
-  const int c0 = (ct - P.tile0[n]) * kTileCols;
-  expand_decode_tiles<TW, TY, QV>(P, R, U, y, ldy, s, e, n, c0, L, p0, tt0, tq0, plan.ntg, usm);
-}
-
-// One wave per workgroup: matrix-core (tile, column group) items, then decode items.
-// Waves per SIMD asked of the compiler: 2 where the body fits 256 registers without
-// spilling (up to two rank steps of 32, except FP8 weights with fp32 outputs); the
-// higher-rank bodies keep their natural allocation (one wave per SIMD).
-template <typename TW, typename TY, int KSM>
-struct ExpandWaves {
-  static constexpr int value = (KSM <= 2 && !(sizeof(TW) == 1 && sizeof(TY) == 4)) ? 2 : 1;
-};
-
-template <typename TW, typename TY, int KSM>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_kernel(PoolView P, RouteView R, UView U,
-                                                    TY* __restrict__ y, int ldy, Plan plan, int n_mfma_blocks) {
-  extern __shared__ float smem[];
-  const int b = blockIdx.x;
-  if (b >= n_mfma_blocks) {
-    const int d = xcd_logical_block(b - n_mfma_blocks, plan.xcd_group);
-    // values per lane of the first tile's early partial loads: the padded rank over 16
-    if (d < plan.n_dec_blocks) expand_decode_item<TW, TY, (KSM <= 2 ? 2 * KSM : 0)>(P, R, U, y, ldy, plan, d, smem);
-    return;
-  }
-  if constexpr (sizeof(TW) <= 2) {   // bf16 and FP8 weights
-    LaneTable lt;
-    lt.load(P);   // in flight with the tile count
-    for (MfmaItems it(b, n_mfma_blocks, R.meta[kMetaTiles] * plan.n_mgroups); it.j < it.end; it.j += it.step) {
-      const int tile = it.j / plan.n_mgroups, g = it.j - tile * plan.n_mgroups;
-      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, lt, smem);
-    }
-  }
-}
-
-template <typename TW, typename TY>
-static void launch_expand_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
-                            const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan, int nm,
-                            const KTimer& tm) {
-  switch (ksm) {
-    case 1: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    case 2: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    case 4: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-    default: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan, nm); break;
-  }
-}
-
-size_t expand_smem_bytes(int wdtype, int Rmax, int use_mfma) {
-  size_t f = (size_t)expand_usm_floats(Rmax);
-  if (use_mfma && wdtype != LORA_F32 && (size_t)kExpandMfmaWaveFloats > f) f = kExpandMfmaWaveFloats;
-  return f * sizeof(float);
-}
-
-hipError_t launch_expand(int wdtype, int ydtype, const PoolView& P, const RouteView& R,
-                         const UView& U, void* y, int ldy, const Plan& plan, hipStream_t stream,
-                         const KTimer& tm) {
-  if (plan.xcd_group < 1 || plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
-      (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
-      plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
-      (plan.use_mfma && (wdtype == LORA_F32 || plan.tile_slots < 1 || plan.n_mgroups < 1 ||
-                         (plan.cb != 1 && plan.cb != kMfmaColBlocksPerUnit))))
-    return hipErrorInvalidValue;
-  const int nm = plan.use_mfma ? mfma_blocks(plan.n_mgroups * plan.tile_slots) : 0;
-  const int q = kXcds * plan.xcd_group;
-  const dim3 grid(nm + (plan.n_dec_blocks + q - 1) / q * q);
-  const uint32_t lds = (uint32_t)expand_smem_bytes(wdtype, P.Rmax, plan.use_mfma);
-  // rank steps of 32 the matrix-core part keeps in registers: Rk / 32 rounded up to a power of 2
-  const int ksm = P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8;
-  if (wdtype == LORA_BF16) {
-    if (ydtype == LORA_BF16)
-      launch_expand_w<uint16_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
-    else
-      launch_expand_w<uint16_t, float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
-  } else if (wdtype == LORA_FP8E4M3) {
-    if (ydtype == LORA_BF16)
-      launch_expand_w<uint8_t, uint16_t>(ksm, grid, lds, stream, P, R, U, static_cast<uint16_t*>(y), ldy, plan, nm, tm);
-    else
-      launch_expand_w<uint8_t, float>(ksm, grid, lds, stream, P, R, U, static_cast<float*>(y), ldy, plan, nm, tm);
-  } else {
-    RAX_LAUNCH(tm, (expand_kernel<float, float, 1>), grid, dim3(64), lds, stream, P, R, U,
-               static_cast<float*>(y), ldy, plan, nm);
   }
   return hipGetLastError();
 }
