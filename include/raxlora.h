@@ -96,6 +96,7 @@ typedef int lora_status;
 #define LORA_MAX_RANK      256
 #define LORA_MAX_IN_FEATURES 65536
 #define LORA_MAX_GROUP     8      /* target modules of one grouped call */
+#define LORA_NOALLOC_SCRATCH_BYTES (16u << 20)   /* scratch of lora_linear_noalloc, per GPU */
 
 /* Message for the last failing call on this thread ("" if none). Never NULL. */
 const char* lora_last_error(void);
@@ -319,6 +320,25 @@ lora_status lora_linear_join(const lora_pool* pool, const lora_routing* routing,
 lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing, const int32_t* token_slot_ids,
                                    int T, const void* x, int ldx, void* y, int ldy, lora_dtype ydtype,
                                    hipStream_t stream, hipEvent_t y_ready);
+
+/*
+ * lora_linear for callers that cannot allocate device memory at call time (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same shrink and expand launches with the same results bitwise, but the k-split
+ * partial sums live in a fixed scratch array of LORA_NOALLOC_SCRATCH_BYTES inside the
+ * library's device image instead of the pool's workspace.  The call allocates and
+ * frees nothing (the array's device address is looked up once per GPU, on the first
+ * call there).  The caller still passes x and y as for lora_linear.
+ * Every call on one GPU shares that GPU's array and leaves its last contents there;
+ * nothing in it needs to start at zero.  Calls that overlap in time on one GPU (other
+ * streams, other threads) race on it: serialise them, e.g. on one stream.
+ * Needs nsplit * num_slices * T * Rk * 4 bytes, where Rk is max_lora_rank rounded up
+ * to 32 and nsplit at most 16 (in_features / 512 rounded up, halved for batches of at
+ * least 64 tokens per slot); above the maximum the call fails with CAPACITY before any
+ * work is enqueued.  Arguments and other errors as lora_linear.
+ */
+lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx, void* y,
+                                int ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
  * Several target modules of one batch in one shrink and one expand launch: for each

@@ -19,6 +19,7 @@ LORA_F32, LORA_BF16, LORA_FP8E4M3 = 0, 1, 2
 LORA_SRC_DEVICE, LORA_PREMULTIPLY = 1, 2
 LORA_MAX_SLICES, LORA_MAX_SLOTS, LORA_MAX_RANK, LORA_MAX_IN_FEATURES = 8, 1024, 256, 65536
 LORA_MAX_GROUP = 8
+LORA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS = {
     0: "LORA_OK", -1: "LORA_ERR_INVALID_ARG", -2: "LORA_ERR_SHAPE", -3: "LORA_ERR_DTYPE",
@@ -55,6 +56,7 @@ SIGNATURES = {
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_bandwidth_probe": (_I, [_VP, C.c_uint64, _VP, C.c_uint64, _I, _VP]),
+    "lora_linear_noalloc": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
     "lora_linear_group": (_I, [C.POINTER(_P), _I, _P, C.POINTER(_VP), C.POINTER(C.c_int), C.POINTER(_VP),
                                C.POINTER(C.c_int), _I, _VP]),
     "lora_route_linear_group": (_I, [C.POINTER(_P), _I, _P, _VP, _I, C.POINTER(_VP), C.POINTER(C.c_int),

@@ -875,6 +875,33 @@ lora_status lora_linear(const lora_pool* pool, const lora_routing* routing, cons
   return linear_impl(pool, routing, x, ldx, y, ldy, ydtype, stream, nullptr);
 }
 
+lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx, void* y,
+                                int ldy, lora_dtype ydtype, hipStream_t stream) {
+  lora_status st = check_pair(pool, routing);
+  if (st != LORA_OK) return st;
+  if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
+  if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
+  if (routing->T == 0) return ok();
+  // the partials of this call: [nsplit][N][T][Rk] fp32, rows by sorted position
+  const CallSplit cs = call_split(pool, routing);
+  const size_t need = (size_t)cs.nsplit * pool->N * routing->T * pool->Rk * sizeof(float);
+  if (need > rax::kNoAllocScratchBytes)
+    return fail(LORA_ERR_CAPACITY, "this call needs %zu bytes of scratch (%d k splits x %d slices x %d tokens x %d "
+                "ranks x 4), above the %zu-byte array", need, cs.nsplit, pool->N, routing->T, pool->Rk,
+                rax::kNoAllocScratchBytes);
+  DeviceGuard g(pool->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  void* scratch = nullptr;
+  hipError_t e = rax::noalloc_scratch(pool->device, &scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  const long long rows = routing->T;
+  const rax::UView W{static_cast<float*>(scratch), (long long)pool->N * rows * pool->Rk, rows * pool->Rk, pool->Rk,
+                     cs.nsplit, 0};
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  return ok();
+}
+
 lora_status lora_linear_join(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
                              void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready) {
   return linear_impl(pool, routing, x, ldx, y, ldy, ydtype, stream, y_ready);

@@ -40,6 +40,7 @@ constexpr int kRecTokens = kRecInts - 4;   // token ids a slot record holds
 constexpr bool kHaveMfmaPath = true;    // matrix-core kernels compiled in
 constexpr int kSelfRouteTokens = 256;   // most tokens of a batch whose shrink launch builds its routing
 constexpr int kSelfRouteKeys = 256;     // most keys (slots + 1) of such a batch
+constexpr size_t kNoAllocScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;   // the allocation-free call's scratch
 
 struct SlotEntry {
   int32_t rank;         // 0 = empty slot
@@ -205,6 +206,10 @@ hipError_t launch_embed_gather(int wdtype, const PoolView& P, const RouteView& R
 hipError_t launch_embed_gather_tok(int wdtype, const PoolView& P, const RouteView& R, const int32_t* slot_ids,
                                    const int32_t* vocab_ids, int V, const UView& W, const SelfRoute* sr,
                                    hipStream_t stream, const KTimer& tm);
+// Device address of the allocation-free call's scratch array on `device`, which
+// must be the current device (taken with hipGetSymbolAddress on the first call per
+// device, then kept); kNoAllocScratchBytes long.
+hipError_t noalloc_scratch(int device, void** ptr);
 // diagnostics: a streaming read of read_bytes (ratio <= 0; one word per thread into dst),
 // or a read with one 16-byte chunk written per `ratio` chunks read
 hipError_t launch_bandwidth_probe(const void* src, size_t read_bytes, void* dst, size_t dst_bytes, int ratio,

@@ -141,6 +141,11 @@ def test_null_arguments_rejected_without_device():
     assert rx.lib.lora_route_embedding(None, None, None, 0, None, None, 8, rx.LORA_BF16, None) == \
         rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_bandwidth_probe(None, 1 << 20, None, 1 << 22, 0, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_linear_noalloc(None, None, None, 8, None, 8, rx.LORA_BF16, None) == rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_linear_group(None, 1, None, None, None, None, None, rx.LORA_BF16, None) == \
+        rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_route_linear_group(None, 1, None, None, 0, None, None, None, None, rx.LORA_BF16, None) == \
+        rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_pool_destroy(None) == rx.LORA_OK
     assert rx.lib.lora_routing_destroy(None) == rx.LORA_OK
 
