@@ -231,6 +231,8 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
                 raise rx.LoraError(st, "lora_linear")
 
     res = {}
+    if args.only_overlap:
+        return measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res)
     # graphs of G steps each, covering every instance
     graphs = []
     side = torch.cuda.Stream()
@@ -291,6 +293,12 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
         res["seq_routing_step"] = f"lora_build_routing_seq ({T // p} sequences x {p} tokens) + lora_linear per module"
         log(f"sequence-routed step: {res['seq_routing_step_us']:.2f} us/step")
 
+    return measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res)
+
+
+def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
+    """The caller's base GEMM beside the LoRA step (see measure_graph_and_overlap)."""
+    T, M = W.T, len(insts)
     if len(W.modules) == 1 and "W0T" in src[0]:
         W0T = src[0]["W0T"]
         sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
@@ -359,10 +367,17 @@ def measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args):
             if st:
                 raise rx.LoraError(st, "lora_route_linear_join")
 
+        # the forms run one after the other, 2 ms apart (so a kernel trace separates them)
         res["base_gemm_us"] = round(timed(only_gemm), 3)
+        time.sleep(0.002)
         res["gemm_then_lora_us_per_step"] = round(timed(serial), 3)
+        time.sleep(0.002)
         res["gemm_beside_lora_us_per_step"] = round(timed(overlap), 3)
+        time.sleep(0.002)
         res["gemm_beside_lora_independent_steps_us_per_step"] = round(timed(overlap_free), 3)
+        time.sleep(0.002)
+        if args.only_overlap:
+            return res
 
         # the two forms captured in HIP graphs of G2 chained steps each: serial (GEMM then
         # LoRA on one stream) and forked (each GEMM on a side stream that first waits for
@@ -460,10 +475,12 @@ def measure_embedding(torch, rx, lib, W, args, vocab=32000):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
 
+    ids_p = ids.data_ptr()
+    calls = [(pool.handle, R.handle, v.data_ptr(), y.data_ptr(), y.stride(0)) for pool, R, v, y in insts]
+
     def step(i):
-        pool, R, v, y = insts[i % M]
-        st = lib.lora_route_embedding(pool.handle, R.handle, ids.data_ptr(), T, v.data_ptr(), y.data_ptr(), y.stride(0),
-                                      rx.LORA_BF16, stream)
+        ph, rh, vp, yp, ldy = calls[i % M]
+        st = lib.lora_route_embedding(ph, rh, ids_p, T, vp, yp, ldy, rx.LORA_BF16, stream)
         if st:
             raise rx.LoraError(st, "lora_route_embedding")
 
@@ -535,16 +552,34 @@ def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
 
+    import ctypes as C
+    groups = []
+    for R, mods in insts:
+        n = len(mods)
+        groups.append((n, (C.c_void_p * n)(*[p.handle for p, _, _ in mods]),
+                       (C.c_void_p * n)(*[x.data_ptr() for _, x, _ in mods]), (C.c_int * n)(*[x.stride(0) for _, x, _ in mods]),
+                       (C.c_void_p * n)(*[y.data_ptr() for _, _, y in mods]), (C.c_int * n)(*[y.stride(0) for _, _, y in mods])))
+    grouped = len(W.modules) > 1 and not args.per_module
+
+    # every pointer and stride taken once, so the timed loop makes no torch calls
+    ids_p = ids.data_ptr()
+    calls = [(R.handle, [(p.handle, x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0)) for p, x, y in mods])
+             for R, mods in insts]
+
     def step(i):
-        R, mods = insts[i % M]
-        pool, x, y = mods[0]
-        st = lib.lora_route_linear(pool.handle, R.handle, ids.data_ptr(), T, x.data_ptr(), x.stride(0), y.data_ptr(),
-                                   y.stride(0), rx.LORA_BF16, stream)
+        if grouped:
+            n, P, X, LX, Y, LY = groups[i % M]
+            st = lib.lora_route_linear_group(P, n, calls[i % M][0], ids_p, T, X, LX, Y, LY, rx.LORA_BF16, stream)
+            if st:
+                raise rx.LoraError(st, "lora_route_linear_group")
+            return
+        rh, mc = calls[i % M]
+        pool, xp, ldx, yp, ldy = mc[0]
+        st = lib.lora_route_linear(pool, rh, ids_p, T, xp, ldx, yp, ldy, rx.LORA_BF16, stream)
         if st:
             raise rx.LoraError(st, "lora_route_linear")
-        for pool, x, y in mods[1:]:
-            st = lib.lora_linear(pool.handle, R.handle, x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0),
-                                 rx.LORA_BF16, stream)
+        for pool, xp, ldx, yp, ldy in mc[1:]:
+            st = lib.lora_linear(pool, rh, xp, ldx, yp, ldy, rx.LORA_BF16, stream)
             if st:
                 raise rx.LoraError(st, "lora_linear")
 
@@ -571,7 +606,8 @@ def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
             pool.close()
     res = {"us_per_step": round(us, 3), "tokens_per_s": round(T / (us * 1e-6), 1), "step_algorithmic_bytes": step_bytes,
            "step_hbm_gbps": round(step_bytes / (us * 1e-6) / 1e9, 2), "kernels_avg_us": kern, "rotation_instances": M,
-           "weights": "e4m3 (OCP), activations and outputs bf16; vector units only"}
+           "calls": "lora_route_linear_group" if grouped else "lora_route_linear + lora_linear per further module",
+           "weights": "e4m3 (OCP), activations and outputs bf16; the matrix-core shrink on the FP8 matrix cores"}
     log(f"FP8 pools: {us:.2f} us/step ({step_bytes / 1e6:.1f} MB algorithmic), kernels {kern}")
     return res
 
@@ -688,7 +724,12 @@ def measure_workload(torch, rx, num: int, args):
         per_module_us = round(time_steps(torch, pm, steps)[0] * 1e3, 3)
     for inst in insts:
         inst.close()
-    del insts, src
+    insts = []
+    torch.cuda.synchronize()
+    fp8 = None
+    if not args.no_extras and len(W.modules) > 1:
+        fp8 = measure_fp8(torch, rx, rx.lib, W, src, args, step_bytes, acc)
+    del src
     torch.cuda.synchronize()
     us = ms * 1e3
     res = {"us_per_step": round(us, 3), "tokens_per_s": round(W.T / (us * 1e-6), 1), "tokens": W.T,
@@ -701,7 +742,7 @@ def measure_workload(torch, rx, num: int, args):
            "steps_timed": steps, "setup_s": round(time.perf_counter() - t0, 1),
            "calls": "lora_route_linear_group (all modules in one shrink and one expand launch)" if grouped else
                     "lora_route_linear + lora_linear per further module",
-           "per_module_calls_us_per_step": per_module_us}
+           "per_module_calls_us_per_step": per_module_us, "fp8_pools": fp8}
     log(f"workload {W.name}: {us:.1f} us/step ({'grouped' if grouped else 'per module'}; per-module calls "
         f"{per_module_us} us/step), {res['step_hbm_gbps']} GB/s over the step "
         f"({100 * res['step_frac_of_peak']:.1f} % of 8 TB/s), kernels "
@@ -782,6 +823,11 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
+    if args.only_overlap:
+        res = measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
+        for inst in insts:
+            inst.close()
+        return {"only_overlap": res, "workload": W.name}
     ms_per_step, wall_us = time_steps(torch, step, args.steps)
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall_us:.2f} us/step)")
 
@@ -884,6 +930,8 @@ def main():
     ap.add_argument("--workloads", default="3,4,5",
                     help="further workloads timed after the headline one, reported under extra.workloads")
     ap.add_argument("--no-workloads", action="store_true", help="time the headline workload only")
+    ap.add_argument("--only-overlap", action="store_true",
+                    help="time only the base-GEMM overlap forms (for a kernel trace of them) and print their JSON")
     ap.add_argument("--per-module", action="store_true",
                     help="multi-module workloads: one fused call per module instead of one grouped call")
     ap.add_argument("--separate-routing", action="store_true",

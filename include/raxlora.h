@@ -68,8 +68,9 @@ typedef struct lora_routing lora_routing;
  * (the FP8 special case of the weight preparation, and "前向替换").  A pool of this
  * weight type takes bf16 activations x, which the kernels clamp to [-448, 448]
  * and round to e4m3 before use, as the page converts the input; products are exact
- * and accumulate in fp32; y is bf16 or fp32.  The weights are widened to bf16 in
- * registers (exact), so both the vector and the matrix-core paths serve them. */
+ * and accumulate in fp32; y is bf16 or fp32.  The matrix-core shrink runs on the FP8
+ * matrix cores (e4m3 x e4m3); the vector units and the expand widen the weights to
+ * bf16 in registers (exact). */
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1, LORA_FP8E4M3 = 2 } lora_dtype;
 
 typedef int lora_status;

@@ -40,10 +40,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ------------------------------------------------------------ float8 (e4m3)
-// OCP e4m3 ("fn"): every value is exactly a bfloat16 value, so FP8 operands are
-// widened to bf16 in registers and the bf16 arithmetic is reused.  The hardware
-// conversions round to nearest even (checked against the format definition on
-// every e4m3 byte and every bf16 value in [-448, 448]).
+// OCP e4m3 ("fn"): every value is exactly a bfloat16 value.  The matrix-core shrink
+// multiplies e4m3 operands on the FP8 matrix cores; the vector units and the expand
+// (whose other operand, u, is not an FP8 value) widen them to bf16 in registers and
+// reuse the bf16 arithmetic.  The hardware conversions round to nearest even (checked
+// against the format definition on every e4m3 byte and every bf16 value in
+// [-448, 448]).
 __device__ __forceinline__ uint32_t f32x2_hi_to_bf16x2(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);   // exact: the low halves are zero
 }
@@ -67,9 +69,9 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 w, float (&v)[8]) {
 constexpr float kFp8Max = 448.f;
 // clamp to [-448, 448] keeping NaN (a comparison with NaN is false), as torch's clamp does
 __device__ __forceinline__ float fp8_clamp(float v) { return v > kFp8Max ? kFp8Max : (v < -kFp8Max ? -kFp8Max : v); }
-// FP8 pools' input conversion of 8 bf16 activations: clamp to [-448, 448], round to
-// e4m3, back to bf16 (page "TensorRT-LLM 源码完全拆解(二十一)", section "前向替换")
-__device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
+// FP8 pools' input conversion of 8 bf16 activations (page "TensorRT-LLM 源码完全拆解
+// (二十一)", section "前向替换"): clamp to [-448, 448], round to e4m3; 8 bytes, in order
+__device__ __forceinline__ uint2 bf16x8_to_fp8x8(uint4 w) {
   float v[8];
   v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
   v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
@@ -81,8 +83,10 @@ __device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) {
   p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p0, true);
   int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
   p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], p1, true);
-  return fp8x8_to_bf16x8(make_uint2((uint32_t)p0, (uint32_t)p1));
+  return make_uint2((uint32_t)p0, (uint32_t)p1);
 }
+// the same conversion, back to bf16 (for the vector units, which multiply in bf16)
+__device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) { return fp8x8_to_bf16x8(bf16x8_to_fp8x8(w)); }
 
 // One lane's 8 consecutive weight values as a bf16 operand (dot products, MFMA
 // fragments): one 16-byte chunk for bf16 (and fp32: 4 values) pools; 8 bytes for
@@ -105,10 +109,6 @@ template <> struct WChunk<uint8_t> {
     return make_uint2(c.x & m, c.y & m);
   }
 };
-// x chunks of a shrink with weights TW: bf16 as given, put on the e4m3 grid for FP8 pools
-template <typename TW> __device__ __forceinline__ uint4 x_for(uint4 x) {
-  if constexpr (sizeof(TW) == 1) return bf16x8_to_fp8_grid(x); else return x;
-}
 
 // -------------------------------------------------------------- lane chunks
 // Every lane moves 16 bytes per load: 8 bf16 or 4 fp32 elements.

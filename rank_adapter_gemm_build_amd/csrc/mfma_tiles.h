@@ -44,6 +44,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ long as_i64(uint2 v) { return __builtin_bit_cast(long, v); }
 
 constexpr int kMfmaGroup = 4;                    // shrink k-steps whose fragments load together
 constexpr int kDsPitch = kMfmaCols + 4;          // LDS row pitch (floats) of the expand result tile
@@ -75,7 +76,11 @@ __device__ __forceinline__ void shrink_load_group(ShrinkFrags<TW, NB>& f, const 
 }
 
 // Products of one group; fragments of steps outside [sg, s1), of rows past the last
-// valid one and of tokens past the tile's length are zeroed here.
+// valid one and of tokens past the tile's length are zeroed here.  FP8 pools run on the
+// FP8 matrix cores (v_mfma_f32_16x16x32_fp8_fp8: the same 16x16x32 shape and lane
+// layout, 8 e4m3 bytes per lane and operand): the weights go in as stored and the
+// activations are converted once, to e4m3 bytes (clamped, rounded to nearest even);
+// the products of two e4m3 values are exact and accumulate in fp32.
 template <typename TW, int NB>
 __device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<TW, NB>& f, bool tval, const bool (&rval)[NB],
                                                  int sg, int s1, int k, int lk, f32x4_t (&acc)[NB]) {
@@ -83,11 +88,19 @@ __device__ __forceinline__ void shrink_mma_group(const ShrinkFrags<TW, NB>& f, b
 #pragma unroll
   for (int g = 0; g < kMfmaGroup; ++g) {
     const bool inb = sg + g < s1 && (sg + g) * kMfmaK + 8 * lk < k;  // k % 8 == 0: chunks wholly in or out
-    const uint4 xa = keep_if(x_for<TW>(f.xa[g]), tval && inb);
+    if constexpr (sizeof(TW) == 1) {
+      const uint2 xq = W::keep(bf16x8_to_fp8x8(f.xa[g]), tval && inb);
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(W::widen(W::keep(f.wb[g][b], rval[b]))),
-                                                       acc[b], 0, 0, 0);
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_i64(xq), as_i64(W::keep(f.wb[g][b], rval[b])), acc[b],
+                                                            0, 0, 0);
+    } else {
+      const uint4 xa = keep_if(f.xa[g], tval && inb);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(W::widen(W::keep(f.wb[g][b], rval[b]))),
+                                                         acc[b], 0, 0, 0);
+    }
   }
 }
 

@@ -1,4 +1,7 @@
-"""HBM traffic per launch from rocprofv3 counter runs (diagnostics, not the hot path).
+"""Summaries of rocprofv3 runs of bench.py for profiles/ (measurement tooling, not part
+of the library).
+
+HBM traffic per launch from rocprofv3 counter runs:
 
 Two runs of the same bench command with ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``
 give per-dispatch counter values in KiB.  The same bench run also launches a plain
@@ -10,9 +13,11 @@ so a later change to the kernels makes the entry stale (bench.py then reports
 ``traffic: null``).
 
 Usage:
-    python -m rank_adapter_gemm_build_amd.traffic WORKLOAD_NAME FETCH_CSV WRITE_CSV [COMMAND]
-    python -m rank_adapter_gemm_build_amd.traffic --stats STATS_CSV OUT_MD TITLE COMMAND
-(the second form writes a short markdown summary of a rocprofv3 --stats table)
+    python traffic.py WORKLOAD_NAME FETCH_CSV WRITE_CSV [COMMAND]
+    python traffic.py --stats STATS_CSV OUT_MD TITLE COMMAND
+    python traffic.py --overlap KERNEL_TRACE_CSV OUT_MD COMMAND
+(the second form writes a short markdown summary of a rocprofv3 --stats table; the
+third the per-step timeline of bench.py --only-overlap from a --kernel-trace run)
 """
 from __future__ import annotations
 
@@ -22,7 +27,7 @@ import os
 import re
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 512 * 2 ** 20
 
 
@@ -39,7 +44,7 @@ def _per_dispatch(path: str, counter: str):
 
 
 def _family(name: str):
-    m = re.search(r"rax::(shrink|expand|routing|finish_u)_kernel", name)
+    m = re.search(r"rax::(shrink|expand|routing|finish_u)(?:_group)?_kernel", name)
     return {"routing": "routing", "finish_u": "finish_u"}.get(m.group(1), m.group(1)) if m else None
 
 
@@ -87,9 +92,75 @@ def stats_markdown(stats_csv: str, out_md: str, title: str, command: str):
         f.write("\n".join(lines) + "\n")
 
 
+def _trace_rows(path: str):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            kind = ("gemm" if name.startswith("Cijk") or "gemm" in name.lower() else
+                    "shrink" if re.search(r"rax::shrink(_group)?_kernel", name) else
+                    "expand" if re.search(r"rax::expand(_group)?_kernel", name) else "other")
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind, r.get("Queue_Id", "?")))
+    rows.sort()
+    return rows
+
+
+def overlap_markdown(trace_csv: str, out_md: str, command: str, gap_ns: int = 1_000_000):
+    """The forms of bench.py --only-overlap (base GEMM alone; GEMM then LoRA on one stream;
+    GEMM and LoRA on two streams joined by an event, steps chained; the same with
+    independent steps), separated by idle gaps of more than 1 ms: per form and step,
+    when the GEMM, the shrink and the expand run, and the idle time between the GEMM's
+    end and the expand's start (the event wait)."""
+    rows = [r for r in _trace_rows(trace_csv) if r[2] != "other"]
+    phases, cur = [], []
+    for r in rows:
+        if cur and r[0] - max(c[1] for c in cur) > gap_ns:
+            phases.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        phases.append(cur)
+    names = ["base GEMM alone", "GEMM then LoRA, one stream", "GEMM beside LoRA, joined, chained steps",
+             "GEMM beside LoRA, joined, independent steps"]
+    lines = [f"# Base-GEMM overlap timeline, decode workload (64 tokens, 8 slots, k = d = 4096, r = 16)", "",
+             "Command (from the repository root; rocprofv3 writes the kernel trace named below):", "", "```",
+             command, "```", "",
+             "Per form: the last steps' mean durations and gaps from the kernel trace (start and end stamps of",
+             "each dispatch, in microseconds). 'wait' is the idle time from a GEMM's end to the start of the",
+             "expand that waits for it; 'shrink beside GEMM' is the part of the shrink that runs while the",
+             "GEMM runs.", "",
+             "| form | steps | us per step | GEMM us | shrink us | expand us | wait us | shrink beside GEMM us | queues |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for name, ph in zip(names, phases):
+        gem = [r for r in ph if r[2] == "gemm"]
+        shr = [r for r in ph if r[2] == "shrink"]
+        exp = [r for r in ph if r[2] == "expand"]
+        n = len(gem)
+        if n < 2:
+            continue
+        k = max(1, min(n, len(exp), 20) if exp else min(n, 20))
+        gem, shr, exp = gem[-k:], shr[-k:], exp[-k:]
+        per_step = (max(r[1] for r in ph[-3 * k:]) - min(r[0] for r in ph[-3 * k:])) / k / 1e3
+        dur = lambda rs: sum(r[1] - r[0] for r in rs) / len(rs) / 1e3 if rs else 0.0
+        waits, beside = [], []
+        for g, e in zip(gem, exp):
+            waits.append(max(0, e[0] - g[1]) / 1e3)
+        for g, s in zip(gem, shr):
+            beside.append(max(0, min(g[1], s[1]) - max(g[0], s[0])) / 1e3)
+        mean = lambda v: sum(v) / len(v) if v else 0.0
+        queues = sorted({r[3] for r in ph})
+        lines.append(f"| {name} | {k} | {per_step:.1f} | {dur(gem):.1f} | {dur(shr):.1f} | {dur(exp):.1f} | "
+                     f"{mean(waits):.1f} | {mean(beside):.1f} | {len(queues)} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 2 and argv[1] == "--stats":
         stats_markdown(argv[2], argv[3], argv[4], argv[5])
+        return 0
+    if len(argv) >= 2 and argv[1] == "--overlap":
+        overlap_markdown(argv[2], argv[3], argv[4])
         return 0
     if len(argv) < 4:
         print(__doc__)
