@@ -376,8 +376,6 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
         time.sleep(0.002)
         res["gemm_beside_lora_independent_steps_us_per_step"] = round(timed(overlap_free), 3)
         time.sleep(0.002)
-        if args.only_overlap:
-            return res
 
         # the two forms captured in HIP graphs of G2 chained steps each: serial (GEMM then
         # LoRA on one stream) and forked (each GEMM on a side stream that first waits for
@@ -386,7 +384,7 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
         G2 = min(16, M)
         fa = torch.cuda.Stream()
 
-        def capture(forked):
+        def capture(forked, lora=True):
             gr = torch.cuda.CUDAGraph()
             warm = torch.cuda.Stream()
             warm.wait_stream(torch.cuda.current_stream())
@@ -400,7 +398,9 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
                 cs = torch.cuda.current_stream()
                 for i in range(G2):
                     inst = insts[i]
-                    if forked:
+                    if not lora:
+                        gemm(inst)
+                    elif forked:
                         fa.wait_stream(cs)
                         with torch.cuda.stream(fa):
                             gemm(inst)
@@ -418,8 +418,10 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
             torch.cuda.synchronize()
             return gr
 
-        for key, forked in (("graph_gemm_then_lora_us_per_step", False), ("graph_gemm_beside_lora_us_per_step", True)):
-            gr = capture(forked)
+        for key, forked, lora in (("graph_base_gemm_us", False, False), ("graph_gemm_then_lora_us_per_step", False, True),
+                                  ("graph_gemm_beside_lora_us_per_step", True, True)):
+            time.sleep(0.002)
+            gr = capture(forked, lora)
             gr.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -431,7 +433,8 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
             torch.cuda.synchronize()
             res[key] = round(a.elapsed_time(b) * 1e3 / (reps * G2), 3)
             del gr
-        log(f"graphs of {G2} steps: GEMM then LoRA {res['graph_gemm_then_lora_us_per_step']:.2f} us/step, "
+        log(f"graphs of {G2} steps: base GEMM alone {res['graph_base_gemm_us']:.2f} us, "
+            f"GEMM then LoRA {res['graph_gemm_then_lora_us_per_step']:.2f} us/step, "
             f"GEMM beside LoRA {res['graph_gemm_beside_lora_us_per_step']:.2f} us/step")
         res["base_gemm"] = f"torch.mm [{T},{W0T.shape[0]}] x [{W0T.shape[0]},{W0T.shape[1]}] bf16, one W0 for all instances"
         log(f"base GEMM {res['base_gemm_us']:.2f} us; GEMM then LoRA {res['gemm_then_lora_us_per_step']:.2f} us/step; "

@@ -4,30 +4,35 @@
 // written once), so the probe offers two forms: a pure read of `read_bytes`, and a
 // read of `read_bytes` with one byte written for every `ratio` bytes read.
 //
-// Every lane moves 16 bytes per access, 8 accesses in flight per loop trip, over a
-// grid-stride loop; the read form folds what it reads into one word per thread
-// (written once at the end, so the loads cannot be dropped).
+// Every lane moves 16 bytes per access.  The read form gives each workgroup one
+// contiguous stretch of the buffer, read 16 accesses deep per lane (consecutive lanes
+// on consecutive 16-byte chunks), and folds what it reads into one word per thread
+// (written once at the end, so the loads cannot be dropped): measured on MI355X this
+// reads at about 6.1-6.2 TB/s, against 5.2-5.6 TB/s for a grid-stride loop over the
+// whole buffer.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
 
 namespace rax {
 
-constexpr int kProbeUnroll = 8;
+constexpr int kProbeUnroll = 16;
+constexpr int kProbeThreads = 256;
 
-__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, size_t n16,
-                                                         uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                                   uint32_t* __restrict__ sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = min((size_t)blockIdx.x * per, n16), b1 = min(b0 + per, n16);
   uint32_t acc = 0;
-  for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+  size_t i = b0 + threadIdx.x;
+  for (; i + (kProbeUnroll - 1) * kProbeThreads < b1; i += kProbeUnroll * kProbeThreads) {
     uint4 v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = src[i + u * kProbeThreads];
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += kProbeThreads) {
     const uint4 v = src[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -61,9 +66,10 @@ hipError_t launch_bandwidth_probe(const void* src, size_t read_bytes, void* dst,
     return hipErrorInvalidValue;
   const size_t n16 = read_bytes / 16;
   if (ratio <= 0) {
-    const int grid = probe_grid(n16 / kProbeUnroll);
+    // four workgroups per CU, each with a contiguous stretch (at least one full pass)
+    const int grid = (int)std::max<size_t>(1, std::min<size_t>(1024, n16 / (kProbeUnroll * kProbeThreads)));
     if ((size_t)grid * 256 * sizeof(uint32_t) > dst_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(src), n16,
+    hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kProbeThreads), 0, stream, static_cast<const uint4*>(src), n16,
                        static_cast<uint32_t*>(dst));
   } else {
     const size_t n_out = n16 / (size_t)ratio;

@@ -108,7 +108,8 @@ def _trace_rows(path: str):
 def overlap_markdown(trace_csv: str, out_md: str, command: str, gap_ns: int = 1_000_000):
     """The forms of bench.py --only-overlap (base GEMM alone; GEMM then LoRA on one stream;
     GEMM and LoRA on two streams joined by an event, steps chained; the same with
-    independent steps), separated by idle gaps of more than 1 ms: per form and step,
+    independent steps; then the GEMM alone, the serial step and the forked step captured
+    in HIP graphs), separated by idle gaps of more than 1 ms: per form and step,
     when the GEMM, the shrink and the expand run, and the idle time between the GEMM's
     end and the expand's start (the event wait)."""
     rows = [r for r in _trace_rows(trace_csv) if r[2] != "other"]
@@ -120,15 +121,22 @@ def overlap_markdown(trace_csv: str, out_md: str, command: str, gap_ns: int = 1_
         cur.append(r)
     if cur:
         phases.append(cur)
+    # the forms are the first four stretches with base GEMMs in them (earlier stretches are
+    # the set-up and the warm-up steps of the LoRA step alone)
+    phases = [ph for ph in phases if sum(1 for r in ph if r[2] == "gemm") >= 5]
+    # eager forms, then per graph its warm-up steps (eager, on a side stream) and its replays
+    phases = phases[:4] + phases[5::2][:3]
     names = ["base GEMM alone", "GEMM then LoRA, one stream", "GEMM beside LoRA, joined, chained steps",
-             "GEMM beside LoRA, joined, independent steps"]
+             "GEMM beside LoRA, joined, independent steps", "HIP graph: base GEMM alone",
+             "HIP graph: GEMM then LoRA, one stream", "HIP graph: GEMM on a forked stream, LoRA joined to it"]
     lines = [f"# Base-GEMM overlap timeline, decode workload (64 tokens, 8 slots, k = d = 4096, r = 16)", "",
              "Command (from the repository root; rocprofv3 writes the kernel trace named below):", "", "```",
              command, "```", "",
              "Per form: the last steps' mean durations and gaps from the kernel trace (start and end stamps of",
-             "each dispatch, in microseconds). 'wait' is the idle time from a GEMM's end to the start of the",
-             "expand that waits for it; 'shrink beside GEMM' is the part of the shrink that runs while the",
-             "GEMM runs.", "",
+             "each dispatch, in microseconds; the tracer itself lengthens every gap between kernels). 'us per",
+             "step' is the time from one base GEMM's start to the next; 'wait' is the time from a GEMM's end to",
+             "the start of the expand of the same step (on one stream the shrink runs in between); 'shrink",
+             "beside GEMM' is the part of the shrink that runs while the GEMM runs.", "",
              "| form | steps | us per step | GEMM us | shrink us | expand us | wait us | shrink beside GEMM us | queues |",
              "|---|---|---|---|---|---|---|---|---|"]
     for name, ph in zip(names, phases):
@@ -140,7 +148,8 @@ def overlap_markdown(trace_csv: str, out_md: str, command: str, gap_ns: int = 1_
             continue
         k = max(1, min(n, len(exp), 20) if exp else min(n, 20))
         gem, shr, exp = gem[-k:], shr[-k:], exp[-k:]
-        per_step = (max(r[1] for r in ph[-3 * k:]) - min(r[0] for r in ph[-3 * k:])) / k / 1e3
+        starts = [g[0] for g in gem]
+        per_step = (starts[-1] - starts[0]) / (len(starts) - 1) / 1e3   # GEMM start to the next GEMM start
         dur = lambda rs: sum(r[1] - r[0] for r in rs) / len(rs) / 1e3 if rs else 0.0
         waits, beside = [], []
         for g, e in zip(gem, exp):
