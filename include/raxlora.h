@@ -49,6 +49,11 @@
  *                             instead of four when (column groups of four x tile
  *                             slots) is at most this (default 512)
  *       RAXLORA_XCD_GROUP     consecutive decode units kept on one XCD (default 4)
+ *       RAXLORA_SLOT_MODE     0: never use the slot-major kernels (one unit per slot,
+ *                             weight loads issued before the routing data arrives);
+ *                             1: use them wherever the shape allows (T <= 256,
+ *                             in_features <= 32768, bf16 or FP8 weights); default:
+ *                             for 4 S <= T <= 128
  */
 #ifndef RAXLORA_H
 #define RAXLORA_H

@@ -219,6 +219,23 @@ void choose_split(lora_pool* p) {
   p->nsplit = ceil_div(chunks, p->ns);
 }
 
+// k split of the slot-major shrink (slot mode): workgroups of 1, 2, 4 or 8 waves, each
+// wave taking at most 8 matrix-core steps of 32 of its part; the fewest waves that
+// leave at most 8 parts (so the expand reads every value's partial sums in one batch;
+// k <= 16384), else 8 waves and at most kMaxSplit parts (k <= 32768).  slot_nsplit is
+// 0 when k is longer (no slot mode).
+constexpr int kSlotStepsPerWave = 8;
+int slot_waves(int k) {
+  const int steps = ceil_div(k, rax::kMfmaK);
+  for (int nw = 1; nw < 8; nw *= 2)
+    if (steps <= kSlotStepsPerWave * nw * 8) return nw;
+  return 8;
+}
+int slot_nsplit(int k) {
+  const int steps = ceil_div(k, rax::kMfmaK), per = kSlotStepsPerWave * slot_waves(k);
+  return steps <= per * rax::kMaxSplit ? ceil_div(steps, per) : 0;
+}
+
 
 // Common checks of shrink / expand / linear.
 lora_status check_pair(const lora_pool* pool, const lora_routing* routing) {
@@ -260,8 +277,33 @@ lora_status check_y(const lora_pool* pool, int T, const void* y, int ldy, lora_d
 struct CallSplit {
   int nsplit, ns;
 };
-CallSplit call_split(const lora_pool* p, const lora_routing* r) {
+bool use_mfma(const lora_pool* pool);
+
+// Slot mode (both kernels slot-major, every segment on the matrix cores; see the
+// slot-major shrink and expand units): for small decode batches in which most of the
+// pool's slots are active (4 S <= T <= 128), where a step is a chain of memory round
+// trips rather than a stream and the usual units' chain of routing lookups (tile
+// list, then token ids, then operands) dominates.  The units then issue their weight
+// fragments before any routing data has arrived; an inactive slot costs its units
+// those loads.  Measured on MI355X: the decode workload (T = 64, 8 slots) 12.2 -> 11.2
+// us per step; at T = 256 over 64 slots (three packed modules, grouped) slot mode is
+// slower (61 -> 73 us), so it stays off there.  RAXLORA_SLOT_MODE=0 turns it off, 1
+// uses it wherever the shape allows (T <= 256, k <= 32768, bf16 or FP8 weights).  A
+// grouped call uses it when every module would.
+bool slot_mode(const lora_pool* p, const lora_routing* r) {
+  const int env = env_int("RAXLORA_SLOT_MODE", -1);
+  if (env == 0 || p->embedding || !use_mfma(p) || r->T < 1 || r->T > rax::kSelfRouteTokens || slot_nsplit(p->k) == 0)
+    return false;
+  return env == 1 || (r->T >= 4 * r->S && r->T <= 128);
+}
+
+CallSplit call_split(const lora_pool* p, const lora_routing* r, bool slot) {
   CallSplit c{p->nsplit, p->ns};
+  if (slot) {
+    c.nsplit = slot_nsplit(p->k);
+    c.ns = ceil_div(ceil_div(p->k, chunk_width(p->wdtype)), c.nsplit);
+    return c;
+  }
   if (r->T >= 64 * std::max(1, r->S) && p->nsplit >= 2) {
     const int chunks = ceil_div(p->k, chunk_width(p->wdtype));
     c.ns = ceil_div(chunks, ceil_div(p->nsplit, 2));
@@ -292,13 +334,32 @@ bool use_mfma(const lora_pool* pool) {
 // (segments of at least mfma_min tokens go to the matrix cores when those are on),
 // and the matrix-core tile slots cover every tile a batch of T tokens can produce
 // (the kernels would loop over any excess).
-rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
+rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand, bool slot) {
   rax::Plan pl{};
-  const CallSplit cs = call_split(pool, r);
+  const CallSplit cs = call_split(pool, r, slot);
   pl.nsplit = cs.nsplit;
   pl.ns = cs.ns;
   pl.nrg = ceil_div(pool->N * pool->Rmax, 64);
   pl.xcd_group = std::max(1, std::min(64, env_int("RAXLORA_XCD_GROUP", 4)));
+  if (slot) {
+    // slot-major units: shrink (slot, k part, 16-row block), expand (slot, column
+    // group); one 128-column block per expand unit while that leaves at most
+    // RAXLORA_CB1_MAX units of four blocks
+    pl.slot_mode = 1;
+    pl.slot_waves = slot_waves(pool->k);
+    pl.use_mfma = 1;
+    pl.nrb = ceil_div(pool->N * pool->Rmax, 16);
+    pl.ntg = 1;
+    pl.tile_slots = 1;
+    int g4 = 0, g1 = 0;
+    for (int n = 0; n < pool->N; ++n) {
+      g4 += ceil_div(pool->mblk0[n + 1] - pool->mblk0[n], rax::kMfmaColBlocksPerUnit);
+      g1 += pool->mblk0[n + 1] - pool->mblk0[n];
+    }
+    pl.cb = (long long)g4 * pool->S <= env_int("RAXLORA_CB1_MAX", 512) ? 1 : rax::kMfmaColBlocksPerUnit;
+    pl.n_mgroups = pl.cb == 1 ? g1 : g4;
+    return pl;
+  }
   pl.use_mfma = use_mfma(pool) && r->T >= r->mfma_min ? 1 : 0;
   int mean = std::max(1, ceil_div(r->T, r->S));
   if (pl.use_mfma) mean = std::min(mean, r->mfma_min - 1);
@@ -325,8 +386,8 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand) {
 
 // self_ids: build the routing inside the launch from these ids (small batches)
 lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
-                       const rax::UView& U, hipStream_t stream, const int32_t* self_ids = nullptr) {
-  const rax::Plan pl = make_plan(pool, routing, false);
+                       const rax::UView& U, hipStream_t stream, bool slot, const int32_t* self_ids = nullptr) {
+  const rax::Plan pl = make_plan(pool, routing, false, slot);
   rax::SelfRoute sr{self_ids, route_out(routing)};
   hipError_t e = rax::launch_shrink(pool->wdtype, pool_view(pool), route_view(routing), x, ldx, U, pl,
                                     self_ids ? &sr : nullptr, stream, timer_for(rax::kKShrink));
@@ -335,8 +396,8 @@ lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const
 }
 
 lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const rax::UView& U,
-                       void* y, int ldy, lora_dtype ydtype, hipStream_t stream) {
-  const rax::Plan pl = make_plan(pool, routing, true);
+                       void* y, int ldy, lora_dtype ydtype, hipStream_t stream, bool slot) {
+  const rax::Plan pl = make_plan(pool, routing, true, slot);
   hipError_t e = rax::launch_expand(pool->wdtype, ydtype, pool_view(pool), slot_order(pool), route_view(routing), U,
                                     y, ldy, pl, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "expand launch");
@@ -349,14 +410,15 @@ lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const
 lora_status shrink_join_expand(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
                                void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready,
                                const int32_t* self_ids) {
-  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
-  lora_status st = run_shrink(pool, routing, x, ldx, W, stream, self_ids);
+  const bool slot = slot_mode(pool, routing);
+  const rax::UView W = workspace_view(pool, call_split(pool, routing, slot).nsplit);
+  lora_status st = run_shrink(pool, routing, x, ldx, W, stream, slot, self_ids);
   if (st != LORA_OK) return st;
   if (y_ready) {
     hipError_t e = hipStreamWaitEvent(stream, y_ready, 0);
     if (e != hipSuccess) return hip_fail(e, "waiting for y_ready");
   }
-  return run_expand(pool, routing, W, y, ldy, ydtype, stream);
+  return run_expand(pool, routing, W, y, ldy, ydtype, stream, slot);
 }
 
 lora_status linear_impl(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx, void* y,
@@ -439,6 +501,9 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
                        const int32_t* self_ids) {
   rax::GroupView G{};
   G.n = n;
+  // slot mode for the whole launch when every module would take it on its own
+  bool slot = true;
+  for (int m = 0; m < n; ++m) slot = slot && slot_mode(pools[m], routing);
   for (int m = 0; m < n; ++m) {
     rax::GroupEntry& e = G.e[m];
     e.P = pool_view(pools[m]);
@@ -446,15 +511,15 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
     e.ldx = ldx[m];
     e.y = y[m];
     e.ldy = ldy[m];
-    e.U = workspace_view(pools[m], call_split(pools[m], routing).nsplit);
-    e.plan = make_plan(pools[m], routing, false);
+    e.U = workspace_view(pools[m], call_split(pools[m], routing, slot).nsplit);
+    e.plan = make_plan(pools[m], routing, false, slot);
   }
   const rax::RouteView R = route_view(routing);
   rax::SelfRoute sr{self_ids, route_out(routing)};
   hipError_t e = rax::launch_shrink_group(pools[0]->wdtype, G, R, self_ids ? &sr : nullptr, stream,
                                           timer_for(rax::kKShrink));
   if (e != hipSuccess) return hip_fail(e, "grouped shrink launch");
-  for (int m = 0; m < n; ++m) G.e[m].plan = make_plan(pools[m], routing, true);
+  for (int m = 0; m < n; ++m) G.e[m].plan = make_plan(pools[m], routing, true, slot);
   e = rax::launch_expand_group(pools[0]->wdtype, ydtype, G, R, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "grouped expand launch");
   return LORA_OK;
@@ -568,7 +633,9 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   const size_t bk_bytes = (size_t)max_slots * p->Rk * p->D * p->esize;
   choose_split(p);
   if (embedding) p->nsplit = p->ns = 1;   // the gathered u is final: one part
-  const size_t ws_bytes = (size_t)p->nsplit * num_slices * max_tokens * p->Rk * sizeof(float);
+  // workspace parts: the most any call can use (the slot-major shrink may split finer)
+  const int ws_parts = embedding || wdtype == LORA_F32 ? p->nsplit : std::max(p->nsplit, slot_nsplit(in_features));
+  const size_t ws_bytes = (size_t)ws_parts * num_slices * max_tokens * p->Rk * sizeof(float);
   hipError_t e;
   if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
       (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
@@ -846,9 +913,10 @@ lora_status lora_shrink(const lora_pool* pool, const lora_routing* routing, cons
   DeviceGuard g(pool->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   // split partials into the workspace, then finished in split order into the caller's u
-  const rax::UView W = workspace_view(pool, call_split(pool, routing).nsplit);
-  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
-  const rax::Plan pl = make_plan(pool, routing, false);
+  const bool slot = slot_mode(pool, routing);
+  const rax::UView W = workspace_view(pool, call_split(pool, routing, slot).nsplit);
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream, slot)) != LORA_OK) return st;
+  const rax::Plan pl = make_plan(pool, routing, false, slot);
   hipError_t e = rax::launch_finish_u(pool_view(pool), route_view(routing), W, caller_u_view(pool, routing, u),
                                       pl, stream, timer_for(rax::kKFinish));
   if (e != hipSuccess) return hip_fail(e, "finish launch");
@@ -866,7 +934,7 @@ lora_status lora_expand(const lora_pool* pool, const lora_routing* routing, cons
   DeviceGuard g(pool->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   const rax::UView U = caller_u_view(pool, routing, const_cast<float*>(u));
-  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream, false)) != LORA_OK) return st;
   return ok();
 }
 
@@ -883,7 +951,8 @@ lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routi
   if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
   if (routing->T == 0) return ok();
   // the partials of this call: [nsplit][N][T][Rk] fp32, rows by sorted position
-  const CallSplit cs = call_split(pool, routing);
+  const bool slot = slot_mode(pool, routing);
+  const CallSplit cs = call_split(pool, routing, slot);
   const size_t need = (size_t)cs.nsplit * pool->N * routing->T * pool->Rk * sizeof(float);
   if (need > rax::kNoAllocScratchBytes)
     return fail(LORA_ERR_CAPACITY, "this call needs %zu bytes of scratch (%d k splits x %d slices x %d tokens x %d "
@@ -897,8 +966,8 @@ lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routi
   const long long rows = routing->T;
   const rax::UView W{static_cast<float*>(scratch), (long long)pool->N * rows * pool->Rk, rows * pool->Rk, pool->Rk,
                      cs.nsplit, 0};
-  if ((st = run_shrink(pool, routing, x, ldx, W, stream)) != LORA_OK) return st;
-  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  if ((st = run_shrink(pool, routing, x, ldx, W, stream, slot)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream, slot)) != LORA_OK) return st;
   return ok();
 }
 
@@ -969,7 +1038,7 @@ lora_status lora_embedding(const lora_pool* pool, const lora_routing* routing, c
   hipError_t e = rax::launch_embed_gather(pool->wdtype, pool_view(pool), route_view(routing), vocab_ids, pool->k, W,
                                           stream, timer_for(rax::kKGather));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
-  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream, false)) != LORA_OK) return st;
   return ok();
 }
 
@@ -1001,7 +1070,7 @@ lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, c
     if (fused) routing->T = -1;   // the routing was not built: unusable until rebuilt
     return hip_fail(e, "gather launch");
   }
-  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream)) != LORA_OK) return st;
+  if ((st = run_expand(pool, routing, U, y, ldy, ydtype, stream, false)) != LORA_OK) return st;
   return ok();
 }
 

@@ -115,6 +115,10 @@ struct Plan {
   int n_mgroups;           // matrix-core expand: column groups of cb blocks (per slice, summed)
   int use_mfma;            // long segments go to the matrix-core part
   int xcd_group;           // consecutive units dealt to one XCD (1 = plain round-robin)
+  int slot_mode;           // 1: slot-major units in both kernels (every segment on the matrix
+                           //    cores): shrink workgroups (slot, k part, 16-row block nrb) of
+                           //    slot_waves waves, expand units (slot, column group); no decode units
+  int slot_waves;          // slot mode: waves sharing one k part's steps (at most 8 steps each)
 };
 
 // One module of a grouped launch (several target modules of one batch, sharing its

@@ -35,6 +35,11 @@ size_t expand_smem_bytes(int wdtype, int Rmax, int use_mfma) {
 static int expand_ksm(const PoolView& P) { return P.Rk <= 32 ? 1 : P.Rk <= 64 ? 2 : P.Rk <= 128 ? 4 : 8; }
 
 static bool expand_shape_ok(int wdtype, const PoolView& P, const UView& U, const Plan& plan) {
+  if (plan.slot_mode)
+    return !(wdtype == LORA_F32 || !plan.use_mfma || plan.n_dec_blocks != 0 || plan.n_mgroups < 1 || U.nsplit < 1 ||
+             U.nsplit > kMaxSplit || (U.by_token && U.nsplit != 1) ||
+             (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
+             (plan.cb != 1 && plan.cb != kMfmaColBlocksPerUnit));
   return !(plan.xcd_group < 1 || plan.ntg < 1 || U.nsplit < 1 || U.nsplit > kMaxSplit ||
            (U.by_token && U.nsplit != 1) || (!U.by_token && (U.row_stride % 4 != 0 || U.row_stride < P.Rk)) ||
            plan.n_dec_blocks != P.n_ctiles * P.S * plan.ntg ||
@@ -44,7 +49,10 @@ static bool expand_shape_ok(int wdtype, const PoolView& P, const UView& U, const
 
 int expand_blocks(int wdtype, const PoolView& P, const Plan& plan, int& n_mfma_blocks) {
   (void)wdtype;
-  (void)P;
+  if (plan.slot_mode) {   // slot-major units only (XCD-aligned slot groups)
+    n_mfma_blocks = (P.S + kXcds - 1) / kXcds * kXcds * plan.n_mgroups;
+    return n_mfma_blocks;
+  }
   n_mfma_blocks = plan.use_mfma ? mfma_blocks(plan.n_mgroups * plan.tile_slots) : 0;
   const int q = kXcds * plan.xcd_group;
   return n_mfma_blocks + (plan.n_dec_blocks + q - 1) / q * q;
@@ -75,7 +83,8 @@ hipError_t launch_expand_group(int wdtype, int ydtype, const GroupView& G0, cons
   if (!group_layout(wdtype, G, R, nullptr, true, blocks)) return hipErrorInvalidValue;
   size_t lds = 0;
   for (int m = 0; m < G.n; ++m) {
-    if (!expand_shape_ok(wdtype, G.e[m].P, G.e[m].U, G.e[m].plan) || expand_ksm(G.e[m].P) != expand_ksm(G.e[0].P))
+    if (!expand_shape_ok(wdtype, G.e[m].P, G.e[m].U, G.e[m].plan) || expand_ksm(G.e[m].P) != expand_ksm(G.e[0].P) ||
+        G.e[m].plan.slot_mode != G.e[0].plan.slot_mode)
       return hipErrorInvalidValue;
     lds = std::max(lds, expand_smem_bytes(wdtype, G.e[m].P.Rmax, G.e[m].plan.use_mfma));
   }

@@ -180,6 +180,37 @@ __device__ __forceinline__ void expand_body(const PoolView& P, const RouteView& 
   }
 }
 
+// Slot mode: workgroup b of a module takes slot s = 8 (b / 8 / n_mgroups) + b % 8 (so
+// it shares an XCD with the slot's shrink items) and column group (b / 8) % n_mgroups.
+// Kernels of their own, so the register allocation of the tile-list kernels is not
+// affected by this body.
+template <typename TW, typename TY, int KSM>
+__device__ __forceinline__ void expand_slot_body(const PoolView& P, const RouteView& R, const UView& U,
+                                                 TY* __restrict__ y, int ldy, const Plan& plan, int b,
+                                                 float* __restrict__ smem) {
+  if constexpr (sizeof(TW) <= 2) {
+    const int per = plan.n_mgroups, q = b / kXcds;
+    const int s = (q / per) * kXcds + b % kXcds, g = q - (q / per) * per;
+    if (s < P.S) expand_slot_unit<TW, TY, KSM>(P, R, U, y, ldy, s, g, plan.cb, smem);
+  }
+}
+
+template <typename TW, typename TY, int KSM>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_slot_kernel(
+    PoolView P, RouteView R, UView U, TY* __restrict__ y, int ldy, Plan plan) {
+  extern __shared__ float smem[];
+  expand_slot_body<TW, TY, KSM>(P, R, U, y, ldy, plan, blockIdx.x, smem);
+}
+
+template <typename TW, typename TY, int KSM>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_slot_group_kernel(
+    GroupView G, RouteView R) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x;
+  const GroupEntry& e = G.e[group_module(G, b)];
+  expand_slot_body<TW, TY, KSM>(e.P, R, e.U, static_cast<TY*>(e.y), e.ldy, e.plan, b - e.blk0, smem);
+}
+
 template <typename TW, typename TY, int KSM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_kernel(PoolView P, SlotOrder O, RouteView R, UView U,
                                                     TY* __restrict__ y, int ldy, Plan plan, int n_mfma_blocks) {
@@ -203,6 +234,17 @@ template <typename TW, typename TY>
 static void launch_expand_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const PoolView& P,
                             const SlotOrder& O, const RouteView& R, const UView& U, TY* y, int ldy, const Plan& plan,
                             int nm, const KTimer& tm) {
+  if constexpr (sizeof(TW) <= 2) {
+    if (plan.slot_mode) {
+      switch (ksm) {
+        case 1: RAX_LAUNCH(tm, (expand_slot_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
+        case 2: RAX_LAUNCH(tm, (expand_slot_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
+        case 4: RAX_LAUNCH(tm, (expand_slot_kernel<TW, TY, 4>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
+        default: RAX_LAUNCH(tm, (expand_slot_kernel<TW, TY, 8>), grid, dim3(64), lds, stream, P, R, U, y, ldy, plan); break;
+      }
+      return;
+    }
+  }
   switch (ksm) {
     case 1: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, P, O, R, U, y, ldy, plan, nm); break;
     case 2: RAX_LAUNCH(tm, (expand_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, P, O, R, U, y, ldy, plan, nm); break;
@@ -214,6 +256,17 @@ static void launch_expand_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream
 template <typename TW, typename TY>
 static void launch_expand_group_w(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const GroupView& G,
                                   const RouteView& R, const KTimer& tm) {
+  if constexpr (sizeof(TW) <= 2) {
+    if (G.e[0].plan.slot_mode) {   // every module's plan takes the same mode
+      switch (ksm) {
+        case 1: RAX_LAUNCH(tm, (expand_slot_group_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, G, R); break;
+        case 2: RAX_LAUNCH(tm, (expand_slot_group_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, G, R); break;
+        case 4: RAX_LAUNCH(tm, (expand_slot_group_kernel<TW, TY, 4>), grid, dim3(64), lds, stream, G, R); break;
+        default: RAX_LAUNCH(tm, (expand_slot_group_kernel<TW, TY, 8>), grid, dim3(64), lds, stream, G, R); break;
+      }
+      return;
+    }
+  }
   switch (ksm) {
     case 1: RAX_LAUNCH(tm, (expand_group_kernel<TW, TY, 1>), grid, dim3(64), lds, stream, G, R); break;
     case 2: RAX_LAUNCH(tm, (expand_group_kernel<TW, TY, 2>), grid, dim3(64), lds, stream, G, R); break;

@@ -133,6 +133,159 @@ __device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const
   });
 }
 
+// LDS ints of a self-routing shrink workgroup
+constexpr int kShrinkSelfLds = route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64);
+static_assert(kShrinkSelfLds >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
+
+// ------------------------------------------------------------ slot-major shrink
+// Slot mode (small batches with most slots active): one workgroup per (slot s, k part,
+// 16-row block rb of the pool's N x Rmax rows), every segment length on the matrix
+// cores.  The part's k steps of 32 are split over the plan's slot_waves waves, at most
+// 8 steps each (so a wave's loads go out as one batch of 8 A and 8 x fragments); the
+// waves' products are added in wave order through LDS and written as the part's
+// partial sum, by sorted position, as the tile items write theirs (a part with no k
+// steps writes zeros).  Row f = 16 rb + lane % 16 is rank row f % Rmax of slice
+// f / Rmax (rows past a slot's rank are zero in A and masked), so a wave's A fragments
+// depend on nothing but the workgroup's index and go out first, in the same round trip
+// as the batch's ids (SELF: the first wave derives the slot's segment from them) or
+// the slot's routing record, and the slot-table entry.
+constexpr int kSlotSteps = 8;        // k steps of 32 per wave
+constexpr int kSlotMaxWaves = 8;     // waves per workgroup
+struct SlotShared {
+  float red[kSlotMaxWaves][kMfmaTileM][kMfmaTileM + 1];
+  int tok[kSelfRouteT];
+  int seg[2];
+};
+
+template <typename TW, bool SELF>
+__device__ __forceinline__ void shrink_slot_wg(const PoolView& P, const RouteView& R, const int32_t* __restrict__ ids,
+                                               const uint16_t* __restrict__ x, int ldx, const UView& U,
+                                               const Plan& plan, int b, SlotShared& sm) {
+  using W = WChunk<TW>;
+  const int per = plan.nsplit * plan.nrb, q = b / kXcds;
+  const int s = (q / per) * kXcds + b % kXcds, rest = q - (q / per) * per;
+  if (s >= P.S) return;   // whole workgroup
+  const int part = rest / plan.nrb, rb = rest - part * plan.nrb;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lk = lane >> 4;
+  const int nw = plan.slot_waves;   // waves past it (a grouped launch's wider workgroups) only join the barriers
+  const int F = P.N * P.Rmax, f = 16 * rb + lr;
+  const bool fv = f < F;
+  const int n = fv ? f / P.Rmax : 0, j = fv ? f - n * P.Rmax : 0;
+  int s0, s1;
+  mfma_part_range(P.k, part, U.nsplit, s0, s1);
+  const int spw = (s1 - s0 + nw - 1) / nw;               // <= kSlotSteps (the host's split)
+  const int w0 = w < nw ? min(s0 + w * spw, s1) : s1, w1 = min(w0 + spw, s1);
+  const int wlast = max(w1 - 1, w0);
+  const TW* __restrict__ arow = static_cast<const TW*>(P.A) + (((size_t)s * P.N + n) * P.Rmax + j) * P.k;
+  typename W::type af[kSlotSteps];
+#pragma unroll
+  for (int st = 0; st < kSlotSteps; ++st)
+    af[st] = W::load(arow + min(min(w0 + st, wlast) * kMfmaK + 8 * lk, P.k - 8));
+  const SlotEntry e = P.table[s];
+  int L, p0, tok0 = 0;
+  if constexpr (SELF) {
+    if (w == 0) {
+      BatchKeys K;
+      K.load(ids, R.T, R.S);
+      K.segment(s, L, p0, sm.tok);
+      if (lane == 0) { sm.seg[0] = L; sm.seg[1] = p0; }
+    }
+    __syncthreads();
+    L = __builtin_amdgcn_readfirstlane(sm.seg[0]);
+    p0 = __builtin_amdgcn_readfirstlane(sm.seg[1]);
+  } else {
+    // the record's header and its first token ids (entries past the segment repeat a
+    // valid token), so the first tile needs no further round trip
+    const int* __restrict__ rec = R.rec + (size_t)s * kRecInts;
+    const int2 hdr = *reinterpret_cast<const int2*>(rec);
+    tok0 = rec[4 + lr];
+    L = __builtin_amdgcn_readfirstlane(hdr.x);
+    p0 = __builtin_amdgcn_readfirstlane(hdr.y);
+  }
+  const int r = e.rank;
+  const bool row_ok = fv && j < r;
+  if (L == 0 || r == 0 || __ballot(row_ok) == 0ull) return;   // whole workgroup (same slot and rows)
+  for (int t0 = 0; t0 < L; t0 += kMfmaTileM) {
+    const int len = min(kMfmaTileM, L - t0), ti = t0 + min(lr, len - 1);
+    int tk;
+    if constexpr (SELF) tk = sm.tok[ti];
+    else tk = t0 == 0 ? tok0 : (ti < kRecTokens ? R.rec[(size_t)s * kRecInts + 4 + ti] : R.sorted[p0 + ti]);
+    const uint16_t* __restrict__ xrow = x + (size_t)tk * ldx;
+    uint4 xa[kSlotSteps];
+#pragma unroll
+    for (int st = 0; st < kSlotSteps; ++st) xa[st] = ld16(xrow + min(min(w0 + st, wlast) * kMfmaK + 8 * lk, P.k - 8));
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bool tval = lr < len;
+#pragma unroll
+    for (int st = 0; st < kSlotSteps; ++st) {
+      // steps past the wave's share, and this lane's chunk past k in the last step
+      // (k % 8 == 0: chunks are wholly in or out), contribute zero
+      const bool inb = w0 + st < w1 && (w0 + st) * kMfmaK + 8 * lk < P.k;
+      if constexpr (sizeof(TW) == 1) {
+        const uint2 xq = W::keep(bf16x8_to_fp8x8(xa[st]), tval && inb);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_i64(xq), as_i64(W::keep(af[st], row_ok)), acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(keep_if(xa[st], tval && inb)),
+                                                      as_bf16x8(W::keep(af[st], row_ok)), acc, 0, 0, 0);
+      }
+    }
+    // lane holds D[token 4 lk + i][row f]; the waves' sums added in wave order
+    if (w < nw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.red[w][4 * lk + i][lr] = acc[i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kMfmaTileM * kMfmaTileM; idx += blockDim.x) {   // (token, row) of the tile
+      const int t = idx >> 4, rr = idx & 15, fr = 16 * rb + rr;
+      const int nn = fr / P.Rmax, jj = fr - nn * P.Rmax;
+      if (t < len && fr < F && jj < r) {
+        float v = sm.red[0][t][rr];
+        for (int ww = 1; ww < nw; ++ww) v += sm.red[ww][t][rr];
+        U.p[part * U.split_stride + nn * U.n_stride + (long long)(p0 + t0 + t) * U.row_stride + jj] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename TW, bool SELF>
+__global__ __launch_bounds__(64 * kSlotMaxWaves) void shrink_slot_kernel(PoolView P, RouteView R,
+                                                                         const uint16_t* __restrict__ x, int ldx,
+                                                                         UView U, Plan plan, SelfRoute sr) {
+  __shared__ __align__(16) char smem[sizeof(SlotShared) > kShrinkSelfLds * sizeof(int) ? sizeof(SlotShared)
+                                                                                       : kShrinkSelfLds * sizeof(int)];
+  int b = blockIdx.x;
+  if constexpr (SELF) {
+    if (b < kXcds) {
+      if (b == 0 && threadIdx.x < 64)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out,
+                                                  reinterpret_cast<int*>(smem));
+      return;
+    }
+    b -= kXcds;
+  }
+  shrink_slot_wg<TW, SELF>(P, R, sr.ids, x, ldx, U, plan, b, *reinterpret_cast<SlotShared*>(smem));
+}
+
+template <typename TW, bool SELF>
+__global__ __launch_bounds__(64 * kSlotMaxWaves) void shrink_slot_group_kernel(GroupView G, RouteView R, SelfRoute sr) {
+  __shared__ __align__(16) char smem[sizeof(SlotShared) > kShrinkSelfLds * sizeof(int) ? sizeof(SlotShared)
+                                                                                       : kShrinkSelfLds * sizeof(int)];
+  int b = blockIdx.x;
+  if constexpr (SELF) {
+    if (b < kXcds) {
+      if (b == 0 && threadIdx.x < 64)
+        route_wave<kSelfRouteQ, kSelfRouteK / 64>(sr.ids, R.T, 1, R.S, R.mfma_min, R.tile_m, R.max_tiles, sr.out,
+                                                  reinterpret_cast<int*>(smem));
+      return;
+    }
+    b -= kXcds;
+  }
+  const GroupEntry& e = G.e[group_module(G, b)];
+  shrink_slot_wg<TW, SELF>(e.P, R, sr.ids, static_cast<const uint16_t*>(e.x), e.ldx, e.U, e.plan, b - e.blk0,
+                           *reinterpret_cast<SlotShared*>(smem));
+}
+
 // One module's shrink workgroup b (b counted from the module's first workgroup):
 // matrix-core (k part, tile, row group) items, then decode units.  SELF: the launch
 // also builds the routing (route_wave in its first workgroup), and the units take
@@ -208,9 +361,6 @@ __device__ __forceinline__ void shrink_body(const PoolView& P, const RouteView& 
   }
 }
 
-// LDS ints of a self-routing shrink workgroup
-constexpr int kShrinkSelfLds = route_wave_lds_ints(kSelfRouteQ, kSelfRouteK / 64);
-static_assert(kShrinkSelfLds >= kSelfRouteK + 2 * kSelfRouteT, "unit LDS");
 
 // One wave per workgroup.  SELF: workgroup 0 runs route_wave and workgroups 1-7 are
 // idle, so the others keep their XCD numbering.
@@ -258,7 +408,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sh
 
 int shrink_blocks(int wdtype, const PoolView& P, const Plan& plan, int& n_mfma_blocks) {
   (void)wdtype;
-  (void)P;
+  if (plan.slot_mode) {   // slot-major items only (XCD-aligned slot groups)
+    n_mfma_blocks = (P.S + kXcds - 1) / kXcds * kXcds * plan.nsplit * plan.nrb;
+    return n_mfma_blocks;
+  }
   n_mfma_blocks = plan.use_mfma ? mfma_blocks(plan.tile_slots * plan.nrg * plan.nsplit) : 0;
   const int q = kXcds * plan.xcd_group;
   return n_mfma_blocks + (plan.n_dec_blocks + q - 1) / q * q;
@@ -269,6 +422,18 @@ static void launch_shrink_t(const PoolView& P, const RouteView& R, const T* x, i
                             const Plan& plan, const SelfRoute* sr, hipStream_t stream, const KTimer& tm) {
   int nm;
   const int blocks = shrink_blocks(0, P, plan, nm);
+  if constexpr (sizeof(T) == 2 && sizeof(TW) <= 2) {
+    if (plan.slot_mode) {
+      const dim3 block(64 * plan.slot_waves);
+      if (sr)
+        RAX_LAUNCH(tm, (shrink_slot_kernel<TW, true>), dim3(kXcds + blocks), block, 0u, stream, P, R, x, ldx, U, plan,
+                   *sr);
+      else
+        RAX_LAUNCH(tm, (shrink_slot_kernel<TW, false>), dim3(blocks), block, 0u, stream, P, R, x, ldx, U, plan,
+                   SelfRoute{});
+      return;
+    }
+  }
   if (sr)
     RAX_LAUNCH(tm, (shrink_kernel<T, TW, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, P, R, x, ldx, U, plan, nm,
                *sr);
@@ -282,6 +447,16 @@ static bool shrink_shape_ok(int wdtype, const PoolView& P, const RouteView& R, c
                             const SelfRoute* sr) {
   const int cw = 64 * (wdtype == LORA_F32 ? 4 : 8);   // x is bf16 for FP8 pools
   const int chunks = (P.k + cw - 1) / cw;
+  if (plan.slot_mode) {
+    // every wave's share of its part fits its register-held A fragments
+    const int steps = (P.k + kMfmaK - 1) / kMfmaK;
+    const int per_part = (steps + plan.nsplit - 1) / std::max(plan.nsplit, 1);
+    return !(U.by_token || wdtype == LORA_F32 || !plan.use_mfma || U.nsplit != plan.nsplit || plan.nsplit < 1 ||
+             plan.nsplit > kMaxSplit || plan.slot_waves < 1 || plan.slot_waves > kSlotMaxWaves ||
+             (per_part + plan.slot_waves - 1) / plan.slot_waves > kSlotSteps || plan.n_dec_blocks != 0 ||
+             plan.nrb * kShrinkRows < P.N * P.Rmax || R.T > kSelfRouteT ||
+             (sr && (!sr->ids || R.T < 1 || R.S + 1 > kSelfRouteK)));
+  }
   return !(plan.xcd_group < 1 || U.by_token || U.nsplit != plan.nsplit || plan.nsplit < 1 || plan.nsplit > kMaxSplit ||
            plan.ns < 1 || plan.nsplit * plan.ns < chunks || plan.ntg < 1 || plan.nrb * kShrinkRows < P.N * P.Rmax ||
            plan.n_dec_blocks != P.S * plan.nrb * plan.nsplit * plan.ntg ||
@@ -325,6 +500,19 @@ bool group_layout(int wdtype, GroupView& G, const RouteView& R, const SelfRoute*
 template <typename T, typename TW>
 static void launch_shrink_group_t(const GroupView& G, int blocks, const RouteView& R, const SelfRoute* sr,
                                   hipStream_t stream, const KTimer& tm) {
+  if constexpr (sizeof(T) == 2 && sizeof(TW) <= 2) {
+    if (G.e[0].plan.slot_mode) {   // every module's plan takes the same mode
+      int nw = 1;
+      for (int m = 0; m < G.n; ++m) nw = std::max(nw, G.e[m].plan.slot_waves);
+      if (sr)
+        RAX_LAUNCH(tm, (shrink_slot_group_kernel<TW, true>), dim3(kXcds + blocks), dim3(64 * nw), 0u, stream, G, R,
+                   *sr);
+      else
+        RAX_LAUNCH(tm, (shrink_slot_group_kernel<TW, false>), dim3(blocks), dim3(64 * nw), 0u, stream, G, R,
+                   SelfRoute{});
+      return;
+    }
+  }
   if (sr)
     RAX_LAUNCH(tm, (shrink_group_kernel<T, TW, true>), dim3(kXcds + blocks), dim3(64), 0u, stream, G, R, *sr);
   else

@@ -462,7 +462,7 @@ struct ExpandBlockWidth {
 template <typename TW, typename TY, int NKS, int NSB, int CB>
 __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, TY* __restrict__ y, int ldy,
                                                  const TW* __restrict__ bk, int rs, int n, int on, int dn,
-                                                 int c00, int p0, int len, const int* __restrict__ tokp, int r,
+                                                 int c00, int p0, int len, const int* __restrict__ tokp, int tokv, int r,
                                                  int nks, float scale, float* __restrict__ ds) {
   constexpr int BC = ExpandBlockWidth<TW, TY, NKS>::value;
   constexpr int NB = CB * (kMfmaCols / BC);                     // blocks of the unit
@@ -475,7 +475,7 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
     // this lane's token id first, then the partials and the first block's B: loads
     // complete in order, so the y rows can be addressed (and their loads issued) as
     // soon as the token id is in, while the rest is still in flight
-    const int tok = *tokp;
+    const int tok = tokp ? *tokp : tokv;
     sched_fence();
     UPartials<NSB> up;
     up.load(U, n, p0, len, r, 0);
@@ -492,7 +492,7 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
       uq.finish(U, len, r, ks, uh[ks], ul[ks]);
     }
   } else {
-    Y.load(*tokp, y, ldy, on);
+    Y.load(tokp ? *tokp : tokv, y, ldy, on);
     b0.issue(Y, bk, rs, dn, c00, nks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) u_frag_by_token(R, U, n, p0, len, r, ks, uh[ks], ul[ks]);
@@ -548,25 +548,20 @@ struct LaneTable {
   }
 };
 
+// The body of one expand tile: `len` tokens at sorted position p0 of slot `slot` (table
+// entry e, rank > 0, slice n present), columns c00 .. of slice n; this lane's token id
+// (token lane % 16, clamped into the tile) at tokp, or tokv when tokp is null.
 template <typename TW, typename TY, int KSM>
-__device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
-                                                 TY* __restrict__ y, int ldy, int tile, int grp, int cb,
-                                                 const LaneTable& lt, float* __restrict__ ds) {
-  int blk0;
-  const int n = mfma_group_slice(P, grp, cb, blk0);
-  if (n < 0) return;
-  const int on = P.o[n], dn = P.d[n], c00 = blk0 * kMfmaCols;
-  const int4 td = R.tiles[tile];
-  const int slot = td.x, p0 = td.y, len = td.z;
-  const SlotEntry e = lt.get(P, slot);
-  // this lane's token id (token lane % 16): loaded by the body ahead of the partials
-  const int* __restrict__ tokp = R.sorted + p0 + min(lane_id() & 15, len - 1);
-  if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
+__device__ __forceinline__ void expand_mfma_tile(const PoolView& P, const RouteView& R, const UView& U,
+                                                 TY* __restrict__ y, int ldy, int slot, const SlotEntry& e, int n,
+                                                 int c00, int p0, int len, const int* __restrict__ tokp, int tokv,
+                                                 int cb, float* __restrict__ ds) {
+  const int on = P.o[n], dn = P.d[n];
   const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
   const TW* __restrict__ bk = static_cast<const TW*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
   const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
 #define RAX_EXPAND_BODY(NK, NB, CB) \
-  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tokp, r, nks, e.scale, ds)
+  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tokp, tokv, r, nks, e.scale, ds)
 #define RAX_EXPAND_BODIES(NK)                                                          \
   do {                                                                                 \
     if (cb == 1) {                                                                     \
@@ -587,6 +582,53 @@ __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteV
   }
 #undef RAX_EXPAND_BODIES
 #undef RAX_EXPAND_BODY
+}
+
+template <typename TW, typename TY, int KSM>
+__device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteView& R, const UView& U,
+                                                 TY* __restrict__ y, int ldy, int tile, int grp, int cb,
+                                                 const LaneTable& lt, float* __restrict__ ds) {
+  int blk0;
+  const int n = mfma_group_slice(P, grp, cb, blk0);
+  if (n < 0) return;
+  const int4 td = R.tiles[tile];
+  const int slot = td.x, p0 = td.y, len = td.z;
+  const SlotEntry e = lt.get(P, slot);
+  // this lane's token id (token lane % 16): loaded by the body ahead of the partials
+  const int* __restrict__ tokp = R.sorted + p0 + min(lane_id() & 15, len - 1);
+  if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
+  expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, slot, e, n, blk0 * kMfmaCols, p0, len, tokp, 0, cb, ds);
+}
+
+// Slot-mode expand unit: every tile of slot s's segment (any length) for column group
+// grp.  First round trip: the slot's routing record (segment length, first sorted
+// position, first token ids; entries past the segment repeat a valid token) and the
+// slot-table entry; the first tile's partials, B fragments and y rows then go out
+// together.  Tokens past the record's come from the sorted list.
+template <typename TW, typename TY, int KSM>
+__device__ __forceinline__ void expand_slot_unit(const PoolView& P, const RouteView& R, const UView& U,
+                                                 TY* __restrict__ y, int ldy, int s, int grp, int cb,
+                                                 float* __restrict__ ds) {
+  int blk0;
+  const int n = mfma_group_slice(P, grp, cb, blk0);
+  if (n < 0) return;
+  const int lr = lane_id() & 15;
+  const int* __restrict__ rec = R.rec + (size_t)s * kRecInts;
+  const int2 hdr = *reinterpret_cast<const int2*>(rec);
+  const int tok0 = rec[4 + lr];
+  const SlotEntry e = P.table[s];
+  const int L = __builtin_amdgcn_readfirstlane(hdr.x), p0 = __builtin_amdgcn_readfirstlane(hdr.y);
+  if (L == 0 || e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
+  for (int t0 = 0; t0 < L; t0 += kMfmaTileM) {
+    const int len = min(kMfmaTileM, L - t0), ti = t0 + min(lr, len - 1);
+    const int tk = t0 == 0 ? tok0 : (ti < kRecTokens ? rec[4 + ti] : R.sorted[p0 + ti]);
+    // values the tile body derives are recomputed per tile rather than held across
+    // the loop (an opaque copy of the slot's entry and indices)
+    SlotEntry ev = e;
+    int sv = s, nv = n, cv = blk0 * kMfmaCols;
+    asm volatile("" : "+s"(sv), "+s"(nv), "+s"(cv), "+s"(ev.rank), "+s"(ev.scale), "+s"(ev.slice_mask));
+    expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, sv, ev, nv, cv, p0 + t0, len, nullptr, tk, cb, ds);
+  }
 }
 
 }  // namespace rax

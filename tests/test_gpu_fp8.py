@@ -109,7 +109,7 @@ def test_fp8_registration_bit_exact(rx, premultiply, rslora):
     pool.close()
 
 
-@pytest.mark.parametrize("mode", ["default", "vector", "all-mfma"])
+@pytest.mark.parametrize("mode", ["default", "tiles", "slot", "vector", "all-mfma"])
 def test_fp8_exact_integer_case(rx, mode):
     """Small integers everywhere: every product and partial sum is exact in fp32, so
     the fp32 output equals the definition exactly, on the vector units, the matrix
@@ -117,7 +117,9 @@ def test_fp8_exact_integer_case(rx, mode):
     import os
     T, S, k, slices, Rmax = 70, 5, 512, [256, 64], 40
     ranks, A, B, ids, x, alpha = _case(11, T, S, k, slices, Rmax, integer=True)
-    env = {"vector": {"RAXLORA_DISABLE_MFMA": "1"}, "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}}.get(mode, {})
+    env = {"tiles": {"RAXLORA_SLOT_MODE": "0"}, "slot": {"RAXLORA_SLOT_MODE": "1"},
+           "vector": {"RAXLORA_DISABLE_MFMA": "1"},
+           "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_SLOT_MODE": "0"}}.get(mode, {})
     os.environ.update(env)
     try:
         pool = _pool(rx, S, Rmax, k, slices, T, ranks, A, B, alpha)

@@ -98,13 +98,15 @@ GROUP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["default", "all-mfma", "vector"])
+@pytest.mark.parametrize("mode", ["default", "tiles", "slot", "all-mfma", "vector"])
 @pytest.mark.parametrize("case", GROUP_CASES, ids=[f"seed{c[0]}" for c in GROUP_CASES])
 def test_group_matches_per_module_calls(rx, case, mode):
     seed, T, S, Rmax, dtype, mods, segments = case
     W = _group_case(seed, T, S, Rmax, dtype, mods, segments=segments)
     _log(f"group seed={seed} T={W.T} S={S} modules={[(m.k, m.slices) for m in W.modules]} {dtype} mode={mode}")
-    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}, "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
+    env = {"tiles": {"RAXLORA_SLOT_MODE": "0"}, "slot": {"RAXLORA_SLOT_MODE": "1"},
+           "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_SLOT_MODE": "0"},
+           "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
     os.environ.update(env)
     try:
         pools = [make_pool(rx, W, m) for m in W.modules]

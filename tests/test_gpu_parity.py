@@ -294,7 +294,9 @@ def test_shrink_and_expand_standalone(rx):
 
 
 def test_untouched_rows_and_columns(rx):
-    """No-LoRA rows, empty slots, zero-scale slots and missing slices stay bit-identical."""
+    """No-LoRA rows, empty slots, zero-scale slots and missing slices stay bit-identical
+    (the tile-list kernels; slot mode has the same test of its own)."""
+    import os
     import torch
     W = small_case(61, T=120, S=6, k=512, slices=[64, 128, 32], Rmax=8, invalid=4)
     mod = W.modules[0]
@@ -305,7 +307,11 @@ def test_untouched_rows_and_columns(rx):
     pool.register(4, a, b, W.alpha[4], W.ranks[4], adapter_scale=0.0)   # slot 4 unloaded by scale 0
     R, ids = make_routing(rx, W)
     y = to_device(mod.y_base, "bf16")
-    rx.linear(pool, R, to_device(mod.x, "bf16"), y)
+    os.environ["RAXLORA_SLOT_MODE"] = "0"
+    try:
+        rx.linear(pool, R, to_device(mod.x, "bf16"), y)
+    finally:
+        os.environ.pop("RAXLORA_SLOT_MODE", None)
     torch.cuda.synchronize()
     got, base = bits(y), mod.y_base
     keys = np.where((W.ids >= 0) & (W.ids < W.S), W.ids, W.S)
@@ -482,7 +488,7 @@ def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
         _log(f"  {mode}: normwise rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("mode", ["default", "all-mfma", "all-mfma-wide", "mfma16", "vector"])
+@pytest.mark.parametrize("mode", ["default", "tiles", "slot", "all-mfma", "all-mfma-wide", "mfma16", "vector"])
 def test_short_segments_every_path(rx, mode):
     """Segments of 1..17 tokens through each split between the vector and matrix-core
     units: the default threshold, every segment on the matrix cores (1-token tiles;
@@ -497,9 +503,10 @@ def test_short_segments_every_path(rx, mode):
     ads = oracle_adapters(W, mod)
     ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
                        max_rank=W.Rmax)
-    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "1000000000"},
-           "all-mfma-wide": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "0"},
-           "mfma16": {"RAXLORA_MFMA_MIN_SEG": "16"},
+    env = {"tiles": {"RAXLORA_SLOT_MODE": "0"}, "slot": {"RAXLORA_SLOT_MODE": "1"},
+           "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "1000000000", "RAXLORA_SLOT_MODE": "0"},
+           "all-mfma-wide": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_CB1_MAX": "0", "RAXLORA_SLOT_MODE": "0"},
+           "mfma16": {"RAXLORA_MFMA_MIN_SEG": "16", "RAXLORA_SLOT_MODE": "0"},
            "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
     os.environ.update(env)
     try:
@@ -512,7 +519,7 @@ def test_short_segments_every_path(rx, mode):
 
 
 @pytest.mark.parametrize("Rmax", [96, 128, 256])
-@pytest.mark.parametrize("mode", ["mfma", "vector"])
+@pytest.mark.parametrize("mode", ["mfma", "slot", "vector"])
 def test_high_rank_pools(rx, Rmax, mode):
     """Pools whose padded rank needs 3-8 matrix-core rank steps (the expand's general
     body) and several B^T row batches on the vector units; ranks mixed up to Rmax,
@@ -526,12 +533,14 @@ def test_high_rank_pools(rx, Rmax, mode):
     ads = oracle_adapters(W, mod)
     ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), ads, slices, W.ids, W.S, "bf16",
                        max_rank=Rmax)
-    if mode == "vector":
-        os.environ["RAXLORA_DISABLE_MFMA"] = "1"
+    env = {"vector": {"RAXLORA_DISABLE_MFMA": "1"}, "mfma": {"RAXLORA_SLOT_MODE": "0"},
+           "slot": {"RAXLORA_SLOT_MODE": "1"}}[mode]
+    os.environ.update(env)
     try:
         y = _run_linear(rx, W, mod, np.zeros((W.T, sum(slices)), dtype=np.float32), "f32")
     finally:
-        os.environ.pop("RAXLORA_DISABLE_MFMA", None)
+        for key in env:
+            os.environ.pop(key, None)
     err = check_close(from_device(y), ref, "bf16", f"delta (Rmax={Rmax}, {mode})")
     _log(f"  normwise rel err {err:.2e}")
 

@@ -74,14 +74,16 @@ def _fused(rx, W, mod, y0, ydt):
     return y, q
 
 
-@pytest.mark.parametrize("mode", ["default", "all-mfma", "vector"])
+@pytest.mark.parametrize("mode", ["default", "tiles", "slot", "all-mfma", "vector"])
 @pytest.mark.parametrize("case", CASES, ids=[f"seed{c[0]}" for c in CASES])
 def test_route_linear_matches_two_calls(rx, case, mode):
     seed, T, S, k, slices, Rmax, dtype, invalid, segments = case
     W = small_case(seed, T=T, S=S, k=k, slices=slices, Rmax=Rmax, dtype=dtype, invalid=invalid, segments=segments)
     mod = W.modules[0]
     _log(f"route_linear seed={seed} T={W.T} S={S} slices={slices} Rmax={Rmax} {dtype} mode={mode}")
-    env = {"all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1"}, "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
+    env = {"tiles": {"RAXLORA_SLOT_MODE": "0"}, "slot": {"RAXLORA_SLOT_MODE": "1"},
+           "all-mfma": {"RAXLORA_MFMA_MIN_SEG": "1", "RAXLORA_SLOT_MODE": "0"},
+           "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
     os.environ.update(env)
     try:
         D = sum(slices)
