@@ -422,8 +422,10 @@ def measure_overlap(torch, rx, lib, insts, src, W, ydt, args, step_on, res):
                                   ("graph_gemm_beside_lora_us_per_step", True, True)):
             time.sleep(0.002)
             gr = capture(forked, lora)
+            time.sleep(0.002)   # gaps around the first replay keep a kernel trace's phases apart
             gr.replay()
             torch.cuda.synchronize()
+            time.sleep(0.002)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = max(2, n // G2)
             a.record()

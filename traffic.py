@@ -44,7 +44,7 @@ def _per_dispatch(path: str, counter: str):
 
 
 def _family(name: str):
-    m = re.search(r"rax::(shrink|expand|routing|finish_u)(?:_group)?_kernel", name)
+    m = re.search(r"rax::(shrink|expand|routing|finish_u)(?:_slot)?(?:_group)?_kernel", name)
     return {"routing": "routing", "finish_u": "finish_u"}.get(m.group(1), m.group(1)) if m else None
 
 
@@ -98,8 +98,8 @@ def _trace_rows(path: str):
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
             kind = ("gemm" if name.startswith("Cijk") or "gemm" in name.lower() else
-                    "shrink" if re.search(r"rax::shrink(_group)?_kernel", name) else
-                    "expand" if re.search(r"rax::expand(_group)?_kernel", name) else "other")
+                    "shrink" if re.search(r"rax::shrink(_slot)?(_group)?_kernel", name) else
+                    "expand" if re.search(r"rax::expand(_slot)?(_group)?_kernel", name) else "other")
             rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind, r.get("Queue_Id", "?")))
     rows.sort()
     return rows
@@ -124,8 +124,9 @@ def overlap_markdown(trace_csv: str, out_md: str, command: str, gap_ns: int = 1_
     # the forms are the first four stretches with base GEMMs in them (earlier stretches are
     # the set-up and the warm-up steps of the LoRA step alone)
     phases = [ph for ph in phases if sum(1 for r in ph if r[2] == "gemm") >= 5]
-    # eager forms, then per graph its warm-up steps (eager, on a side stream) and its replays
-    phases = phases[:4] + phases[5::2][:3]
+    # eager forms, then per graph three stretches: its warm-up steps (eager, on a side
+    # stream), its first replay and the timed replays
+    phases = phases[:4] + phases[6::3][:3]
     names = ["base GEMM alone", "GEMM then LoRA, one stream", "GEMM beside LoRA, joined, chained steps",
              "GEMM beside LoRA, joined, independent steps", "HIP graph: base GEMM alone",
              "HIP graph: GEMM then LoRA, one stream", "HIP graph: GEMM on a forked stream, LoRA joined to it"]
