@@ -49,6 +49,8 @@
  *                             instead of four when (column groups of four x tile
  *                             slots) is at most this (default 512)
  *       RAXLORA_XCD_GROUP     consecutive decode units kept on one XCD (default 4)
+ *       RAXLORA_LOG           1: one line on stderr per shrink or expand launch with
+ *                             the launch shape chosen (path, k split, waves, units)
  *       RAXLORA_SLOT_MODE     0: never use the slot-major kernels (one unit per slot,
  *                             weight loads issued before the routing data arrives);
  *                             1: use them wherever the shape allows (T <= 256,

@@ -149,6 +149,21 @@ int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
+// RAXLORA_LOG=1: one line on stderr per launch of the LoRA kernels, with the launch
+// shape the plan chose (read once per process; for diagnosing which path a call takes)
+bool log_on() {
+  static const bool on = env_int("RAXLORA_LOG", 0) != 0;
+  return on;
+}
+void log_plan(const char* what, const lora_pool* p, const lora_routing* r, const rax::Plan& pl, int modules) {
+  if (!log_on()) return;
+  std::fprintf(stderr,
+               "raxlora: %s T=%d S=%d k=%d N=%d D=%d Rmax=%d modules=%d mode=%s nsplit=%d waves=%d use_mfma=%d "
+               "tile_slots=%d cb=%d n_dec=%d\n",
+               what, r->T, r->S, p->k, p->N, p->D, p->Rmax, modules, pl.slot_mode ? "slot" : "tiles", pl.nsplit,
+               pl.slot_mode ? pl.slot_waves : 1, pl.use_mfma, pl.tile_slots, pl.cb, pl.n_dec_blocks);
+}
+
 rax::PoolView pool_view(const lora_pool* p) {
   rax::PoolView v{};
   v.A = p->A;
@@ -386,6 +401,7 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand, b
 lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx,
                        const rax::UView& U, hipStream_t stream, bool slot, const int32_t* self_ids = nullptr) {
   const rax::Plan pl = make_plan(pool, routing, false, slot);
+  log_plan(self_ids ? "shrink (routing inside)" : "shrink", pool, routing, pl, 1);
   rax::SelfRoute sr{self_ids, route_out(routing)};
   hipError_t e = rax::launch_shrink(pool->wdtype, pool_view(pool), route_view(routing), x, ldx, U, pl,
                                     self_ids ? &sr : nullptr, stream, timer_for(rax::kKShrink));
@@ -396,6 +412,7 @@ lora_status run_shrink(const lora_pool* pool, const lora_routing* routing, const
 lora_status run_expand(const lora_pool* pool, const lora_routing* routing, const rax::UView& U,
                        void* y, int ldy, lora_dtype ydtype, hipStream_t stream, bool slot) {
   const rax::Plan pl = make_plan(pool, routing, true, slot);
+  log_plan(U.by_token ? "expand (u by token)" : "expand", pool, routing, pl, 1);
   hipError_t e = rax::launch_expand(pool->wdtype, ydtype, pool_view(pool), slot_order(pool), route_view(routing), U,
                                     y, ldy, pl, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "expand launch");
@@ -514,10 +531,13 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
   }
   const rax::RouteView R = route_view(routing);
   rax::SelfRoute sr{self_ids, route_out(routing)};
+  log_plan(self_ids ? "grouped shrink (routing inside), first module" : "grouped shrink, first module", pools[0],
+           routing, G.e[0].plan, n);
   hipError_t e = rax::launch_shrink_group(pools[0]->wdtype, G, R, self_ids ? &sr : nullptr, stream,
                                           timer_for(rax::kKShrink));
   if (e != hipSuccess) return hip_fail(e, "grouped shrink launch");
   for (int m = 0; m < n; ++m) G.e[m].plan = make_plan(pools[m], routing, true, slot);
+  log_plan("grouped expand, first module", pools[0], routing, G.e[0].plan, n);
   e = rax::launch_expand_group(pools[0]->wdtype, ydtype, G, R, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "grouped expand launch");
   return LORA_OK;

@@ -138,6 +138,15 @@ int main() {
   EXPECT(lora_routing_create(&r8, 0, 64, 8), LORA_OK);
   std::vector<int32_t> ids8(64, 3);
   EXPECT(lora_route_embedding(emb, r8, ids8.data(), 64, vocab.data(), y.data(), 4096, LORA_BF16, nullptr), LORA_OK);
+  // a decode batch over few slots: the slot-major kernels (64 tokens, 8 slots)
+  lora_pool* small = nullptr;
+  EXPECT(lora_pool_create(&small, 0, 8, 16, 4096, slices_down, 1, LORA_BF16, 64), LORA_OK);
+  for (int slot = 0; slot < 8; ++slot)
+    EXPECT(lora_register_adapter(small, slot, a3, b3, 32.f, 16, 0, 1.f, 0u, nullptr), LORA_OK);
+  EXPECT(lora_linear(small, r8, x.data(), 4096, y.data(), 4096, LORA_BF16, nullptr), LORA_OK);
+  EXPECT(lora_route_linear(small, r8, ids8.data(), 64, x.data(), 4096, y.data(), 4096, LORA_BF16, nullptr), LORA_OK);
+  EXPECT(lora_linear_noalloc(small, r8, x.data(), 4096, y.data(), 4096, LORA_BF16, nullptr), LORA_OK);
+  EXPECT(lora_pool_destroy(small), LORA_OK);
   EXPECT(lora_embedding(emb, r8, vocab.data(), y.data(), 4096, LORA_BF16, nullptr), LORA_OK);
   EXPECT(lora_linear(emb, r8, x.data(), 32000, y.data(), 4096, LORA_BF16, nullptr), LORA_ERR_INVALID_ARG);
 

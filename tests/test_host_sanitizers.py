@@ -24,7 +24,12 @@ def test_abi_host_code_under_asan_ubsan(tmp_path):
            os.path.join(HERE, "driver.cpp"), "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1",
+               RAXLORA_LOG="1")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-6000:])
     assert "0 failures" in r.stdout
+    # RAXLORA_LOG: one line per launch, naming the path the plan chose
+    log = [l for l in r.stderr.splitlines() if l.startswith("raxlora: ")]
+    assert any("mode=slot" in l for l in log) and any("mode=tiles" in l for l in log), r.stderr[-2000:]
+    assert any(l.startswith("raxlora: grouped shrink") for l in log)
