@@ -194,17 +194,15 @@ lora_status lora_unregister_adapter(lora_pool* pool, int slot, hipStream_t strea
 
 /* Host mirror of a slot's table entry (synchronous, no device access): rank,
  * scale still applied after the branch (1 when pre-multiplied), mask of present
- * slices, and the byte offsets of the slot's A block and of its B block from the
- * base of each (the pool stores B once, rank-contiguous per output column: column c
- * at c * (rank rounded up to 8) within the slot's block).  Any out pointer may be
- * NULL. */
+ * slices, and the byte offsets of the slot's A and rank-major B blocks from the
+ * pool base.  Any out pointer may be NULL. */
 lora_status lora_pool_slot_info(const lora_pool* pool, int slot, int* rank, float* scale,
                                 uint32_t* slice_mask, uint64_t* a_offset, uint64_t* bt_offset);
 
 /* Copy a slot's stored slice back to host memory (synchronous; for tests):
  * A_host [max_lora_rank, in_features] (embedding pools: [vocab, max_lora_rank])
- * and Bt_host [max_lora_rank, slice_out[slice]] (the stored B transposed to
- * rank-major rows on the host), both in the pool dtype, rows >= rank zero.
+ * and Bt_host [max_lora_rank, slice_out[slice]]
+ * (B transposed, rank-major), both in the pool dtype, rows >= rank zero.
  * Either pointer may be NULL. */
 lora_status lora_pool_read_slot(const lora_pool* pool, int slot, int slice, void* A_host,
                                 void* Bt_host);

@@ -28,7 +28,8 @@ struct lora_pool {
   size_t esize = 2;
   bool embedding = false;     // A stored [S][V][Rmax] (rows by vocabulary id); k = V
   void* A = nullptr;
-  void* Bk = nullptr;         // B, rank-contiguous per column (the one copy of B)
+  void* Bt = nullptr;
+  void* Bk = nullptr;
   SlotEntry* table = nullptr;
   float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rk] by sorted position
   int nsplit = 1, ns = 1;     // decode shrink: k splits, chunk steps per split (fixed by k)
@@ -37,7 +38,7 @@ struct lora_pool {
 };
 
 namespace {
-// Decode expand units of a high-rank slot run longest (one batch of B per 16 ranks),
+// Decode expand units of a high-rank slot run longest (one B^T batch per 16 ranks),
 // so they are dispatched first: slots sorted by descending rank, ties by index.
 void update_order(lora_pool* p) {
   if (p->S > rax::kMaxOrderedSlots) return;
@@ -167,6 +168,7 @@ void log_plan(const char* what, const lora_pool* p, const lora_routing* r, const
 rax::PoolView pool_view(const lora_pool* p) {
   rax::PoolView v{};
   v.A = p->A;
+  v.Bt = p->Bt;
   v.Bk = p->Bk;
   v.table = p->table;
   v.S = p->S;
@@ -647,6 +649,7 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   update_order(p);
 
   const size_t a_bytes = (size_t)max_slots * num_slices * max_lora_rank * in_features * p->esize;
+  const size_t b_bytes = (size_t)max_slots * max_lora_rank * p->D * p->esize;
   const size_t bk_bytes = (size_t)max_slots * p->Rk * p->D * p->esize;
   choose_split(p);
   if (embedding) p->nsplit = p->ns = 1;   // the gathered u is final: one part
@@ -654,14 +657,16 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   const int ws_parts = embedding || wdtype == LORA_F32 ? p->nsplit : std::max(p->nsplit, slot_nsplit(in_features));
   const size_t ws_bytes = (size_t)ws_parts * num_slices * max_tokens * p->Rk * sizeof(float);
   hipError_t e;
-  if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
+  if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
+      (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
       (e = hipMalloc((void**)&p->table, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
       (e = hipMalloc((void**)&p->ws, ws_bytes)) != hipSuccess) {
     lora_pool_destroy(p);
     return hip_fail(e, "pool allocation");
   }
   // empty slots read as rank 0; weights start at zero so padding rows are inert
-  if ((e = hipMemset(p->A, 0, a_bytes)) != hipSuccess || (e = hipMemset(p->Bk, 0, bk_bytes)) != hipSuccess ||
+  if ((e = hipMemset(p->A, 0, a_bytes)) != hipSuccess || (e = hipMemset(p->Bt, 0, b_bytes)) != hipSuccess ||
+      (e = hipMemset(p->Bk, 0, bk_bytes)) != hipSuccess ||
       (e = hipMemset(p->table, 0, (size_t)max_slots * sizeof(SlotEntry))) != hipSuccess ||
       (e = hipDeviceSynchronize()) != hipSuccess) {
     lora_pool_destroy(p);
@@ -688,6 +693,7 @@ lora_status lora_pool_destroy(lora_pool* p) {
   if (!p) return ok();
   DeviceGuard g(p->device);
   if (p->A) (void)hipFree(p->A);
+  if (p->Bt) (void)hipFree(p->Bt);
   if (p->Bk) (void)hipFree(p->Bk);
   if (p->table) (void)hipFree(p->table);
   if (p->ws) (void)hipFree(p->ws);
@@ -744,9 +750,10 @@ lora_status lora_register_adapter(lora_pool* pool, int slot, const void* const* 
       b_src = db;
     }
     char* A_dst = static_cast<char*>(pool->A) + (((size_t)slot * pool->N + n) * pool->Rmax) * pool->k * es;
+    char* Bt_dst = static_cast<char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[n]) * es;
     char* Bk_dst = static_cast<char*>(pool->Bk) +
                    ((size_t)slot * pool->D * pool->Rk + (size_t)pool->o[n] * rax::bk_stride(rank)) * es;
-    e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bk_dst, rank, pool->Rmax,
+    e = rax::launch_pack_slice(pool->wdtype, a_src, b_src, A_dst, Bt_dst, Bk_dst, rank, pool->Rmax,
                                pool->Rk, pool->k, pool->d[n], pool->D, s, premul ? 1 : 0, pool->embedding ? 1 : 0,
                                stream);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "pack launch"); }
@@ -785,7 +792,7 @@ lora_status lora_pool_slot_info(const lora_pool* pool, int slot, int* rank, floa
   if (scale) *scale = e.scale;
   if (slice_mask) *slice_mask = e.slice_mask;
   if (a_offset) *a_offset = (uint64_t)slot * pool->N * pool->Rmax * pool->k * pool->esize;
-  if (bt_offset) *bt_offset = (uint64_t)slot * pool->D * pool->Rk * pool->esize;
+  if (bt_offset) *bt_offset = (uint64_t)slot * pool->Rmax * pool->D * pool->esize;
   return ok();
 }
 
@@ -804,19 +811,10 @@ lora_status lora_pool_read_slot(const lora_pool* pool, int slot, int slice, void
       return hip_fail(e, "copy A");
   }
   if (Bt_host) {
-    // the slice's columns from the rank-contiguous layout (column c at c * rs), written
-    // out rank-major [Rmax][d] with rows >= rank zero
-    const int r = pool->mirror[slot].rank, rs = rax::bk_stride(r), d = pool->d[slice];
-    std::vector<char> cols((size_t)d * rs * es);
-    const char* src =
-        static_cast<const char*>(pool->Bk) + ((size_t)slot * pool->D * pool->Rk + (size_t)pool->o[slice] * rs) * es;
-    if (!cols.empty() && (e = hipMemcpy(cols.data(), src, cols.size(), hipMemcpyDeviceToHost)) != hipSuccess)
-      return hip_fail(e, "copy B");
-    char* dst = static_cast<char*>(Bt_host);
-    std::memset(dst, 0, (size_t)pool->Rmax * d * es);
-    for (int j = 0; j < r; ++j)
-      for (int c = 0; c < d; ++c)
-        std::memcpy(dst + ((size_t)j * d + c) * es, cols.data() + ((size_t)c * rs + j) * es, es);
+    const char* src = static_cast<const char*>(pool->Bt) + ((size_t)slot * pool->Rmax * pool->D + pool->o[slice]) * es;
+    if ((e = hipMemcpy2D(Bt_host, (size_t)pool->d[slice] * es, src, (size_t)pool->D * es,
+                         (size_t)pool->d[slice] * es, pool->Rmax, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "copy Bt");
   }
   return ok();
 }

@@ -2,12 +2,13 @@
 //
 // Device data layout of one pool (one target module with N output slices):
 //   A   [S][N][Rmax][k]     shrink weights as given (rows j >= rank are zero)
-//   Bk  [S][D * Rk]         expand weights with the rank contiguous (B as given), the
-//                           one copy of B both expand paths read: slot s's region of
+//   Bt  [S][Rmax][D]        expand weights, B transposed to rank-major rows; slice n
+//                           occupies columns [o_n, o_n + d_n) of every rank row
+//   Bk  [S][D * Rk]         expand weights with the rank contiguous (B as given),
+//                           the matrix-core operand layout: slot s's region of
 //                           D * Rk elements (Rk = Rmax rounded up to 32) holds
 //                           column c at offset c * bk_stride(rank), the slot's rank
-//                           rounded up to 8 (entries past the rank zero); slice n
-//                           holds columns [o_n, o_n + d_n)
+//                           rounded up to 8 (entries past the rank zero)
 //   table [S]               rank, scale, present-slice mask per slot
 // Slots are addressed by fixed strides, so no pointer table is needed: the
 // address of slot s is base + s * stride, formed in 64-bit arithmetic.
@@ -54,6 +55,7 @@ enum MetaIndex { kMetaT = 0, kMetaActive = 1, kMetaInvalid = 2, kMetaLora = 3, k
 
 struct PoolView {
   const void* A;
+  const void* Bt;
   const void* Bk;
   const SlotEntry* table;
   int S, Rmax, Rk, k, N, D, n_ctiles, n_mblocks;
@@ -157,7 +159,7 @@ hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_mi
                           int* rec, int* meta, hipStream_t stream, const KTimer& tm);
 // a_by_row: store A transposed, [k][Rmax] (embedding pools: k = vocabulary size)
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
-                             void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
+                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
                              int D, float scale, int premultiply, int a_by_row, hipStream_t stream);
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry entry, hipStream_t stream);
 // Output buffers of a routing (device memory; sizes as in RouteView).

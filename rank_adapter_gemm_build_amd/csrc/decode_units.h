@@ -10,13 +10,12 @@
 // token l % 4) for split s.  Splits are added in split order by their single
 // reader, so results do not depend on timing.
 //
-// Expand tile: a 512-column tile of one slice for 4 tokens.  Lanes own 8 consecutive
-// columns, whose rank values are one contiguous stretch of the rank-contiguous B
-// layout (the layout the matrix-core expand reads too, so a pool keeps one copy of
-// B).  The tile's rank-space values come from LDS, token-fastest (one 16-byte read
-// gives rank j for all 4 tokens), and the contraction over the rank stays in
-// registers, 8 ranks at a time behind scheduling fences to bound live ranges.  y
-// gets one rounding from y + s * acc in fp32, at the token's own row.
+// Expand tile: a 512-column tile of one slice (lanes own 8 consecutive columns, so
+// each rank-major row of B^T streams as one contiguous 1 KB request) for 4 tokens.
+// The tile's rank-space values come from LDS, token-fastest (one 16-byte read gives
+// rank j for all 4 tokens), and the contraction over the rank stays in registers,
+// rows of B^T consumed four at a time behind scheduling fences to bound live
+// ranges.  y gets one rounding from y + s * acc in fp32, at the token's own row.
 #pragma once
 
 #include "device_util.h"
@@ -138,47 +137,33 @@ template <> struct Row8<uint8_t> {   // FP8 pools: 8 bytes, widened at use
   __device__ __forceinline__ void get(float (&v)[8]) const { fp8x8_to_f32(w, v); }
 };
 
-// ranks per load batch of the decode expand: 16 for bf16 and FP8 pools (64 or 32 registers), 8 for fp32
+// rank rows of B^T per load batch: 16 for bf16 and FP8 pools (64 or 32 registers), 8 for fp32
 template <typename TW> struct ExpandRows { static constexpr int kBatch = sizeof(TW) <= 2 ? 16 : 8; };
 
 // One expand tile in two halves, so a caller can put other work between issuing the
-// loads and using them: issue() loads, for this lane's 8 output columns, the first RB
-// rank values of each column from the rank-contiguous B layout (column c of the slot
-// at c * rs, rs = the slot's rank rounded up to 8; chunks of 8 ranks past rs are
-// replaced by the first chunk and zeroed at use) and the 4 token rows of y; finish()
-// contracts with the rank-space values u4[j] (rank j, 4 tokens; zero past the rank and
-// for tokens past nt), each accumulator taking its ranks in ascending order, and
-// stores rows i < nt.
+// loads and using them: issue() loads the first RB rows of B^T and the 4 token rows
+// of y; finish() contracts with the rank-space values u4[j] (rank j, 4 tokens;
+// zero past the rank and for tokens past nt) and stores rows i < nt.
 template <typename TW, typename TY>
 struct ExpandTile {
   static constexpr int RB = ExpandRows<TW>::kBatch;
-  static constexpr int NQ = RB / 8;          // chunks of 8 ranks per column and batch
   static constexpr int LT = kExpandTok;
-  Row8<TW> b[kColsPerLane][NQ];
+  Row8<TW> b[RB];
   Row8<TY> yv[LT];
   TY* yrow[LT];
-  const TW* bk;
-  int rs;
+  const TW* bt;
   bool inb;
 
-  __device__ __forceinline__ void load_batch(int jb) {
-#pragma unroll
-    for (int c = 0; c < kColsPerLane; ++c)
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) b[c][q].load(bk + (size_t)c * rs + (jb + 8 * q < rs ? jb + 8 * q : 0));
-  }
-
-  // bk_slot: the slot's B at column o_n (columns of stride rs_); columns [c0, c0 + 512) of slice n
-  __device__ __forceinline__ void issue(const PoolView& P, const TW* __restrict__ bk_slot, int rs_, TY* __restrict__ y,
-                                        int ldy, int n, int c0, int r, const int4& tq) {
-    (void)r;
+  // bt_slot: B^T of the slot at column o_n (row stride D); columns [c0, c0 + 512) of slice n
+  __device__ __forceinline__ void issue(const PoolView& P, const TW* __restrict__ bt_slot, TY* __restrict__ y, int ldy,
+                                        int n, int c0, int r, const int4& tq) {
     const int lane = lane_id(), dn = P.d[n];
     const int col = c0 + lane * kColsPerLane;
     inb = col < dn;
     const int colc = min(col, dn - kColsPerLane);
-    rs = rs_;
-    bk = bk_slot + (size_t)colc * rs;
-    load_batch(0);
+    bt = bt_slot + colc;
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jj < r ? jj : 0) * P.D);
 #pragma unroll
     for (int i = 0; i < LT; ++i) {
       yrow[i] = y + (size_t)tok_at(tq, i) * ldy + P.o[n] + colc;
@@ -188,43 +173,37 @@ struct ExpandTile {
 
   __device__ __forceinline__ void finish(const PoolView& P, int r, int nt, float scale,
                                          const float4* __restrict__ u4) {
-    (void)P;
     const int rp = (r + RB - 1) / RB * RB;
     float acc[LT][kColsPerLane];
 #pragma unroll
     for (int i = 0; i < LT; ++i)
 #pragma unroll
       for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = 0.f;
-    // ranks [jb, jb + RB) against the rank-space values, 8 at a time
+    // rows [jb, jb + RB) of B^T against the rank-space values
     auto contract = [&](int jb) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int j0 = jb + 8 * q;
-        float4 uq[8];
+      for (int j4 = 0; j4 < RB; j4 += 4) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) uq[e] = u4[j0 + e];
+        for (int jj = j4; jj < j4 + 4; ++jj) {
+          b[jj].keep(jb + jj < r);
+          float bf[kColsPerLane];
+          b[jj].get(bf);
+          const float4 uq = u4[jb + jj];
+          const float uv[LT] = {uq.x, uq.y, uq.z, uq.w};
 #pragma unroll
-        for (int c = 0; c < kColsPerLane; ++c) {
-          b[c][q].keep(j0 < rs);
-          float bv[8];
-          b[c][q].get(bv);
+          for (int i = 0; i < LT; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float w = j0 + e < r ? bv[e] : 0.f;
-            acc[0][c] = fmaf(w, uq[e].x, acc[0][c]);
-            acc[1][c] = fmaf(w, uq[e].y, acc[1][c]);
-            acc[2][c] = fmaf(w, uq[e].z, acc[2][c]);
-            acc[3][c] = fmaf(w, uq[e].w, acc[3][c]);
-          }
+            for (int c = 0; c < kColsPerLane; ++c) acc[i][c] = fmaf(bf[c], uv[i], acc[i][c]);
         }
         sched_fence();
       }
     };
     sched_fence();
     contract(0);
-    // ranks above RB: further batches, each loaded after the previous is used
+    // ranks above RB: further batches of rows, each loaded after the previous is used
     for (int jb = RB; jb < rp; jb += RB) {
-      load_batch(jb);
+#pragma unroll
+      for (int jj = 0; jj < RB; ++jj) b[jj].load(bt + (size_t)(jb + jj < r ? jb + jj : 0) * P.D);
       sched_fence();
       contract(jb);
     }

@@ -4,10 +4,10 @@
 // instantiates that pair's kernels (so the library's kernels compile in parallel).
 //
 // Decode expand unit (one wave: slot, column tile of one slice, token tiles).  Lanes
-// own 8 consecutive output columns, whose rank values are one contiguous stretch of
-// the rank-contiguous B layout (8 columns x the slot's padded rank per lane); the
-// tile's rank-space values (split partials added) are staged in the wave's LDS and
-// read as broadcasts; the contraction over the rank stays in registers.  The epilogue updates the token's row of y at its original
+// own 8 consecutive output columns, so each rank-major row of B^T streams as one
+// contiguous 1 KB request; the tile's rank-space values (split partials added) are
+// staged in the wave's LDS and read as broadcasts; the contraction over the rank
+// stays in registers.  The epilogue updates the token's row of y at its original
 // index, adding s * acc in fp32, one rounding.  Long segments go to the matrix-core
 // units of mfma_tiles.h.
 #pragma once
@@ -29,7 +29,7 @@ namespace rax {
 // idx = lane + 64 q is rank idx / 4 of token idx % 4 (token-fastest, as the tile reads
 // them from LDS).  load() issues the first kUSplitBatch splits of every value
 // unconditionally (clamped addresses; splits past nsplit re-read the last), so it
-// can go out in the same batch as the tile's B values and y rows; stage() adds them in
+// can go out in the same batch as the tile's B^T and y rows; stage() adds them in
 // split order (-0.0f, the exact identity, for splits past nsplit; any further batch
 // loaded there) and writes usm, zero past the rank or the tile's tokens.
 template <int QV>
@@ -71,10 +71,10 @@ struct DecodeUPartials {
 // One decode expand item: column tile [c0, c0 + 512) of slice n, token tiles
 // tt0, tt0 + 4 * ntg, ... of slot s.  Per tile: the tile's rank-space values (split
 // partials added in split order, from L2) are staged in the wave's LDS token-fastest,
-// and the B values and y rows are loaded, then the contraction.  For the first tile,
+// and the B^T rows and y rows are loaded, then the contraction.  For the first tile,
 // when the padded rank gives at most QV values per lane (QV > 0), the partials go
-// out in the same batch as the B values and y rows, so the tile waits for one round trip
-// after its record; other tiles stage first, then load B and y.
+// out in the same batch as the B^T and y rows, so the tile waits for one round trip
+// after its record; other tiles stage first, then load B^T and y.
 template <typename TW, typename TY, int QV>
 __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const RouteView& R, const UView& U,
                                                     TY* __restrict__ y, int ldy, int s, const SlotEntry& e,
@@ -84,8 +84,7 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   const int lane = lane_id();
   const int r = e.rank;
   const int rp = (r + Tile::RB - 1) / Tile::RB * Tile::RB;   // rank padded to the row batch
-  const int rs = bk_stride(r);   // the slot's columns in the rank-contiguous layout
-  const TW* __restrict__ bk_slot = static_cast<const TW*>(P.Bk) + (size_t)s * P.D * P.Rk + (size_t)P.o[n] * rs;
+  const TW* __restrict__ bt_slot = static_cast<const TW*>(P.Bt) + (size_t)s * P.Rmax * P.D + P.o[n];
   int tt = tt0;
   if constexpr (QV > 0) {
     if (!U.by_token && kExpandTok * rp <= 64 * QV) {
@@ -93,7 +92,7 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
       DecodeUPartials<QV> up;
       up.load(U, n, p0 + tt, nt, r);
       Tile tile;
-      tile.issue(P, bk_slot, rs, y, ldy, n, c0, r, tq0);
+      tile.issue(P, bt_slot, y, ldy, n, c0, r, tq0);
       sched_fence();
       up.stage(U, rp, usm);
       wave_lds_sync();
@@ -114,7 +113,7 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
       usm[idx] = ok ? v : 0.f;
     }
     Tile tile;
-    tile.issue(P, bk_slot, rs, y, ldy, n, c0, r, tq);
+    tile.issue(P, bt_slot, y, ldy, n, c0, r, tq);
     wave_lds_sync();
     tile.finish(P, r, nt, e.scale, reinterpret_cast<const float4*>(usm));
     wave_lds_sync();
@@ -127,7 +126,7 @@ template <typename TW, typename TY, int QV, typename Order>
 __device__ __forceinline__ void expand_decode_item(const PoolView& P, const RouteView& R, const UView& U,
                                                    TY* __restrict__ y, int ldy, const Plan& plan,
                                                    int item, float* __restrict__ usm, const Order& order) {
-  // token-tile siblings (same slot and columns, same B values) are neighbours
+  // token-tile siblings (same slot and columns, same rows of B^T) are neighbours
   const int tg = item % plan.ntg;
   const int rest = item / plan.ntg;
   const int ct = rest % P.n_ctiles, si = rest / P.n_ctiles;

@@ -35,21 +35,23 @@ __global__ void pack_a_kernel(const T* __restrict__ src, T* __restrict__ dst, lo
     dst[e] = (src != nullptr && e < n_src) ? src[e] : T(0);
 }
 
-// B slice [d][rank] -> Bk [d][rs] (column i of the slice at i * rs, rs = rank rounded
-// up to 8); entries j >= rank are zero.  Optional fold of the scale: one fp32 product
-// rounded once to T.
+// B slice [d][rank] -> Bt rows [Rmax][D] (columns [0, d) of the slice) and Bk
+// [d][rs] (rs = rank rounded up to 8); entries j >= rank are zero.  Optional fold of
+// the scale: one fp32 product rounded once to T.
 template <typename T>
-__global__ void pack_b_kernel(const T* __restrict__ src, T* __restrict__ bk, int rank, int rs, int d, float scale,
-                              int premultiply) {
+__global__ void pack_b_kernel(const T* __restrict__ src, T* __restrict__ bt, T* __restrict__ bk,
+                              int rank, int Rmax, int rs, int d, int D, float scale, int premultiply) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d) return;
-  for (int j = 0; j < rs; ++j) {
+  const int jn = Rmax > rs ? Rmax : rs;
+  for (int j = 0; j < jn; ++j) {
     T v = T(0);
     if (src != nullptr && j < rank) {
       v = src[(long long)i * rank + j];
       if (premultiply) from_f(scale * to_f(v), v);
     }
-    bk[(long long)i * rs + j] = v;
+    if (j < Rmax) bt[(long long)j * D + i] = v;
+    if (j < rs) bk[(long long)i * rs + j] = v;
   }
 }
 
@@ -69,7 +71,7 @@ __global__ void pack_a_t_kernel(const T* __restrict__ src, T* __restrict__ dst, 
 __global__ void set_slot_kernel(SlotEntry* table, int slot, SlotEntry entry) { table[slot] = entry; }
 
 template <typename T>
-static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* Bk_dst,
+static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* Bt_dst, void* Bk_dst,
                        int rank, int Rmax, int Rk, int k, int d, int D, float scale, int premultiply,
                        int a_by_row, hipStream_t stream) {
   const long long n_all = (long long)Rmax * k, n_src = (long long)rank * k;
@@ -83,21 +85,21 @@ static hipError_t pack(const void* A_src, const void* B_src, void* A_dst, void* 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_b_kernel<T>, dim3((d + 255) / 256), dim3(256), 0, stream,
-                     static_cast<const T*>(B_src), static_cast<T*>(Bk_dst), rank, bk_stride(rank), d, scale,
-                     premultiply);
+                     static_cast<const T*>(B_src), static_cast<T*>(Bt_dst), static_cast<T*>(Bk_dst),
+                     rank, Rmax, bk_stride(rank), d, D, scale, premultiply);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_slice(int wdtype, const void* A_src, const void* B_src, void* A_dst,
-                             void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
+                             void* Bt_dst, void* Bk_dst, int rank, int Rmax, int Rk, int k, int d,
                              int D, float scale, int premultiply, int a_by_row, hipStream_t stream) {
   if (wdtype == LORA_BF16)
-    return pack<uint16_t>(A_src, B_src, A_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
+    return pack<uint16_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                           premultiply, a_by_row, stream);
   if (wdtype == LORA_FP8E4M3)
-    return pack<uint8_t>(A_src, B_src, A_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
+    return pack<uint8_t>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                          premultiply, a_by_row, stream);
-  return pack<float>(A_src, B_src, A_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
+  return pack<float>(A_src, B_src, A_dst, Bt_dst, Bk_dst, rank, Rmax, Rk, k, d, D, scale,
                      premultiply, a_by_row, stream);
 }
 

@@ -44,8 +44,8 @@ int g_launches = 0;   // launches the host code asked for
 namespace rax {
 hipError_t launch_routing(const int32_t*, int, int, int, int, int, int, int*, int*, int*, int*, int4*, int4*, int*,
                           int*, hipStream_t, const KTimer&) { ++g_launches; return hipSuccess; }
-hipError_t launch_pack_slice(int, const void*, const void*, void*, void*, int, int, int, int, int, int, float, int,
-                             int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_pack_slice(int, const void*, const void*, void*, void*, void*, int, int, int, int, int, int, float,
+                             int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_set_slot(SlotEntry* table, int slot, SlotEntry e, hipStream_t) {
   table[slot] = e;   // the stub table is host memory: keep it like the device would
   ++g_launches;
