@@ -49,6 +49,10 @@
  *                             instead of four when (column groups of four x tile
  *                             slots) is at most this (default 512)
  *       RAXLORA_XCD_GROUP     consecutive decode units kept on one XCD (default 4)
+ *       RAXLORA_GROUP_ORDER   0: grouped calls lay out their modules and decode units
+ *                             in the order given (default 1: modules with the longest
+ *                             shrink items first, decode expand units by descending
+ *                             slot rank; results are the same either way)
  *       RAXLORA_LOG           1: one line on stderr per shrink or expand launch with
  *                             the launch shape chosen (path, k split, waves, units)
  *       RAXLORA_SLOT_MODE     0: never use the slot-major kernels (one unit per slot,

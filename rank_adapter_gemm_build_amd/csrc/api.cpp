@@ -521,8 +521,19 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
   // slot mode for the whole launch when every module would take it on its own
   bool slot = true;
   for (int m = 0; m < n; ++m) slot = slot && slot_mode(pools[m], routing);
-  for (int m = 0; m < n; ++m) {
-    rax::GroupEntry& e = G.e[m];
+  // the shrink launch takes the modules with the longest items (most k steps per
+  // part) first, so they are not the last workgroups dispatched; each module's
+  // workgroups compute what they would in any order
+  int ord[LORA_MAX_GROUP];
+  for (int m = 0; m < n; ++m) ord[m] = m;
+  auto part_steps = [&](int m) {
+    return ceil_div(ceil_div(pools[m]->k, rax::kMfmaK), call_split(pools[m], routing, slot).nsplit);
+  };
+  if (env_int("RAXLORA_GROUP_ORDER", 1))
+    std::stable_sort(ord, ord + n, [&](int a, int b) { return part_steps(a) > part_steps(b); });
+  for (int i = 0; i < n; ++i) {
+    const int m = ord[i];
+    rax::GroupEntry& e = G.e[i];
     e.P = pool_view(pools[m]);
     e.x = x[m];
     e.ldx = ldx[m];
@@ -538,7 +549,20 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
   hipError_t e = rax::launch_shrink_group(pools[0]->wdtype, G, R, self_ids ? &sr : nullptr, stream,
                                           timer_for(rax::kKShrink));
   if (e != hipSuccess) return hip_fail(e, "grouped shrink launch");
-  for (int m = 0; m < n; ++m) G.e[m].plan = make_plan(pools[m], routing, true, slot);
+  for (int i = 0; i < n; ++i) G.e[i].plan = make_plan(pools[ord[i]], routing, true, slot);
+  // decode expand units by descending slot rank (the longest first), the rank of a slot
+  // taken as its largest over the modules; the order changes when units run, not what
+  // they compute
+  if (routing->S <= rax::kMaxOrderedSlots && env_int("RAXLORA_GROUP_ORDER", 1)) {
+    std::vector<int> idx(routing->S), rk(routing->S, 0);
+    for (int s = 0; s < routing->S; ++s) {
+      idx[s] = s;
+      for (int m = 0; m < n; ++m) rk[s] = std::max(rk[s], pools[m]->mirror[s].rank);
+    }
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return rk[a] > rk[b]; });
+    G.order.ordered = 1;
+    for (int s = 0; s < routing->S; ++s) G.order.s[s] = (uint8_t)idx[s];
+  }
   log_plan("grouped expand, first module", pools[0], routing, G.e[0].plan, n);
   e = rax::launch_expand_group(pools[0]->wdtype, ydtype, G, R, stream, timer_for(rax::kKExpand));
   if (e != hipSuccess) return hip_fail(e, "grouped expand launch");

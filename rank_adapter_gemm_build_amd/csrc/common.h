@@ -140,6 +140,8 @@ struct GroupEntry {
 struct GroupView {
   int n;
   GroupEntry e[kMaxGroup];
+  SlotOrder order;   // dispatch order of the decode expand units: slots by descending rank
+                     // (the largest over the modules), when ordered
 };
 
 // Optional per-launch timing: when start is non-null the kernel is launched with
@@ -180,6 +182,10 @@ struct SelfRoute {
   const int32_t* ids;
   RouteOut out;
 };
+// a grouped launch's arguments (module descriptors, routing, self-route) and the
+// runtime's hidden arguments fit the 4 KB kernel-argument segment
+static_assert(sizeof(GroupView) + sizeof(RouteView) + sizeof(SelfRoute) + 256 <= 4096, "grouped launch arguments");
+
 hipError_t launch_shrink(int wdtype, const PoolView& P, const RouteView& R, const void* x, int ldx,
                          const UView& U, const Plan& plan, const SelfRoute* sr, hipStream_t stream,
                          const KTimer& tm);

@@ -220,14 +220,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<
 }
 
 // Several modules of one batch in one launch (workgroup b runs as workgroup b - blk0
-// of its module's own launch would, with the slots dispatched by index)
+// of its module's own launch would, with the slots dispatched in the group's order)
 template <typename TW, typename TY, int KSM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ExpandWaves<TW, TY, KSM>::value))) void expand_group_kernel(GroupView G, RouteView R) {
   extern __shared__ float smem[];
   const int b = blockIdx.x;
   const GroupEntry& e = G.e[group_module(G, b)];
   expand_body<TW, TY, KSM>(e.P, R, e.U, static_cast<TY*>(e.y), e.ldy, e.plan, e.nm, b - e.blk0, smem,
-                           [](int si) { return si; });
+                           [&](int si) { return G.order.ordered ? (int)G.order.s[si] : si; });
 }
 
 template <typename TW, typename TY>
