@@ -515,9 +515,12 @@ def measure_embedding(torch, rx, lib, W, args, vocab=32000):
 def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
     """The same workload with FP8 (e4m3) adapter pools: every A and B converted to
     e4m3 by torch (float8_e4m3fn), activations and outputs bf16 as before; one step
-    = lora_route_linear + lora_linear per further module, rotating over instances
-    like the main loop.  Algorithmic bytes: the bf16 step's with the weight bytes
-    halved (x and y unchanged)."""
+    = lora_route_linear + lora_linear per further module, rotating over as many
+    instances as the bf16 loop (their traffic still several times the 256 MB
+    Infinity Cache; more instances, as many as the smaller FP8 step would take for
+    the same traffic, were measured to slow both the bf16 and the FP8 decode step by
+    about 1.2 us, so the two forms are compared at one rotation).  Algorithmic bytes:
+    the bf16 step's with the weight bytes halved (x and y unchanged)."""
     import numpy as np
     if W.dtype != "bf16" or not hasattr(torch, "float8_e4m3fn"):
         return None
@@ -529,7 +532,7 @@ def measure_fp8(torch, rx, lib, W, src, args, step_bytes_bf16, acc_bf16):
                  for s, r in W.ranks.items() if counts[s] > 0)
     step_bytes = step_bytes_bf16 - wbytes // 2
     per_inst = sum(W.S * W.Rmax * (m.k * len(m.slices) + 2 * sum(m.slices)) for m in W.modules)
-    M = max(2, min(args.max_instances, int(np.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes, 1)))))
+    M = max(2, min(args.max_instances, int(np.ceil(args.rotate_mib * 2 ** 20 / max(step_bytes_bf16, 1)))))
     M = min(M, max(2, int(40 * 2 ** 30 // max(per_inst, 1))))
 
     def fp8(t):

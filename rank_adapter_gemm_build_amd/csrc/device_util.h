@@ -46,17 +46,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // reuse the bf16 arithmetic.  The hardware conversions round to nearest even (checked
 // against the format definition on every e4m3 byte and every bf16 value in
 // [-448, 448]).
-__device__ __forceinline__ uint32_t f32x2_hi_to_bf16x2(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);   // exact: the low halves are zero
-}
-// 8 e4m3 bytes -> 8 bf16 (one 16-byte chunk)
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+// 8 e4m3 bytes -> 8 bf16 (one 16-byte chunk): gfx950's byte-pair to bf16-pair
+// conversion at scale 1, exact (checked on all 256 bytes against the fp32 conversion)
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 w) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  return make_uint4(f32x2_hi_to_bf16x2(a[0], a[1]), f32x2_hi_to_bf16x2(b[0], b[1]), f32x2_hi_to_bf16x2(c[0], c[1]),
-                    f32x2_hi_to_bf16x2(d[0], d[1]));
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, true)));
 }
 // 8 e4m3 bytes -> 8 floats
 __device__ __forceinline__ void fp8x8_to_f32(uint2 w, float (&v)[8]) {
@@ -69,21 +66,31 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 w, float (&v)[8]) {
 constexpr float kFp8Max = 448.f;
 // clamp to [-448, 448] keeping NaN (a comparison with NaN is false), as torch's clamp does
 __device__ __forceinline__ float fp8_clamp(float v) { return v > kFp8Max ? kFp8Max : (v < -kFp8Max ? -kFp8Max : v); }
+// Clamp of two packed bf16 values to [-448, 448] on their bit patterns, NaN kept: the
+// magnitude m (15 bits) is offset by 0x807f modulo 2^16, which puts the non-NaN
+// magnitudes 0 .. 0x7f80 at 0x807f .. 0xffff and the NaNs (0x7f81 ..) at 0 .. 0x7e;
+// one unsigned minimum against 448's offset magnitude (0x43e0 + 0x807f) then caps
+// exactly the finite and infinite magnitudes above 448, and the offset is taken back.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_clamp_fp8max(uint32_t w) {
+  const u16x2_t off = {0x807f, 0x807f}, cap = {0xc45f, 0xc45f};
+  const u16x2_t m = __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, w & 0x7fff7fffu) + off, cap) - off;
+  return (__builtin_bit_cast(uint32_t, m) & 0x7fff7fffu) | (w & 0x80008000u);
+}
 // FP8 pools' input conversion of 8 bf16 activations (page "TensorRT-LLM 源码完全拆解
-// (二十一)", section "前向替换"): clamp to [-448, 448], round to e4m3; 8 bytes, in order
+// (二十一)", section "前向替换"): clamp to [-448, 448], round to e4m3; 8 bytes, in order.
+// The clamp runs on the packed bf16 pairs, and gfx950's bf16-pair conversion (scale 1,
+// round to nearest even) writes two bytes per instruction; it alone would turn values
+// past 448 into NaN.  Checked on all 65536 bf16 bit patterns: the same bytes as the
+// clamp in fp32 followed by the fp32 conversion.
+__device__ __forceinline__ uint32_t bf16x4_to_fp8x4(uint32_t lo, uint32_t hi) {
+  i16x2_t p = {0, 0};
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, bf16x2_clamp_fp8max(lo)), 1.0f, false);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, bf16x2_clamp_fp8max(hi)), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, p);
+}
 __device__ __forceinline__ uint2 bf16x8_to_fp8x8(uint4 w) {
-  float v[8];
-  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-  v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
-  v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fp8_clamp(v[i]);
-  int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-  p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p0, true);
-  int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-  p1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], p1, true);
-  return make_uint2((uint32_t)p0, (uint32_t)p1);
+  return make_uint2(bf16x4_to_fp8x4(w.x, w.y), bf16x4_to_fp8x4(w.z, w.w));
 }
 // the same conversion, back to bf16 (for the vector units, which multiply in bf16)
 __device__ __forceinline__ uint4 bf16x8_to_fp8_grid(uint4 w) { return fp8x8_to_bf16x8(bf16x8_to_fp8x8(w)); }

@@ -133,6 +133,39 @@ def test_fp8_exact_integer_case(rx, mode):
     pool.close()
 
 
+@pytest.mark.parametrize("mode", ["default", "slot", "vector"])
+def test_fp8_every_bf16_activation_converts_exactly(rx, mode):
+    """Every bf16 bit pattern of x but the NaNs (set to 0) through the activation
+    conversion: with A and B one-hot (token t's rank-space value j is its x column j)
+    and scale 1, the fp32 branch of token t column d is e4m3(clamp(x[t][d])) exactly,
+    on the matrix cores (tile lists and slot mode) and on the vector units; +-inf and
+    everything past +-448 give +-448."""
+    import os
+    T, k, r = 256, 256, 256
+    pat = np.arange(T * k, dtype=np.uint32).astype(np.uint16).reshape(T, k)
+    f = (pat.astype(np.uint32) << 16).view(np.float32)
+    x = np.where(np.isnan(f), np.uint16(0), pat).astype(np.uint16)
+    eye = np.eye(r, dtype=np.float64)
+    A = {0: [_fp8_bytes(eye)]}
+    B = {0: [_fp8_bytes(eye)]}
+    ranks, alpha, ids = {0: r}, {0: float(r)}, np.zeros(T, dtype=np.int32)
+    env = {"slot": {"RAXLORA_SLOT_MODE": "1"}, "vector": {"RAXLORA_DISABLE_MFMA": "1"}}.get(mode, {})
+    os.environ.update(env)
+    try:
+        pool = _pool(rx, 1, r, k, [k], T, ranks, A, B, alpha)
+        y = _run(rx, pool, ids, x, np.zeros((T, k), dtype=np.float32), "f32")
+    finally:
+        for key in env:
+            os.environ.pop(key, None)
+    ref = _oracle(ranks, A, B, ids, x, alpha, 1, [k], r, np.zeros((T, k)))
+    got = from_device(y)
+    assert np.array_equal(got, ref)
+    xf = O.bf16_bits_to_f64(x)
+    assert np.array_equal(got, O.fp8_quantize(xf))                       # the conversion alone
+    assert np.all(got[np.isinf(xf)] == np.sign(xf[np.isinf(xf)]) * 448.0)
+    pool.close()
+
+
 @pytest.mark.parametrize("seed,T,S,k,slices,Rmax,premultiply", [
     (21, 37, 5, 520, [136, 24], 16, False),
     (22, 64, 8, 4096, [4096], 16, False),
