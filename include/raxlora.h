@@ -136,7 +136,9 @@ lora_status lora_compute_scale(float alpha, int rank, int rslora, float adapter_
  * padding of every slot ([TRT-LLM] "LoraConfig": a workspace bound, not
  * enlargeable later).  max_tokens bounds T for lora_linear / lora_shrink (it
  * sizes the pool-owned rank-space workspace: k-split partial sums, up to 16 x
- * num_slices x max_tokens x max_lora_rank fp32).  All slots start empty (rank 0).
+ * num_slices x max_tokens x max_lora_rank fp32, and for pools of at most 32 slots
+ * 16 more rows per slot, where a small decode batch's partial sums of each segment's
+ * first 16 tokens go).  All slots start empty (rank 0).
  * slice_out is a host array, read during the call.  The pool owns its device
  * memory (allocated on `device` here) until lora_pool_destroy.
  * Errors: out/slice_out NULL -> INVALID_ARG; max_slots outside [1, LORA_MAX_SLOTS],
@@ -347,7 +349,8 @@ lora_status lora_route_linear_join(const lora_pool* pool, lora_routing* routing,
  * Needs nsplit * num_slices * T * Rk * 4 bytes, where Rk is max_lora_rank rounded up
  * to 32 and nsplit at most 16 (in_features / 512 rounded up, halved for batches of at
  * least 64 tokens per slot); above the maximum the call fails with CAPACITY before any
- * work is enqueued.  Arguments and other errors as lora_linear.
+ * work is enqueued (when 16 rows per slot more fit as well, a small decode batch uses
+ * them as the pool's workspace would).  Arguments and other errors as lora_linear.
  */
 lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routing, const void* x, int ldx, void* y,
                                 int ldy, lora_dtype ydtype, hipStream_t stream);

@@ -31,7 +31,10 @@ struct lora_pool {
   void* Bt = nullptr;
   void* Bk = nullptr;
   SlotEntry* table = nullptr;
-  float* ws = nullptr;        // k-split partials [nsplit][N][max_tokens][Rk] by sorted position
+  float* ws = nullptr;        // k-split partials [nsplit][N][ws_rows][Rk]: rows by sorted position, then
+                              // slot mode's first-tile rows (kMfmaTileM per slot) when `heads`
+  int ws_rows = 0;
+  bool heads = false;
   int nsplit = 1, ns = 1;     // decode shrink: k splits, chunk steps per split (fixed by k)
   std::vector<SlotEntry> mirror;
   std::vector<uint8_t> order;  // slots by descending rank, stable (S <= kMaxOrderedSlots)
@@ -327,12 +330,17 @@ CallSplit call_split(const lora_pool* p, const lora_routing* r, bool slot) {
   return c;
 }
 
-// The pool's workspace: [nsplit][N][max_tokens][Rk], rows by sorted position (rows
-// padded to Rk, a multiple of 32 floats, so they can be read 16 bytes at a time); a
-// call uses its first nsplit parts.
-rax::UView workspace_view(const lora_pool* p, int nsplit) {
-  return rax::UView{p->ws, (long long)p->N * p->max_tokens * p->Rk, (long long)p->max_tokens * p->Rk, p->Rk,
-                    nsplit, 0};
+// The pool's workspace: [nsplit][N][ws_rows][Rk], rows by sorted position (rows
+// padded to Rk, a multiple of 32 floats, so they can be read 16 bytes at a time), then,
+// for pools that can take slot mode by default (at most kHeadSlots slots), kMfmaTileM
+// rows per slot for the first tile of its segment (`heads`: a slot-mode call's
+// partials of a segment's first tile go there, where the expand finds them without the
+// segment's first sorted position); a call uses its first nsplit parts.
+constexpr int kHeadSlots = 32;   // slot mode is the default only for 4 S <= T <= 128
+rax::UView workspace_view(const lora_pool* p, int nsplit, bool heads = false) {
+  rax::UView v{p->ws, (long long)p->N * p->ws_rows * p->Rk, (long long)p->ws_rows * p->Rk, p->Rk, nsplit, 0};
+  v.head0 = heads && p->heads ? p->max_tokens : -1;
+  return v;
 }
 
 // The caller's u: finished values [N][T][Rmax], rows by token index.
@@ -428,7 +436,7 @@ lora_status shrink_join_expand(const lora_pool* pool, const lora_routing* routin
                                void* y, int ldy, lora_dtype ydtype, hipStream_t stream, hipEvent_t y_ready,
                                const int32_t* self_ids) {
   const bool slot = slot_mode(pool, routing);
-  const rax::UView W = workspace_view(pool, call_split(pool, routing, slot).nsplit);
+  const rax::UView W = workspace_view(pool, call_split(pool, routing, slot).nsplit, slot);
   lora_status st = run_shrink(pool, routing, x, ldx, W, stream, slot, self_ids);
   if (st != LORA_OK) return st;
   if (y_ready) {
@@ -539,7 +547,7 @@ lora_status group_impl(const lora_pool* const* pools, int n, const lora_routing*
     e.ldx = ldx[m];
     e.y = y[m];
     e.ldy = ldy[m];
-    e.U = workspace_view(pools[m], call_split(pools[m], routing, slot).nsplit);
+    e.U = workspace_view(pools[m], call_split(pools[m], routing, slot).nsplit, slot);
     e.plan = make_plan(pools[m], routing, false, slot);
   }
   const rax::RouteView R = route_view(routing);
@@ -679,7 +687,9 @@ static lora_status create_pool(lora_pool** out, int device, int max_slots, int m
   if (embedding) p->nsplit = p->ns = 1;   // the gathered u is final: one part
   // workspace parts: the most any call can use (the slot-major shrink may split finer)
   const int ws_parts = embedding || wdtype == LORA_F32 ? p->nsplit : std::max(p->nsplit, slot_nsplit(in_features));
-  const size_t ws_bytes = (size_t)ws_parts * num_slices * max_tokens * p->Rk * sizeof(float);
+  p->heads = !embedding && wdtype != LORA_F32 && max_slots <= kHeadSlots;
+  p->ws_rows = max_tokens + (p->heads ? rax::kMfmaTileM * max_slots : 0);
+  const size_t ws_bytes = (size_t)ws_parts * num_slices * p->ws_rows * p->Rk * sizeof(float);
   hipError_t e;
   if ((e = hipMalloc(&p->A, a_bytes)) != hipSuccess || (e = hipMalloc(&p->Bt, b_bytes)) != hipSuccess ||
       (e = hipMalloc(&p->Bk, bk_bytes)) != hipSuccess ||
@@ -994,10 +1004,15 @@ lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routi
   if ((st = check_x(pool, routing->T, x, ldx)) != LORA_OK) return st;
   if ((st = check_y(pool, routing->T, y, ldy, ydtype)) != LORA_OK) return st;
   if (routing->T == 0) return ok();
-  // the partials of this call: [nsplit][N][T][Rk] fp32, rows by sorted position
+  // the partials of this call: [nsplit][N][rows][Rk] fp32, rows by sorted position, then
+  // in slot mode the first-tile rows of the pool's slots when they fit as well
   const bool slot = slot_mode(pool, routing);
   const CallSplit cs = call_split(pool, routing, slot);
-  const size_t need = (size_t)cs.nsplit * pool->N * routing->T * pool->Rk * sizeof(float);
+  auto bytes = [&](long long rows) { return (size_t)cs.nsplit * pool->N * rows * pool->Rk * sizeof(float); };
+  const bool heads = slot && pool->heads &&
+                     bytes(routing->T + (long long)rax::kMfmaTileM * pool->S) <= rax::kNoAllocScratchBytes;
+  const long long rows = routing->T + (heads ? (long long)rax::kMfmaTileM * pool->S : 0);
+  const size_t need = bytes(rows);
   if (need > rax::kNoAllocScratchBytes)
     return fail(LORA_ERR_CAPACITY, "this call needs %zu bytes of scratch (%d k splits x %d slices x %d tokens x %d "
                 "ranks x 4), above the %zu-byte array", need, cs.nsplit, pool->N, routing->T, pool->Rk,
@@ -1007,9 +1022,9 @@ lora_status lora_linear_noalloc(const lora_pool* pool, const lora_routing* routi
   void* scratch = nullptr;
   hipError_t e = rax::noalloc_scratch(pool->device, &scratch);
   if (e != hipSuccess) return hip_fail(e, "scratch address");
-  const long long rows = routing->T;
-  const rax::UView W{static_cast<float*>(scratch), (long long)pool->N * rows * pool->Rk, rows * pool->Rk, pool->Rk,
-                     cs.nsplit, 0};
+  rax::UView W{static_cast<float*>(scratch), (long long)pool->N * rows * pool->Rk, rows * pool->Rk, pool->Rk,
+               cs.nsplit, 0};
+  W.head0 = heads ? routing->T : -1;
   if ((st = run_shrink(pool, routing, x, ldx, W, stream, slot)) != LORA_OK) return st;
   if ((st = run_expand(pool, routing, W, y, ldy, ydtype, stream, slot)) != LORA_OK) return st;
   return ok();

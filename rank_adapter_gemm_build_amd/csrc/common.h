@@ -95,6 +95,10 @@ struct UView {
   float* p;
   long long split_stride, n_stride, row_stride;
   int nsplit, by_token;
+  // slot mode: the first kMfmaTileM tokens of slot s's segment have their rows at
+  // head0 + kMfmaTileM * s + t instead of at their sorted positions, so the expand finds
+  // them before it has read the slot's routing record (-1: all rows by sorted position)
+  int head0 = -1;
 };
 
 // Launch shape of one shrink or expand call; every workgroup is one wave.

@@ -241,7 +241,8 @@ __device__ __forceinline__ void shrink_slot_wg(const PoolView& P, const RouteVie
       if (t < len && fr < F && jj < r) {
         float v = sm.red[0][t][rr];
         for (int ww = 1; ww < nw; ++ww) v += sm.red[ww][t][rr];
-        U.p[part * U.split_stride + nn * U.n_stride + (long long)(p0 + t0 + t) * U.row_stride + jj] = v;
+        const long long row = t0 == 0 && U.head0 >= 0 ? (long long)U.head0 + kMfmaTileM * s + t : p0 + t0 + t;
+        U.p[part * U.split_stride + nn * U.n_stride + row * U.row_stride + jj] = v;
       }
     }
     __syncthreads();

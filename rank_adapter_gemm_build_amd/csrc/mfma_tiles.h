@@ -250,6 +250,13 @@ struct UPartials {
     base = U.p + n * U.n_stride + (long long)(p0 + min(lr, len - 1)) * U.row_stride + (j0 < r ? j0 : 0);
     load_batch(U, 0);
   }
+  // rank step 0 of row `row` (slot mode's first-tile rows, known before the segment
+  // is: the token and rank are masked in finish())
+  __device__ __forceinline__ void load_head(const UView& U, int n, long long row) {
+    const int j0 = 8 * (lane_id() >> 4);
+    base = U.p + n * U.n_stride + row * U.row_stride + (j0 + 8 <= U.row_stride ? j0 : 0);
+    load_batch(U, 0);
+  }
   __device__ __forceinline__ void add_batch(const UView& U, int q0, float (&v)[8]) const {
 #pragma unroll
     for (int q = 0; q < kUSplitBatch; ++q) {
@@ -279,6 +286,15 @@ struct UPartials {
     for (int q = 0; q < 8; ++q) v[q] = (lr < len && j0 + q < r) ? v[q] : 0.f;
     u_hilo(v, uh, ul);
   }
+};
+
+// The object a body with NSB batches loads its first rank step into: the caller's
+// one-batch object when NSB == 1, else its own.
+template <int NSB> struct UPartialsPick {
+  __device__ __forceinline__ static UPartials<NSB>& get(UPartials<NSB>& own, UPartials<1>&) { return own; }
+};
+template <> struct UPartialsPick<1> {
+  __device__ __forceinline__ static UPartials<1>& get(UPartials<1>&, UPartials<1>& ext) { return ext; }
 };
 
 // The same fragment from the caller's finished u (rows by token, row stride Rmax),
@@ -463,7 +479,8 @@ template <typename TW, typename TY, int NKS, int NSB, int CB>
 __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView& U, TY* __restrict__ y, int ldy,
                                                  const TW* __restrict__ bk, int rs, int n, int on, int dn,
                                                  int c00, int p0, int len, const int* __restrict__ tokp, int tokv, int r,
-                                                 int nks, float scale, float* __restrict__ ds) {
+                                                 int nks, float scale, float* __restrict__ ds, UPartials<1>& ext,
+                                                 bool ext_loaded) {
   constexpr int BC = ExpandBlockWidth<TW, TY, NKS>::value;
   constexpr int NB = CB * (kMfmaCols / BC);                     // blocks of the unit
   using Blk = ExpandMfmaBlock<TW, TY, NKS, BC>;
@@ -477,8 +494,11 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
     // soon as the token id is in, while the rest is still in flight
     const int tok = tokp ? *tokp : tokv;
     sched_fence();
-    UPartials<NSB> up;
-    up.load(U, n, p0, len, r, 0);
+    // one batch of partials: the caller's object, possibly already in flight (slot
+    // mode's first tile)
+    UPartials<NSB> own;
+    UPartials<NSB>& up = UPartialsPick<NSB>::get(own, ext);
+    if (!(NSB == 1 && ext_loaded)) up.load(U, n, p0, len, r, 0);
     b0.issue_b(bk, rs, dn, c00, nks);
     sched_fence();
     Y.load(tok, y, ldy, on);
@@ -555,13 +575,15 @@ template <typename TW, typename TY, int KSM>
 __device__ __forceinline__ void expand_mfma_tile(const PoolView& P, const RouteView& R, const UView& U,
                                                  TY* __restrict__ y, int ldy, int slot, const SlotEntry& e, int n,
                                                  int c00, int p0, int len, const int* __restrict__ tokp, int tokv,
-                                                 int cb, float* __restrict__ ds) {
+                                                 int cb, float* __restrict__ ds, UPartials<1>& ext,
+                                                 bool ext_loaded) {
   const int on = P.o[n], dn = P.d[n];
   const int r = e.rank, nks = (r + kMfmaK - 1) / kMfmaK, rs = bk_stride(r);
   const TW* __restrict__ bk = static_cast<const TW*>(P.Bk) + (size_t)slot * P.D * P.Rk + (size_t)on * rs;
   const int nsb = U.by_token ? 0 : U.nsplit <= kUSplitBatch ? 1 : 2;
 #define RAX_EXPAND_BODY(NK, NB, CB) \
-  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tokp, tokv, r, nks, e.scale, ds)
+  expand_mfma_body<TW, TY, NK, NB, CB>(R, U, y, ldy, bk, rs, n, on, dn, c00, p0, len, tokp, tokv, r, nks, e.scale, ds, \
+                                       ext, ext_loaded)
 #define RAX_EXPAND_BODIES(NK)                                                          \
   do {                                                                                 \
     if (cb == 1) {                                                                     \
@@ -597,14 +619,21 @@ __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteV
   // this lane's token id (token lane % 16): loaded by the body ahead of the partials
   const int* __restrict__ tokp = R.sorted + p0 + min(lane_id() & 15, len - 1);
   if (e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
-  expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, slot, e, n, blk0 * kMfmaCols, p0, len, tokp, 0, cb, ds);
+  UPartials<1> ext;
+  expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, slot, e, n, blk0 * kMfmaCols, p0, len, tokp, 0, cb, ds, ext, false);
 }
 
 // Slot-mode expand unit: every tile of slot s's segment (any length) for column group
-// grp.  First round trip: the slot's routing record (segment length, first sorted
-// position, first token ids; entries past the segment repeat a valid token) and the
-// slot-table entry; the first tile's partials, B fragments and y rows then go out
-// together.  Tokens past the record's come from the sorted list.
+// grp.  The first tile's partials are at first-tile rows when U.head0 >= 0 (rows that
+// depend only on s), else at its sorted positions like the other tiles'.  For pools of
+// one rank step with first-tile rows and one batch of partials, this lane's token id
+// of the first tile goes out first, then that tile's partials, then the slot's routing
+// record header and slot-table entry (scalar loads, counted apart from the vector
+// loads): the y rows and B fragments are addressed as soon as the token id and the
+// entry are in, while the partials, the longest round trip, are still on their way; a
+// segment of one tile then needs nothing else (a longer one reads them again in its
+// tile loop).  Otherwise the record, the token ids and the entry come first, the
+// partials after them.  Tokens past the record's come from the sorted list.
 template <typename TW, typename TY, int KSM>
 __device__ __forceinline__ void expand_slot_unit(const PoolView& P, const RouteView& R, const UView& U,
                                                  TY* __restrict__ y, int ldy, int s, int grp, int cb,
@@ -614,20 +643,41 @@ __device__ __forceinline__ void expand_slot_unit(const PoolView& P, const RouteV
   if (n < 0) return;
   const int lr = lane_id() & 15;
   const int* __restrict__ rec = R.rec + (size_t)s * kRecInts;
+  const bool head = U.head0 >= 0;   // the shrink put the first tile's partials at first-tile rows
+  // issued ahead for pools of one rank step (their units have the registers for it)
+  const bool ahead = KSM == 1 && head && U.nsplit <= kUSplitBatch;
+  int tok0 = 0;
+  UPartials<1> pre;
+  if (ahead) {
+    tok0 = rec[4 + lr];
+    sched_fence();
+    pre.load_head(U, n, (long long)U.head0 + kMfmaTileM * s + lr);
+    sched_fence();
+  }
   const int2 hdr = *reinterpret_cast<const int2*>(rec);
-  const int tok0 = rec[4 + lr];
+  if (!ahead) tok0 = rec[4 + lr];
   const SlotEntry e = P.table[s];
   const int L = __builtin_amdgcn_readfirstlane(hdr.x), p0 = __builtin_amdgcn_readfirstlane(hdr.y);
   if (L == 0 || e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
+  if (ahead && L <= kMfmaTileM) {
+    // a segment of one tile (the common decode case): its partials are already in flight
+    expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, s, e, n, blk0 * kMfmaCols, U.head0 + kMfmaTileM * s, L, nullptr,
+                                  tok0, cb, ds, pre, true);
+    return;
+  }
+  UPartials<1> ext;
   for (int t0 = 0; t0 < L; t0 += kMfmaTileM) {
     const int len = min(kMfmaTileM, L - t0), ti = t0 + min(lr, len - 1);
     const int tk = t0 == 0 ? tok0 : (ti < kRecTokens ? rec[4 + ti] : R.sorted[p0 + ti]);
+    // partial rows: the first tile's at its first-tile rows (read again), the others by
+    // sorted position
+    const int urow = head && t0 == 0 ? U.head0 + kMfmaTileM * s : p0 + t0;
     // values the tile body derives are recomputed per tile rather than held across
     // the loop (an opaque copy of the slot's entry and indices)
     SlotEntry ev = e;
     int sv = s, nv = n, cv = blk0 * kMfmaCols;
     asm volatile("" : "+s"(sv), "+s"(nv), "+s"(cv), "+s"(ev.rank), "+s"(ev.scale), "+s"(ev.slice_mask));
-    expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, sv, ev, nv, cv, p0 + t0, len, nullptr, tk, cb, ds);
+    expand_mfma_tile<TW, TY, KSM>(P, R, U, y, ldy, sv, ev, nv, cv, urow, len, nullptr, tk, cb, ds, ext, false);
   }
 }
 
