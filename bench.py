@@ -879,14 +879,23 @@ def run(args):
     roofline["frac_of_copy"] = round(achieved / ceil["copy_gbps"], 4)
     roofline["frac_of_read_ceiling"] = round(achieved / ceil["read_gbps"], 4)
 
-    # the eager legs first: after the graph and two-stream legs, eager launches on the
-    # current stream were measured slower (the FP8 step 12.9 -> 19.3 us)
-    embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
-    fp8 = None if args.no_extras else measure_fp8(torch, rx, lib, W, src, args, step_bytes, acc)
-    graph_overlap = None if args.no_extras else measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
+    # the eager legs first, each with only its own instances allocated (after the graph
+    # and two-stream legs, eager launches on the current stream were measured slower:
+    # the FP8 step 12.9 -> 19.3 us), then the graph and overlap legs on a new set
     for inst in insts:
         inst.close()
     insts = []
+    torch.cuda.synchronize()
+    embedding = None if args.no_extras else measure_embedding(torch, rx, lib, W, args)
+    fp8 = None if args.no_extras else measure_fp8(torch, rx, lib, W, src, args, step_bytes, acc)
+    graph_overlap = None
+    if not args.no_extras:
+        insts = [Instance(rx, torch, W, src, None) for _ in range(M)]
+        torch.cuda.synchronize()
+        graph_overlap = measure_graph_and_overlap(torch, rx, lib, insts, src, W, ydt, args)
+        for inst in insts:
+            inst.close()
+        insts = []
     del src
     torch.cuda.synchronize()
 
