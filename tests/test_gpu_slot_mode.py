@@ -128,6 +128,33 @@ def test_slot_mode_against_oracle(rx, case):
     _log(f"  delta error: slot mode {err:.2e}, tile lists {err_t:.2e}")
 
 
+def test_slot_mode_noalloc_without_first_tile_rows(rx):
+    """A slot-mode call whose partial sums fit the allocation-free call's array only
+    without the first-tile rows (k = 32768: 16 parts, 3 slices, ranks padded to 256,
+    256 tokens over 8 slots): that call keeps every row by sorted position and is
+    still bitwise equal to lora_linear, whose pool workspace has the first-tile rows."""
+    import torch
+    W = small_case(831, T=256, S=8, k=32768, slices=[64, 64, 64], Rmax=256, ranks={0: 4, 3: 7, 6: 1})
+    mod = W.modules[0]
+    zero = np.zeros((W.T, sum(mod.slices)), dtype=np.float32)
+    _log(f"slot mode, allocation-free call past its first-tile rows: T={W.T} S={W.S} k={mod.k}")
+    with _mode("1"):
+        d_lin = _linear(rx, W, mod, zero, "f32", fused=False)
+        pool = make_pool(rx, W, mod)
+        R, _ = make_routing(rx, W)
+        x = to_device(mod.x, W.dtype)
+        d_na = to_device(zero, "f32")
+        st = rx.lib.lora_linear_noalloc(pool.handle, R.handle, x.data_ptr(), x.stride(0), d_na.data_ptr(),
+                                        d_na.stride(0), rx.LORA_F32, None)
+        assert st == 0, rx.lora_last_error()
+        torch.cuda.synchronize()
+        pool.close(); R.close()
+    assert np.array_equal(bits(d_na), bits(d_lin))
+    delta = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros(zero.shape), oracle_adapters(W, mod), mod.slices, W.ids, W.S,
+                         "bf16", max_rank=W.Rmax)
+    check_close(from_device(d_lin), delta, "bf16", "slot-mode delta, k = 32768, three slices")
+
+
 def test_slot_mode_untouched_rows_and_columns(rx):
     """No-LoRA rows, an empty slot, a zero-scale slot and a missing slice stay
     bit-identical in slot mode."""
