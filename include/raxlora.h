@@ -418,6 +418,19 @@ lora_status lora_route_embedding(const lora_pool* pool, lora_routing* routing, c
                                  const int32_t* vocab_ids, void* y, int ldy, lora_dtype ydtype, hipStream_t stream);
 
 /*
+ * Index checks (diagnostics): a library built with -DRAXLORA_DEBUG (build.py
+ * --debug: libraxlora_debug.so) checks, in its kernels, every index it takes from
+ * memory (token ids, slots, sorted positions, workspace rows) against its range; a
+ * failed check is counted and the access goes to index 0 instead, so a wrong index
+ * shows as a count rather than a fault.  *enabled = 1 in such a build, 0 otherwise
+ * (where *faults is always 0); *faults = the checks failed on the current device since
+ * the last reset (all kernels of the library, after the work enqueued so far has
+ * finished: the call synchronises the device); reset != 0 clears the count.
+ * Errors: NULL -> INVALID_ARG; a HIP error reading the counts -> HIP.
+ */
+lora_status lora_index_checks(int* enabled, unsigned long long* faults, int reset);
+
+/*
  * Bandwidth probe (diagnostics): the rate this GPU's memory gives a plain streaming
  * kernel, the ceiling against which the LoRA kernels' traffic is read.  ratio <= 0:
  * read read_bytes from src (device, 16-byte aligned), 16 bytes per lane, and write

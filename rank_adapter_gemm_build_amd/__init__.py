@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libraxlora.so")
+# RAXLORA_LIBRARY: the path of another build of the same library (the index-checking
+# variant, libraxlora_debug.so) to load instead
+LIB_PATH = os.environ.get("RAXLORA_LIBRARY") or os.path.join(_HERE, "libraxlora.so")
 
 LORA_F32, LORA_BF16, LORA_FP8E4M3 = 0, 1, 2
 LORA_SRC_DEVICE, LORA_PREMULTIPLY = 1, 2
@@ -56,6 +58,7 @@ SIGNATURES = {
     "lora_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_route_linear_join": (_I, [_P, _P, _VP, _I, _VP, _I, _VP, _I, _I, _VP, _VP]),
     "lora_bandwidth_probe": (_I, [_VP, C.c_uint64, _VP, C.c_uint64, _I, _VP]),
+    "lora_index_checks": (_I, [C.POINTER(C.c_int), C.POINTER(C.c_uint64), _I]),
     "lora_linear_noalloc": (_I, [_P, _P, _VP, _I, _VP, _I, _I, _VP]),
     "lora_linear_group": (_I, [C.POINTER(_P), _I, _P, C.POINTER(_VP), C.POINTER(C.c_int), C.POINTER(_VP),
                                C.POINTER(C.c_int), _I, _VP]),
@@ -218,6 +221,14 @@ def lora_route_linear_join(pool: int, routing: int, ids: int, T: int, x: int, ld
                            ydtype: int, stream: int, y_ready: int) -> None:
     _check(lib.lora_route_linear_join(pool, routing, ids or None, T, x or None, ldx, y or None, ldy, ydtype,
                                       stream or None, y_ready or None), "lora_route_linear_join")
+
+
+def index_checks(reset: bool = False):
+    """(enabled, failed checks) of the index-checking build (lora_index_checks); (False,
+    0) for the release build.  Synchronises the device."""
+    en, n = C.c_int(), C.c_uint64()
+    _check(lib.lora_index_checks(C.byref(en), C.byref(n), int(bool(reset))), "lora_index_checks")
+    return bool(en.value), int(n.value)
 
 
 def lora_timing_enable(on: bool) -> None:

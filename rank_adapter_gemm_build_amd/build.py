@@ -21,6 +21,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libraxlora.so")
+# the index-checking variant (-DRAXLORA_DEBUG): the same kernels with every index taken
+# from memory checked against its range (lora_index_checks)
+BUILD_DEBUG = os.path.join(ROOT, "_build_debug")
+LIB_DEBUG = os.path.join(PKG, "libraxlora_debug.so")
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -39,8 +43,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
         cmd = [hipcc(), "-x", "hip", *HIP_ONLY, *COMMON, *extra, "-c", src, "-o", obj]
     else:  # host-only C++: no device pass
@@ -55,35 +59,38 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def _stale(src: str, headers) -> bool:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _stale(src: str, headers, build_dir: str = BUILD) -> bool:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
     return any(os.path.getmtime(f) > t for f in [src, *headers])
 
 
-def build(verbose: bool = True, extra=(), incremental: bool = False) -> str:
+def build(verbose: bool = True, extra=(), incremental: bool = False, debug: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library; returns its path.
-    incremental: recompile only sources older than themselves or any header."""
-    os.makedirs(BUILD, exist_ok=True)
+    incremental: recompile only sources older than themselves or any header.
+    debug: the index-checking variant, libraxlora_debug.so, from objects of its own."""
+    build_dir, lib = (BUILD_DEBUG, LIB_DEBUG) if debug else (BUILD, LIB)
+    extra = list(extra) + (["-DRAXLORA_DEBUG"] if debug else [])
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
         [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
-    todo = [s for s in srcs if not incremental or extra or _stale(s, headers)]
+    todo = [s for s in srcs if not incremental or _stale(s, headers, build_dir)]
     with cf.ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
-        list(ex.map(lambda s: _compile(s, list(extra)), todo))
-    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
-    tmp = LIB + ".tmp"
+        list(ex.map(lambda s: _compile(s, extra, build_dir), todo))
+    objs = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in srcs]
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources for {ARCH}")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources for {ARCH}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(incremental="--incremental" in sys.argv[1:])
+    build(incremental="--incremental" in sys.argv[1:], debug="--debug" in sys.argv[1:])

@@ -17,6 +17,18 @@
 
 using rax::SlotEntry;
 
+#ifdef RAXLORA_DEBUG
+namespace rax {   // each kernel translation unit's count of failed index checks
+hipError_t index_faults_linear(unsigned int*, bool);
+hipError_t index_faults_routing(unsigned int*, bool);
+hipError_t index_faults_w16_y16(unsigned int*, bool);
+hipError_t index_faults_w16_y32(unsigned int*, bool);
+hipError_t index_faults_w32_y32(unsigned int*, bool);
+hipError_t index_faults_w8_y16(unsigned int*, bool);
+hipError_t index_faults_w8_y32(unsigned int*, bool);
+}  // namespace rax
+#endif
+
 struct lora_pool {
   int device = 0;
   int S = 0, Rmax = 0, Rk = 0, k = 0, N = 0, D = 0, max_tokens = 0;
@@ -1144,6 +1156,29 @@ lora_status lora_bandwidth_probe(const void* src, uint64_t read_bytes, void* dst
     return fail(LORA_ERR_SHAPE, "dst_bytes below read_bytes / ratio");
   hipError_t e = rax::launch_bandwidth_probe(src, read_bytes, dst, dst_bytes, ratio, stream);
   if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
+lora_status lora_index_checks(int* enabled, unsigned long long* faults, int reset) {
+  if (!enabled || !faults) return fail(LORA_ERR_INVALID_ARG, "enabled and faults must not be NULL");
+  *faults = 0;
+#ifdef RAXLORA_DEBUG
+  *enabled = 1;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronising before reading the index checks");
+  using Reader = hipError_t (*)(unsigned int*, bool);
+  const Reader readers[] = {rax::index_faults_linear,    rax::index_faults_routing,   rax::index_faults_w16_y16,
+                            rax::index_faults_w16_y32,   rax::index_faults_w32_y32,   rax::index_faults_w8_y16,
+                            rax::index_faults_w8_y32};
+  for (Reader rd : readers) {
+    unsigned int v = 0;
+    if ((e = rd(&v, reset != 0)) != hipSuccess) return hip_fail(e, "reading the index checks");
+    *faults += v;
+  }
+#else
+  (void)reset;
+  *enabled = 0;
+#endif
   return ok();
 }
 

@@ -21,6 +21,34 @@
 
 namespace rax {
 
+// Index checks of the debug build (compiled with -DRAXLORA_DEBUG): an index taken from
+// memory (a token id, a slot, a sorted position, a workspace row) that falls outside
+// its range counts in this translation unit's counter and is replaced by 0, so the
+// access stays in bounds and the fault shows as a count read back by
+// lora_index_checks.  Other builds take the index as it is, with no code.
+#ifdef RAXLORA_DEBUG
+static __device__ unsigned int g_index_faults;
+__device__ __forceinline__ int checked_index(int i, long long n) {
+  if (i >= 0 && i < n) return i;
+  atomicAdd(&g_index_faults, 1u);
+  return 0;
+}
+// host accessor of a translation unit's counter (added to the others by lora_index_checks)
+#define RAX_INDEX_FAULTS_ACCESSOR(name)                                                       \
+  hipError_t index_faults_##name(unsigned int* out, bool reset) {                             \
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_index_faults), sizeof(unsigned int)); \
+    if (e == hipSuccess && reset) {                                                           \
+      const unsigned int zero = 0;                                                            \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_index_faults), &zero, sizeof(unsigned int));         \
+    }                                                                                         \
+    return e;                                                                                 \
+  }
+#else
+__device__ __forceinline__ int checked_index(int i, long long) { return i; }
+#define RAX_INDEX_FAULTS_ACCESSOR(name)
+#endif
+#define RAX_IDX(i, n) ::rax::checked_index((i), (n))
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- bfloat16

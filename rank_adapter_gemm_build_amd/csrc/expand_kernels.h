@@ -43,7 +43,8 @@ struct DecodeUPartials {
     for (int qv = 0; qv < QV; ++qv) {
       const int idx = lane + 64 * qv, j = idx >> 2, i = idx & 3;
       ok[qv] = i < nt && j < r;
-      base[qv] = U.p + n * U.n_stride + (long long)(row0 + (ok[qv] ? i : 0)) * U.row_stride + (ok[qv] ? j : 0);
+      base[qv] = U.p + n * U.n_stride +
+                 (long long)RAX_IDX(row0 + (ok[qv] ? i : 0), U.n_stride / U.row_stride) * U.row_stride + (ok[qv] ? j : 0);
 #pragma unroll
       for (int q = 0; q < kUSplitBatch; ++q) pv[qv][q] = base[qv][(long long)min(q, U.nsplit - 1) * U.split_stride];
     }
@@ -103,12 +104,13 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   }
   for (; tt < L; tt += ntg * kExpandTok) {
     const int nt = min(kExpandTok, L - tt);
-    const int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
+    const int4 tq = tt == tt0 ? tq0 : checked_tokens(segment_tokens(R, s, tt, p0, L), R.T);
     for (int idx = lane; idx < kExpandTok * rp; idx += 64) {
       const int j = idx >> 2, i = idx & 3;
       const bool ok = i < nt && j < r;
       const int ic = ok ? i : 0, jc = ok ? j : 0;
-      const long long row = U.by_token ? (long long)R.sorted[p0 + tt + ic] : (long long)(p0 + tt + ic);
+      const long long row = U.by_token ? (long long)RAX_IDX(R.sorted[p0 + tt + ic], R.T)
+                                       : (long long)RAX_IDX(p0 + tt + ic, U.n_stride / U.row_stride);
       const float v = sum_splits(U.p + n * U.n_stride + row * U.row_stride + jc, U.split_stride, U.nsplit);
       usm[idx] = ok ? v : 0.f;
     }
@@ -137,11 +139,12 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
                                    : make_int4(0, 0, 0, 0);
   const SlotEntry e = P.table[s];
-  const int L = hdr.x, p0 = hdr.y;
+  const int L = hdr.x, p0 = RAX_IDX(hdr.y, R.T - hdr.x + 1);
   if (tt0 >= L) return;
   if (plan.use_mfma && L >= R.mfma_min) return;
   if (e.rank == 0 || e.scale == 0.f) return;
   if (tt0 + 4 > kRecTokens) tq0 = segment_tokens(R, s, tt0, p0, L);
+  tq0 = checked_tokens(tq0, R.T);
   int n = 0;
   while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
   if (!((e.slice_mask >> n) & 1u)) return;
@@ -286,6 +289,7 @@ static void launch_expand_group_w(int ksm, dim3 grid, uint32_t lds, hipStream_t 
   void expand_group_launch_##NAME(int ksm, dim3 grid, uint32_t lds, hipStream_t stream, const GroupView& G, \
                                   const RouteView& R, const KTimer& tm) {                               \
     launch_expand_group_w<TW, TY>(ksm, grid, lds, stream, G, R, tm);                                     \
-  }
+  }                                                                                                     \
+  RAX_INDEX_FAULTS_ACCESSOR(NAME)
 
 }  // namespace rax

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
           ck = -1;                               // this group may advance any key's offset
         }
         if (key >= 0) {
-          sorted[pos] = t;
+          sorted[RAX_IDX(pos, T)] = t;
           if (key < S && rank < kRecTokens) rec[(size_t)key * kRecInts + 4 + rank] = t;
           if (rank == 0) first[key] = t;
           // the key's last lane advances the wave's running offset (all lanes read it above)
@@ -267,5 +267,7 @@ hipError_t launch_routing(const int32_t* ids, int T, int tps, int S, int mfma_mi
              mfma_min, tile_m, max_tiles, counts, offs, sorted, active, desc, tiles, rec, meta);
   return hipGetLastError();
 }
+
+RAX_INDEX_FAULTS_ACCESSOR(routing)
 
 }  // namespace rax

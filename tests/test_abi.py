@@ -146,6 +146,7 @@ def test_null_arguments_rejected_without_device():
         rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_route_linear_group(None, 1, None, None, 0, None, None, None, None, rx.LORA_BF16, None) == \
         rx.LORA_ERR_INVALID_ARG
+    assert rx.lib.lora_index_checks(None, None, 0) == rx.LORA_ERR_INVALID_ARG
     assert rx.lib.lora_pool_destroy(None) == rx.LORA_OK
     assert rx.lib.lora_routing_destroy(None) == rx.LORA_OK
 
@@ -180,3 +181,9 @@ def test_valid_create_reports_missing_device():
     assert st in (rx.LORA_ERR_NO_DEVICE, rx.LORA_ERR_HIP), rx.lora_last_error()
     st2 = rx.lib.lora_routing_create(C.byref(C.c_void_p()), 0, 8, 4)
     assert st2 in (rx.LORA_ERR_NO_DEVICE, rx.LORA_ERR_HIP)
+
+
+def test_index_checks_off_in_the_release_build():
+    """The release library reports its index checks as compiled out, without touching a
+    device."""
+    assert rx.index_checks() == (False, 0)
