@@ -40,10 +40,13 @@ __device__ __forceinline__ int4 segment_tokens(const RouteView& R, int s, int tt
                    R.sorted[min(p0 + tt + 3, last)]);
 }
 
-// a token quad's ids checked against the batch's T (debug builds; no code otherwise)
-__device__ __forceinline__ int4 checked_tokens(const int4& t, int T) {
-  return make_int4(RAX_IDX(t.x, T), RAX_IDX(t.y, T), RAX_IDX(t.z, T), RAX_IDX(t.w, T));
-}
+// a token quad's ids checked against the batch's T (statement; nothing outside debug builds)
+#ifdef RAXLORA_DEBUG
+#define RAX_CHECK_TOKENS(q, T) \
+  ((q) = make_int4(RAX_IDX((q).x, (T)), RAX_IDX((q).y, (T)), RAX_IDX((q).z, (T)), RAX_IDX((q).w, (T))))
+#else
+#define RAX_CHECK_TOKENS(q, T) ((void)0)
+#endif
 
 // element i (a compile-time constant after unrolling) of a token quad
 __device__ __forceinline__ int tok_at(const int4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }

@@ -48,6 +48,13 @@ __device__ __forceinline__ int checked_index(int i, long long) { return i; }
 #define RAX_INDEX_FAULTS_ACCESSOR(name)
 #endif
 #define RAX_IDX(i, n) ::rax::checked_index((i), (n))
+// the same check on a variable, as a statement: nothing at all in other builds, so an
+// expression's types and the code around it stay exactly as written there
+#ifdef RAXLORA_DEBUG
+#define RAX_CHECK_VAR(v, n) ((v) = ::rax::checked_index((int)(v), (n)))
+#else
+#define RAX_CHECK_VAR(v, n) ((void)0)
+#endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 

@@ -43,8 +43,9 @@ struct DecodeUPartials {
     for (int qv = 0; qv < QV; ++qv) {
       const int idx = lane + 64 * qv, j = idx >> 2, i = idx & 3;
       ok[qv] = i < nt && j < r;
-      base[qv] = U.p + n * U.n_stride +
-                 (long long)RAX_IDX(row0 + (ok[qv] ? i : 0), U.n_stride / U.row_stride) * U.row_stride + (ok[qv] ? j : 0);
+      int row = row0 + (ok[qv] ? i : 0);
+      RAX_CHECK_VAR(row, U.n_stride / U.row_stride);
+      base[qv] = U.p + n * U.n_stride + (long long)row * U.row_stride + (ok[qv] ? j : 0);
 #pragma unroll
       for (int q = 0; q < kUSplitBatch; ++q) pv[qv][q] = base[qv][(long long)min(q, U.nsplit - 1) * U.split_stride];
     }
@@ -104,13 +105,14 @@ __device__ __forceinline__ void expand_decode_tiles(const PoolView& P, const Rou
   }
   for (; tt < L; tt += ntg * kExpandTok) {
     const int nt = min(kExpandTok, L - tt);
-    const int4 tq = tt == tt0 ? tq0 : checked_tokens(segment_tokens(R, s, tt, p0, L), R.T);
+    int4 tq = tt == tt0 ? tq0 : segment_tokens(R, s, tt, p0, L);
+    RAX_CHECK_TOKENS(tq, R.T);
     for (int idx = lane; idx < kExpandTok * rp; idx += 64) {
       const int j = idx >> 2, i = idx & 3;
       const bool ok = i < nt && j < r;
       const int ic = ok ? i : 0, jc = ok ? j : 0;
-      const long long row = U.by_token ? (long long)RAX_IDX(R.sorted[p0 + tt + ic], R.T)
-                                       : (long long)RAX_IDX(p0 + tt + ic, U.n_stride / U.row_stride);
+      long long row = U.by_token ? (long long)R.sorted[p0 + tt + ic] : (long long)(p0 + tt + ic);
+      RAX_CHECK_VAR(row, U.by_token ? R.T : U.n_stride / U.row_stride);
       const float v = sum_splits(U.p + n * U.n_stride + row * U.row_stride + jc, U.split_stride, U.nsplit);
       usm[idx] = ok ? v : 0.f;
     }
@@ -139,12 +141,14 @@ __device__ __forceinline__ void expand_decode_item(const PoolView& P, const Rout
   int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
                                    : make_int4(0, 0, 0, 0);
   const SlotEntry e = P.table[s];
-  const int L = hdr.x, p0 = RAX_IDX(hdr.y, R.T - hdr.x + 1);
+  const int L = hdr.x;
+  int p0 = hdr.y;
+  RAX_CHECK_VAR(p0, R.T - L + 1);
   if (tt0 >= L) return;
   if (plan.use_mfma && L >= R.mfma_min) return;
   if (e.rank == 0 || e.scale == 0.f) return;
   if (tt0 + 4 > kRecTokens) tq0 = segment_tokens(R, s, tt0, p0, L);
-  tq0 = checked_tokens(tq0, R.T);
+  RAX_CHECK_TOKENS(tq0, R.T);
   int n = 0;
   while (n + 1 < P.N && ct >= P.tile0[n + 1]) ++n;
   if (!((e.slice_mask >> n) & 1u)) return;

@@ -74,8 +74,11 @@ __device__ __forceinline__ void shrink_decode_tiles(const PoolView& P, const T* 
 #pragma unroll
     for (int i = 0; i < kShrinkTok; ++i) xrow[i] = x + (size_t)tok_at(tq, i) * ldx;
     const float v = shrink_block_partial<T, TW>(P, A, xrow, nt, sp, plan.nsplit, plan.ns);
-    if (of < F && oi < nt)   // rows by sorted position
-      uo[(long long)RAX_IDX(p0 + tt + oi, U.n_stride / U.row_stride) * U.row_stride] = v;
+    if (of < F && oi < nt) {   // rows by sorted position
+      int row = p0 + tt + oi;
+      RAX_CHECK_VAR(row, U.n_stride / U.row_stride);
+      uo[(long long)row * U.row_stride] = v;
+    }
   }
 }
 
@@ -102,11 +105,15 @@ __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const Rout
   const int4 tq0 = tt0 + 4 <= kRecTokens ? *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts + 4 + tt0)
                                          : make_int4(0, 0, 0, 0);
   const SlotEntry e = P.table[s];
-  const int L = hdr.x, p0 = RAX_IDX(hdr.y, R.T - hdr.x + 1);
+  const int L = hdr.x;
+  int p0 = hdr.y;
+  RAX_CHECK_VAR(p0, R.T - L + 1);
   if (tt0 >= L) return;
   if (plan.use_mfma && L >= R.mfma_min) return;   // long segment: matrix-core units
   shrink_decode_tiles<T, TW>(P, x, ldx, U, plan, s, u.sp, u.rb, tt0, L, p0, e, [&](int tt) {
-    return checked_tokens(tt == tt0 && tt0 + 4 <= kRecTokens ? tq0 : segment_tokens(R, s, tt, p0, L), R.T);
+    int4 q = tt == tt0 && tt0 + 4 <= kRecTokens ? tq0 : segment_tokens(R, s, tt, p0, L);
+    RAX_CHECK_TOKENS(q, R.T);
+    return q;
   });
 }
 
@@ -201,7 +208,8 @@ __device__ __forceinline__ void shrink_slot_wg(const PoolView& P, const RouteVie
     const int2 hdr = *reinterpret_cast<const int2*>(rec);
     tok0 = rec[4 + lr];
     L = __builtin_amdgcn_readfirstlane(hdr.x);
-    p0 = RAX_IDX(__builtin_amdgcn_readfirstlane(hdr.y), R.T - L + 1);
+    p0 = __builtin_amdgcn_readfirstlane(hdr.y);
+    RAX_CHECK_VAR(p0, R.T - L + 1);
   }
   const int r = e.rank;
   const bool row_ok = fv && j < r;
@@ -211,7 +219,8 @@ __device__ __forceinline__ void shrink_slot_wg(const PoolView& P, const RouteVie
     int tk;
     if constexpr (SELF) tk = sm.tok[ti];
     else tk = t0 == 0 ? tok0 : (ti < kRecTokens ? R.rec[(size_t)s * kRecInts + 4 + ti] : R.sorted[p0 + ti]);
-    const uint16_t* __restrict__ xrow = x + (size_t)RAX_IDX(tk, R.T) * ldx;
+    RAX_CHECK_VAR(tk, R.T);
+    const uint16_t* __restrict__ xrow = x + (size_t)tk * ldx;
     uint4 xa[kSlotSteps];
 #pragma unroll
     for (int st = 0; st < kSlotSteps; ++st) xa[st] = ld16(xrow + min(min(w0 + st, wlast) * kMfmaK + 8 * lk, P.k - 8));
@@ -242,8 +251,8 @@ __device__ __forceinline__ void shrink_slot_wg(const PoolView& P, const RouteVie
       if (t < len && fr < F && jj < r) {
         float v = sm.red[0][t][rr];
         for (int ww = 1; ww < nw; ++ww) v += sm.red[ww][t][rr];
-        const long long row = RAX_IDX(t0 == 0 && U.head0 >= 0 ? U.head0 + kMfmaTileM * s + t : p0 + t0 + t,
-                                      U.n_stride / U.row_stride);
+        long long row = t0 == 0 && U.head0 >= 0 ? (long long)U.head0 + kMfmaTileM * s + t : p0 + t0 + t;
+        RAX_CHECK_VAR(row, U.n_stride / U.row_stride);
         U.p[part * U.split_stride + nn * U.n_stride + row * U.row_stride + jj] = v;
       }
     }

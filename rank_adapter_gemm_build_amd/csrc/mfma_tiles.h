@@ -162,11 +162,16 @@ __device__ __forceinline__ void shrink_mfma_rows(const PoolView& P, const uint16
     const int fr = fr0 + 16 * b + lr;
     if (fr < F) {
       const int n = fr / r, j = fr - n * r;
-      float* up = U.p + part * U.split_stride + n * U.n_stride + j;
+      float* up = U.p + part * U.split_stride + n * U.n_stride + (long long)p0 * U.row_stride + j;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * lk + i;
-        if (t < len) up[(long long)RAX_IDX(p0 + t, U.n_stride / U.row_stride) * U.row_stride] = acc[b][i];
+        if (t < len) {
+#ifdef RAXLORA_DEBUG
+          if (RAX_IDX(p0 + t, U.n_stride / U.row_stride) != p0 + t) continue;
+#endif
+          up[t * U.row_stride] = acc[b][i];
+        }
       }
     }
   }
@@ -200,10 +205,15 @@ template <typename TW>
 __device__ __forceinline__ void shrink_mfma_unit(const PoolView& P, const RouteView& R, const uint16_t* __restrict__ x,
                                                  int ldx, const UView& U, int tile, int rg, int part, int nsplit) {
   const int4 td = R.tiles[tile];
-  const int slot = RAX_IDX(td.x, P.S), len = td.z, p0 = RAX_IDX(td.y, R.T - len + 1);
+  int slot = td.x, p0 = td.y;
+  const int len = td.z;
+  RAX_CHECK_VAR(slot, P.S);
+  RAX_CHECK_VAR(p0, R.T - len + 1);
   // the slot-table entry and this lane's token id (token lane % 16) in one round trip
   const SlotEntry e = P.table[slot];
-  const uint16_t* __restrict__ xrow = x + (size_t)RAX_IDX(R.sorted[p0 + min(lane_id() & 15, len - 1)], R.T) * ldx;
+  int tok = R.sorted[p0 + min(lane_id() & 15, len - 1)];
+  RAX_CHECK_VAR(tok, R.T);
+  const uint16_t* __restrict__ xrow = x + (size_t)tok * ldx;
   shrink_mfma_tile<TW>(P, e, xrow, U, slot, p0, len, rg, part, nsplit);
 }
 
@@ -247,16 +257,17 @@ struct UPartials {
     const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
     const int j0 = ks * kMfmaK + 8 * lk;
     // j0 < r: j0 + 8 <= r rounded up to 8 <= row_stride, so the 8 floats stay in the row
-    base = U.p + n * U.n_stride + (long long)RAX_IDX(p0 + min(lr, len - 1), U.n_stride / U.row_stride) * U.row_stride +
-           (j0 < r ? j0 : 0);
+    int row = p0 + min(lr, len - 1);
+    RAX_CHECK_VAR(row, U.n_stride / U.row_stride);
+    base = U.p + n * U.n_stride + (long long)row * U.row_stride + (j0 < r ? j0 : 0);
     load_batch(U, 0);
   }
   // rank step 0 of row `row` (slot mode's first-tile rows, known before the segment
   // is: the token and rank are masked in finish())
   __device__ __forceinline__ void load_head(const UView& U, int n, long long row) {
     const int j0 = 8 * (lane_id() >> 4);
-    base = U.p + n * U.n_stride + (long long)RAX_IDX((int)row, U.n_stride / U.row_stride) * U.row_stride +
-           (j0 + 8 <= U.row_stride ? j0 : 0);
+    RAX_CHECK_VAR(row, U.n_stride / U.row_stride);
+    base = U.p + n * U.n_stride + row * U.row_stride + (j0 + 8 <= U.row_stride ? j0 : 0);
     load_batch(U, 0);
   }
   __device__ __forceinline__ void add_batch(const UView& U, int q0, float (&v)[8]) const {
@@ -305,7 +316,9 @@ __device__ __forceinline__ void u_frag_by_token(const RouteView& R, const UView&
                                                 int ks, uint4& uh, uint4& ul) {
   const int lane = lane_id(), lr = lane & 15, lk = lane >> 4;
   const int j0 = ks * kMfmaK + 8 * lk;
-  const float* base = U.p + n * U.n_stride + (long long)RAX_IDX(R.sorted[p0 + min(lr, len - 1)], R.T) * U.row_stride;
+  int tok = R.sorted[p0 + min(lr, len - 1)];
+  RAX_CHECK_VAR(tok, R.T);
+  const float* base = U.p + n * U.n_stride + (long long)tok * U.row_stride;
   float v[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) v[q] = base[min(j0 + q, r - 1)];
@@ -494,7 +507,8 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
     // this lane's token id first, then the partials and the first block's B: loads
     // complete in order, so the y rows can be addressed (and their loads issued) as
     // soon as the token id is in, while the rest is still in flight
-    const int tok = RAX_IDX(tokp ? *tokp : tokv, R.T);
+    int tok = tokp ? *tokp : tokv;
+    RAX_CHECK_VAR(tok, R.T);
     sched_fence();
     // one batch of partials: the caller's object, possibly already in flight (slot
     // mode's first tile)
@@ -514,7 +528,9 @@ __device__ __forceinline__ void expand_mfma_body(const RouteView& R, const UView
       uq.finish(U, len, r, ks, uh[ks], ul[ks]);
     }
   } else {
-    Y.load(RAX_IDX(tokp ? *tokp : tokv, R.T), y, ldy, on);
+    int tok = tokp ? *tokp : tokv;
+    RAX_CHECK_VAR(tok, R.T);
+    Y.load(tok, y, ldy, on);
     b0.issue(Y, bk, rs, dn, c00, nks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) u_frag_by_token(R, U, n, p0, len, r, ks, uh[ks], ul[ks]);
@@ -616,7 +632,10 @@ __device__ __forceinline__ void expand_mfma_unit(const PoolView& P, const RouteV
   const int n = mfma_group_slice(P, grp, cb, blk0);
   if (n < 0) return;
   const int4 td = R.tiles[tile];
-  const int slot = RAX_IDX(td.x, P.S), len = td.z, p0 = RAX_IDX(td.y, R.T - len + 1);
+  int slot = td.x, p0 = td.y;
+  const int len = td.z;
+  RAX_CHECK_VAR(slot, P.S);
+  RAX_CHECK_VAR(p0, R.T - len + 1);
   const SlotEntry e = lt.get(P, slot);
   // this lane's token id (token lane % 16): loaded by the body ahead of the partials
   const int* __restrict__ tokp = R.sorted + p0 + min(lane_id() & 15, len - 1);
@@ -660,7 +679,8 @@ __device__ __forceinline__ void expand_slot_unit(const PoolView& P, const RouteV
   if (!ahead) tok0 = rec[4 + lr];
   const SlotEntry e = P.table[s];
   const int L = __builtin_amdgcn_readfirstlane(hdr.x);
-  const int p0 = RAX_IDX(__builtin_amdgcn_readfirstlane(hdr.y), R.T - L + 1);
+  int p0 = __builtin_amdgcn_readfirstlane(hdr.y);
+  RAX_CHECK_VAR(p0, R.T - L + 1);
   if (L == 0 || e.rank == 0 || e.scale == 0.f || !((e.slice_mask >> n) & 1u)) return;
   if (ahead && L <= kMfmaTileM) {
     // a segment of one tile (the common decode case): its partials are already in flight

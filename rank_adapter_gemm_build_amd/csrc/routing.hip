@@ -169,7 +169,8 @@ __global__ __launch_bounds__(kRoutingMaxThreads) void routing_kernel(
           ck = -1;                               // this group may advance any key's offset
         }
         if (key >= 0) {
-          sorted[RAX_IDX(pos, T)] = t;
+          RAX_CHECK_VAR(pos, T);
+          sorted[pos] = t;
           if (key < S && rank < kRecTokens) rec[(size_t)key * kRecInts + 4 + rank] = t;
           if (rank == 0) first[key] = t;
           // the key's last lane advances the wave's running offset (all lanes read it above)
