@@ -10,6 +10,7 @@ arithmetic.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -41,6 +42,24 @@ def hipcc() -> str:
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def source_digest() -> str:
+    """sha256 (first 16 hex digits) of every file under csrc/ and include/, names and
+    contents: what a built library was compiled from, independent of file times."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for f in sorted(os.listdir(d)):
+            path = os.path.join(d, f)
+            if os.path.isfile(path):
+                with open(path, "rb") as fh:
+                    h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def digest_path(lib: str) -> str:
+    """The file beside a built library that records source_digest() at link time."""
+    return lib + ".sources"
 
 
 def _compile(src: str, extra, build_dir: str = BUILD) -> str:
@@ -87,6 +106,8 @@ def build(verbose: bool = True, extra=(), incremental: bool = False, debug: bool
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
+    with open(digest_path(lib), "w") as fh:
+        fh.write(source_digest() + "\n")
     if verbose:
         print(f"built {lib} from {len(srcs)} sources for {ARCH}")
     return lib

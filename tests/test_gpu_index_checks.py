@@ -10,6 +10,8 @@ import sys
 
 import pytest
 
+from rank_adapter_gemm_build_amd import build as B
+
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -22,10 +24,11 @@ FILES = ["tests/test_gpu_slot_mode.py", "tests/test_gpu_route_linear.py", "tests
 def test_parity_suites_on_the_index_checking_build():
     assert os.path.exists(DEBUG_LIB), \
         f"{DEBUG_LIB} is missing: build it with `python rank_adapter_gemm_build_amd/build.py --debug`"
-    csrc = os.path.join(ROOT, "rank_adapter_gemm_build_amd", "csrc")
-    newest = max(os.path.getmtime(os.path.join(csrc, f)) for f in os.listdir(csrc))
-    assert os.path.getmtime(DEBUG_LIB) >= newest, \
-        f"{DEBUG_LIB} is older than the sources: rebuild it with `python rank_adapter_gemm_build_amd/build.py --debug`"
+    # the sources it was linked from (recorded by the build), compared by content
+    with open(B.digest_path(DEBUG_LIB)) as fh:
+        built = fh.read().strip()
+    assert built == B.source_digest(), \
+        f"{DEBUG_LIB} was built from other sources: rebuild it with `python rank_adapter_gemm_build_amd/build.py --debug`"
     env = dict(os.environ, RAXLORA_LIBRARY=DEBUG_LIB, RAXLORA_EXPECT_INDEX_CHECKS="1")
     cmd = [sys.executable, "-u", "-m", "pytest", *FILES, "-m", "gpu", "-x", "-q", "-p", "no:cacheprovider",
            "--timeout", "300", "--timeout-method", "thread"]
