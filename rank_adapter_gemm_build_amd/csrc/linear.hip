@@ -82,15 +82,21 @@ __device__ __forceinline__ void shrink_decode_tiles(const PoolView& P, const T* 
   }
 }
 
+// Unit numbering, token group fastest, then k split, slot, and the 16-row block
+// slowest: the blocks past a slot's rank (units that exit after their first round
+// trip) then gather at the end of the grid instead of recurring in every slot's run
+// of units.  Consecutive units go to one XCD in groups (xcd_logical_block); with the
+// block inside the slot, every slot's block 0 fell on the same two XCDs, so a pool
+// of mixed ranks loaded those XCDs with up to four times the work of others.
 struct DecodeShrinkIndex {
   int tg, sp, rb, s;
-  __device__ __forceinline__ DecodeShrinkIndex(const Plan& plan, int unit) {
+  __device__ __forceinline__ DecodeShrinkIndex(const Plan& plan, int S, int unit) {
     tg = unit % plan.ntg;
     int rest = unit / plan.ntg;
     sp = rest % plan.nsplit;
     rest /= plan.nsplit;
-    rb = rest % plan.nrb;
-    s = rest / plan.nrb;
+    s = rest % S;
+    rb = rest / S;
   }
 };
 
@@ -98,7 +104,7 @@ template <typename T, typename TW>
 __device__ __forceinline__ void shrink_decode_unit(const PoolView& P, const RouteView& R,
                                                    const T* __restrict__ x, int ldx, const UView& U,
                                                    const Plan& plan, int unit) {
-  const DecodeShrinkIndex u(plan, unit);
+  const DecodeShrinkIndex u(plan, P.S, unit);
   const int s = u.s, tt0 = u.tg * kShrinkTok;
   // first round trip: record header, first token ids, slot-table entry
   const int4 hdr = *reinterpret_cast<const int4*>(R.rec + (size_t)s * kRecInts);
@@ -124,7 +130,7 @@ __device__ __forceinline__ void shrink_decode_unit_self(const PoolView& P, const
                                                         const int32_t* __restrict__ ids, const T* __restrict__ x,
                                                         int ldx, const UView& U, const Plan& plan, int unit,
                                                         int* __restrict__ tok) {
-  const DecodeShrinkIndex u(plan, unit);
+  const DecodeShrinkIndex u(plan, P.S, unit);
   const int s = u.s, tt0 = u.tg * kShrinkTok;
   // first round trip: the batch's ids, slot-table entry
   BatchKeys K;
