@@ -415,6 +415,14 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand, b
   };
   const int g4 = groups(rax::kMfmaColBlocksPerUnit);
   pl.cb = (long long)g4 * pl.tile_slots <= env_int("RAXLORA_CB1_MAX", 512) ? 1 : rax::kMfmaColBlocksPerUnit;
+  // Matrix-core expand tiles dealt to the XCDs one by one when segments are short on
+  // average (T < 64 S): tiles then cost what their slot's rank makes them, and runs of
+  // consecutive tiles gave some XCDs more high-rank tiles than others (Zipf workload:
+  // expand 117.6 -> 113.8 us).  Long segments keep runs of tiles per XCD, whose tiles
+  // share their slot's B in that XCD's L2 (prefill workload: 31.1 us, 36.9 dealt).
+  // RAXLORA_TILE_INTERLEAVE=0 / 1 forces either.
+  const int il = env_int("RAXLORA_TILE_INTERLEAVE", -1);
+  pl.tile_interleave = il >= 0 ? (il != 0) : (r->T < 64 * std::max(1, r->S));
   pl.n_mgroups = pl.cb == 1 ? groups(1) : g4;
   return pl;
 }

@@ -488,6 +488,38 @@ def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
         _log(f"  {mode}: normwise rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("cb1", ["0", "1000000000"], ids=["four-block-units", "one-block-units"])
+def test_expand_tiles_dealt_both_ways(rx, cb1):
+    """The matrix-core expand's two ways of dealing the tile list to the XCDs (runs of
+    consecutive tiles per XCD, or tile t to XCD t mod 8), with expand units of four
+    column blocks and of one: bitwise equal to each other, and the branch alone
+    against the oracle.  Segments of mixed lengths and ranks, more tiles than XCDs."""
+    import os
+    segments = [40, 3, 70, 17, 100, 5, 33, 16, 64, 9, 48]
+    slices = [1024, 384]
+    W = small_case(640, T=0, S=10, k=1024, slices=slices, Rmax=64, segments=segments)
+    mod = W.modules[0]
+    ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), oracle_adapters(W, mod), slices, W.ids,
+                       W.S, "bf16", max_rank=W.Rmax)
+    outs = {}
+    for il in ("0", "1"):
+        env = {"RAXLORA_TILE_INTERLEAVE": il, "RAXLORA_CB1_MAX": cb1, "RAXLORA_SLOT_MODE": "0"}
+        saved = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        try:
+            y = _run_linear(rx, W, mod, np.zeros((W.T, sum(slices)), dtype=np.float32), "f32")
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        outs[il] = from_device(y)
+        err = check_close(outs[il], ref, "bf16", f"delta (tiles dealt {'one by one' if il == '1' else 'in runs'})")
+        _log(f"  interleave {il}, CB1_MAX {cb1}: normwise rel err {err:.2e}")
+    assert np.array_equal(outs["0"], outs["1"]), "the two ways of dealing the tiles differ"
+
+
 @pytest.mark.parametrize("mode", ["default", "tiles", "slot", "all-mfma", "all-mfma-wide", "mfma16", "vector"])
 def test_short_segments_every_path(rx, mode):
     """Segments of 1..17 tokens through each split between the vector and matrix-core
