@@ -416,13 +416,16 @@ rax::Plan make_plan(const lora_pool* pool, const lora_routing* r, bool expand, b
   const int g4 = groups(rax::kMfmaColBlocksPerUnit);
   pl.cb = (long long)g4 * pl.tile_slots <= env_int("RAXLORA_CB1_MAX", 512) ? 1 : rax::kMfmaColBlocksPerUnit;
   // Matrix-core expand tiles dealt to the XCDs one by one when segments are short on
-  // average (T < 64 S): tiles then cost what their slot's rank makes them, and runs of
-  // consecutive tiles gave some XCDs more high-rank tiles than others (Zipf workload:
-  // expand 117.6 -> 113.8 us).  Long segments keep runs of tiles per XCD, whose tiles
-  // share their slot's B in that XCD's L2 (prefill workload: 31.1 us, 36.9 dealt).
-  // RAXLORA_TILE_INTERLEAVE=0 / 1 forces either.
+  // average (T < 64 S): tiles cost what their slot's rank makes them, and the
+  // contiguous eighths of the tile list gave some XCDs more high-rank tiles than
+  // others.  Zipf workload expand: eighths 116.7 us, runs of 1 / 2 / 4 tiles 113.7 /
+  // 112.9 / 115.9; packed three-module workload: eighths 31.0-31.2, runs of 1 30.7,
+  // runs of 2 33.6.  Long segments keep one contiguous eighth per XCD: there an XCD's
+  // tiles come from two or three slots, whose B fit its L2 (prefill workload: 30.9
+  // us; runs of 1, 2 or 4 36.6-37.7).  RAXLORA_TILE_INTERLEAVE=0 keeps the eighths,
+  // n > 0 deals runs of n tiles.
   const int il = env_int("RAXLORA_TILE_INTERLEAVE", -1);
-  pl.tile_interleave = il >= 0 ? (il != 0) : (r->T < 64 * std::max(1, r->S));
+  pl.tile_interleave = il >= 0 ? std::min(il, 1 << 20) : (r->T < 64 * std::max(1, r->S) ? 1 : 0);
   pl.n_mgroups = pl.cb == 1 ? groups(1) : g4;
   return pl;
 }

@@ -123,7 +123,8 @@ struct Plan {
                            //    cores): shrink workgroups (slot, k part, 16-row block nrb) of
                            //    slot_waves waves, expand units (slot, column group); no decode units
   int slot_waves;          // slot mode: waves sharing one k part's steps (at most 8 steps each)
-  int tile_interleave;     // matrix-core expand: tile t on XCD t % 8 (else contiguous runs of tiles per XCD)
+  int tile_interleave;     // matrix-core expand: n > 0 deals the tile list to the XCDs in runs of n
+                           // tiles (run i on XCD i % 8); 0: XCD x takes the x-th eighth of the list
 };
 
 // One module of a grouped launch (several target modules of one batch, sharing its

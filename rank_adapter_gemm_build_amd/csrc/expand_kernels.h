@@ -180,22 +180,21 @@ __device__ __forceinline__ void expand_body(const PoolView& P, const RouteView& 
   if constexpr (sizeof(TW) <= 2) {   // bf16 and FP8 weights
     LaneTable lt;
     lt.load(P);   // in flight with the tile count
-    // item l of this worker's XCD is (tile t0 + tstride * (l / n_mgroups), column group
-    // l % n_mgroups): XCD x takes the x-th run of the tile list, or (tile_interleave)
-    // tiles x, x + 8, x + 16, ...; one call site, so the unit is inlined once
+    // item l of this worker's XCD is (its tile l / n_mgroups, column group l % n_mgroups):
+    // XCD x takes the x-th eighth of the tile list, or (tile_interleave = n > 0) the runs
+    // of n tiles x, x + 8, x + 16, ...; one call site, so the unit is inlined once
     const int ntiles = R.meta[kMetaTiles];
     MfmaItems it(b, n_mfma_blocks, ntiles * plan.n_mgroups);
-    int t0 = 0, tstride = 1;
-    if (plan.tile_interleave) {
-      const int x = b % kXcds;
-      t0 = x;
-      tstride = kXcds;
+    const int run = plan.tile_interleave, x = b % kXcds;
+    if (run > 0) {
+      const int cyc = ntiles / (kXcds * run), rem = ntiles - cyc * kXcds * run;
       it.j = b / kXcds;
-      it.end = ntiles > x ? (ntiles - x + kXcds - 1) / kXcds * plan.n_mgroups : 0;
+      it.end = (cyc * run + min(run, max(0, rem - x * run))) * plan.n_mgroups;
     }
     for (; it.j < it.end; it.j += it.step) {
       const int q = it.j / plan.n_mgroups, g = it.j - q * plan.n_mgroups;
-      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, t0 + tstride * q, g, plan.cb, lt, smem);
+      const int tile = run > 0 ? ((q / run) * kXcds + x) * run + q % run : q;
+      expand_mfma_unit<TW, TY, KSM>(P, R, U, y, ldy, tile, g, plan.cb, lt, smem);
     }
   }
 }

@@ -490,10 +490,11 @@ def test_long_segments_matrix_cores(rx, segments, Rmax, slices):
 
 @pytest.mark.parametrize("cb1", ["0", "1000000000"], ids=["four-block-units", "one-block-units"])
 def test_expand_tiles_dealt_both_ways(rx, cb1):
-    """The matrix-core expand's two ways of dealing the tile list to the XCDs (runs of
-    consecutive tiles per XCD, or tile t to XCD t mod 8), with expand units of four
-    column blocks and of one: bitwise equal to each other, and the branch alone
-    against the oracle.  Segments of mixed lengths and ranks, more tiles than XCDs."""
+    """The matrix-core expand's ways of dealing the tile list to the XCDs (one
+    contiguous eighth per XCD, or runs of 1, 2 or 3 tiles dealt round the XCDs), with
+    expand units of four column blocks and of one: bitwise equal to each other, and the
+    branch alone against the oracle.  Segments of mixed lengths and ranks, 28 tiles
+    (more than the XCDs, and partial runs at the end)."""
     import os
     segments = [40, 3, 70, 17, 100, 5, 33, 16, 64, 9, 48]
     slices = [1024, 384]
@@ -502,7 +503,7 @@ def test_expand_tiles_dealt_both_ways(rx, cb1):
     ref = O.lora_apply(to_f64(mod.x, "bf16"), np.zeros((W.T, sum(slices))), oracle_adapters(W, mod), slices, W.ids,
                        W.S, "bf16", max_rank=W.Rmax)
     outs = {}
-    for il in ("0", "1"):
+    for il in ("0", "1", "2", "3"):
         env = {"RAXLORA_TILE_INTERLEAVE": il, "RAXLORA_CB1_MAX": cb1, "RAXLORA_SLOT_MODE": "0"}
         saved = {k: os.environ.get(k) for k in env}
         os.environ.update(env)
@@ -515,9 +516,10 @@ def test_expand_tiles_dealt_both_ways(rx, cb1):
                 else:
                     os.environ[k] = v
         outs[il] = from_device(y)
-        err = check_close(outs[il], ref, "bf16", f"delta (tiles dealt {'one by one' if il == '1' else 'in runs'})")
+        err = check_close(outs[il], ref, "bf16", f"delta (tile runs of {il}; 0: eighths)")
         _log(f"  interleave {il}, CB1_MAX {cb1}: normwise rel err {err:.2e}")
-    assert np.array_equal(outs["0"], outs["1"]), "the two ways of dealing the tiles differ"
+    for il in ("1", "2", "3"):
+        assert np.array_equal(outs["0"], outs[il]), f"tiles dealt in runs of {il} differ from the eighths"
 
 
 @pytest.mark.parametrize("mode", ["default", "tiles", "slot", "all-mfma", "all-mfma-wide", "mfma16", "vector"])
