@@ -49,6 +49,10 @@
  *                             instead of four when (column groups of four x tile
  *                             slots) is at most this (default 512)
  *       RAXLORA_XCD_GROUP     consecutive decode units kept on one XCD (default 4)
+ *       RAXLORA_TILE_INTERLEAVE  matrix-core expand: 0 gives XCD x the x-th eighth
+ *                             of the tile list, n > 0 deals runs of n tiles round
+ *                             the XCDs (default: 1 when T < 64 S, else 0; the
+ *                             results are the same either way)
  *       RAXLORA_GROUP_ORDER   0: grouped calls lay out their modules and decode units
  *                             in the order given (default 1: modules with the longest
  *                             shrink items first, decode expand units by descending
